@@ -1,0 +1,432 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (no GPU).
+
+Each test names the passage or the mathematical fact it checks. None of them re-derives a result by
+re-typing the oracle's own formula: they use values printed on the pages, closed forms, invariants,
+special cases that reduce to a library routine, exact rational arithmetic or brute force on tiny inputs.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def f32(v):
+    return np.asarray(v, dtype=np.float32)
+
+
+# --------------------------------------------------------------------------- printed worked examples
+
+def test_worked_example_symmetric_int8():
+    """Symmetric INT8 worked example ("大模型压缩：从研究到生产的完整攻略（1）", symmetric quantization)."""
+    g = gold("worked_example_symmetric_int8.json")
+    x = f32([g["x"]])
+    q, s, z = oracle.quantize(x, 8, True, oracle.TENSOR)
+    assert z is None
+    assert abs(float(s[0]) - g["printed_scale_approx"]) < 5e-5
+    printed = g["printed_codes"]
+    # four of the five printed codes are reproduced exactly, including 127 for the absmax element
+    for i in (0, 2, 3, 4):
+        assert q[0, i] == printed[i]
+    assert q[0].tolist() == g["expected_codes"]
+    xhat, _ = oracle.dequantize(q, s, None, oracle.TENSOR)
+    for i in (0, 2, 3):
+        assert abs(float(xhat[0, i]) - g["printed_dequant"][i]) < 6e-4
+    assert abs(float(xhat[0, 4]) - g["printed_dequant"][4]) < 5e-3
+
+
+def test_worked_example_printed_minus72_is_a_slip():
+    """No standard rounding of x/s gives the printed vector, so the printed -72 cannot be the method's."""
+    g = gold("worked_example_symmetric_int8.json")
+    x = np.array(g["x"], np.float64)
+    s = 2.1 / 127.0
+    t = x / s
+    printed = np.array(g["printed_codes"])
+    candidates = {
+        "half-even": np.round(t),
+        "half-away": np.sign(t) * np.floor(np.abs(t) + 0.5),
+        "floor": np.floor(t),
+        "ceil": np.ceil(t),
+        "trunc": np.trunc(t),
+    }
+    for name, r in candidates.items():
+        assert not np.array_equal(r.astype(int), printed), name
+    # the exact real quotient for -1.2 is nowhere near a rounding tie
+    assert abs(t[1] - (-72.5)) > 0.05
+
+
+def test_outlier_example():
+    """Outlier example: one value of 100 sets s ~ 0.79 and squeezes [-2, 2] into codes [-3, 3]."""
+    g = gold("outlier_example.json")
+    normal_vals = np.linspace(-2.0, 2.0, 401, dtype=np.float32)
+    x = np.concatenate([normal_vals, f32([g["outlier"]])])[None, :]
+    q, s, _ = oracle.quantize(x, 8, True, oracle.TENSOR)
+    assert abs(float(s[0]) - g["printed_scale_approx"]) < 0.005
+    assert q[0, -1] == 127
+    lo, hi = g["printed_normal_code_range"]
+    assert q[0, :-1].min() == lo and q[0, :-1].max() == hi
+
+
+def test_int4_group_bookkeeping_llama7b():
+    """§11.1.6 of "第11章 模型量化与压缩": 4096x4096, g=128 -> 32 groups per row, 131,072 groups, codes in [-7, 7],
+    s = group absmax / 7 (checked with numpy's max on a few groups)."""
+    g = gold("int4_group_example.json")
+    n, k = g["shape"]
+    w = workloads.attn7b(ms=(1,))["w"]
+    q, s, z = oracle.quantize(w, 4, True, oracle.GROUP, g["group_size"])
+    assert s.size == g["groups_total"] == n * k // g["group_size"]
+    assert s.reshape(n, -1).shape[1] == g["groups_per_row"]
+    assert q.min() >= g["code_range"][0] and q.max() <= g["code_range"][1]
+    wf = workloads.bf16_to_f32(w)
+    for row, grp in [(0, 0), (17, 31), (4095, 5)]:
+        seg = wf[row, grp * 128:(grp + 1) * 128]
+        assert s[row * 32 + grp] == np.float32(np.abs(seg).max()) / np.float32(7)
+        assert np.abs(q[row, grp * 128:(grp + 1) * 128]).max() == 7
+
+
+def test_metadata_overhead_accounting():
+    """§1.1 of "量化、蒸馏与模型压缩" and §11.3.7 of "第11章 模型量化与压缩": metadata share for g=128 and g=32
+    under 16-bit scales; the count of extra parameters is d_out*d_in/g."""
+    g = gold("metadata_overhead.json")
+    for gs in (128, 32):
+        share = 16.0 / (4.0 * gs)
+        lo, hi = g["ranges"][str(gs)]
+        assert lo <= share <= hi
+        assert abs(share - g["approx"][str(gs)]) < 0.006
+        assert oracle.n_segments(11008, 4096, oracle.GROUP, gs) == 11008 * 4096 // gs
+
+
+# --------------------------------------------------------------------------- rounding and division
+
+def test_round_half_to_even_at_exact_ties():
+    """A group with absmax 7 has s = 1 exactly, so x/s is exact and the ties are real ties."""
+    x = f32([[7.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -3.5] + [0.0] * 24])
+    q, s, _ = oracle.quantize(x, 4, True, oracle.GROUP, 32)
+    assert s[0] == 1.0
+    assert q[0, :8].tolist() == [7, 2, 4, -2, 0, 0, 2, -4]
+
+
+def test_hand_computed_group():
+    """absmax 3.5 -> s = 0.5 (exact); -3.5/0.5 = -7 ... and -1.75/0.5 = -3.5 ties to -4."""
+    x = f32([[3.5, -1.75, 0.5, 0.0, -3.5, 1.25, 0.75, 0.2] + [0.0] * 24])
+    q, s, _ = oracle.quantize(x, 4, True, oracle.GROUP, 32)
+    assert s[0] == 0.5
+    assert q[0, :8].tolist() == [7, -4, 1, 0, -7, 2, 2, 0]
+
+
+def test_asymmetric_round_then_add_zero_point():
+    """The core formula rounds x/s and then adds z. With s = 1 and z = 93, x = 0.5 gives 93; rounding
+    x/s + z as one number (the blog's variant) would give 94. Pins the order of the two operations."""
+    x = f32([[-93.0, 162.0, 0.5, 0.0, 1.5]])
+    q, s, z = oracle.quantize(x, 8, False, oracle.ROW)
+    assert s[0] == 1.0 and z[0] == 93
+    assert q[0].tolist() == [0, 255, 93, 93, 95]
+
+
+def _exact_f32_quotient(x, s):
+    """Correctly rounded binary32 quotient via exact rationals (nearest, ties to even)."""
+    r = Fraction(float(x)) / Fraction(float(s))
+    lo = np.float32(float(r))  # float(r) is the correctly rounded binary64; refine to binary32 below
+    cands = sorted({lo, np.nextafter(lo, np.float32(np.inf)), np.nextafter(lo, np.float32(-np.inf))},
+                   key=lambda c: (abs(Fraction(float(c)) - r), int(np.float32(c).view(np.uint32)) & 1))
+    return cands[0]
+
+
+def test_division_not_reciprocal_multiply():
+    """The code of x is taken from the correctly rounded quotient x/s. Find a value where x*(1/s) rounds
+    across a half-integer while x/s does not, and check the oracle follows exact division."""
+    s = np.float32(0.3)  # the group absmax is 7*s' below; pick s from a group directly
+    rng = np.random.default_rng(7)
+    found = None
+    for _ in range(200000):
+        a = np.float32(rng.uniform(0.5, 7.0))
+        s = a / np.float32(7)
+        h = np.float32(rng.integers(-6, 6)) + np.float32(0.5)
+        xv = np.float32(h * s)
+        for cand in (xv, np.nextafter(xv, np.float32(9)), np.nextafter(xv, np.float32(-9))):
+            qd = np.rint(_exact_f32_quotient(cand, s))
+            qr = np.rint(np.float32(cand * (np.float32(1) / s)))
+            if qd != qr and abs(cand) < a:
+                found = (a, cand, int(qd))
+                break
+        if found:
+            break
+    assert found is not None
+    a, xv, qd = found
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = a
+    x[0, 1] = xv
+    q, s_out, _ = oracle.quantize(x, 4, True, oracle.GROUP, 32)
+    assert s_out[0] == np.float32(a) / np.float32(7)
+    assert q[0, 1] == qd
+
+
+# --------------------------------------------------------------------------- error bound and zero point
+
+@pytest.mark.parametrize("bits,sym,gran,gs", [
+    (4, True, oracle.GROUP, 128), (4, True, oracle.GROUP, 32), (4, False, oracle.GROUP, 64),
+    (8, True, oracle.ROW, 0), (8, False, oracle.ROW, 0), (8, True, oracle.TENSOR, 0),
+    (4, False, oracle.TENSOR, 0), (8, False, oracle.GROUP, 128)])
+def test_error_bound_half_step(bits, sym, gran, gs):
+    """|x - x_hat| <= s/2 for every element that is not clipped ("量化、蒸馏与模型压缩", error bound under
+    nearest rounding), up to the rounding of the fp32 quotient: s/2 + |x| 2^-24, in exact arithmetic."""
+    rng = np.random.default_rng(bits * 100 + gs + int(sym))
+    x = (rng.standard_normal((16, 256)) * rng.uniform(0.01, 3.0, size=(16, 1))).astype(np.float32)
+    x[3, :64] += 2.0  # a shifted block (all positive) for the asymmetric cases
+    q, s, z = oracle.quantize(x, bits, sym, gran, gs)
+    seg = np.zeros(x.shape, np.int64)
+    if gran == oracle.ROW:
+        seg = np.repeat(np.arange(16), 256).reshape(16, 256)
+    elif gran == oracle.GROUP:
+        seg = np.arange(x.size).reshape(x.shape) // gs
+    ss = s[seg].astype(np.float64)
+    zz = 0 if z is None else z[seg].astype(np.int64)
+    xhat = ss * (q - zz)  # exact in binary64 (24-bit scale times a small integer)
+    err = np.abs(x.astype(np.float64) - xhat)
+    bound = ss / 2 + np.abs(x) * 2.0 ** -24
+    qmin, qmax = (-(2 ** (bits - 1) - 1), 2 ** (bits - 1) - 1) if sym else (0, 2 ** bits - 1)
+    inside = (q > qmin) & (q < qmax)
+    assert np.all(err[inside] <= bound[inside])
+    # ends of the range: still within the bound except for (rare) clipping
+    frac_bad = np.mean(err > bound)
+    assert frac_bad < 1e-3
+    assert q.min() >= qmin and q.max() <= qmax
+
+
+def test_asymmetric_zero_is_exact():
+    """With a zero point a real 0 maps to q = z and back to exactly 0 (blog, asymmetric quantization)."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((8, 256)).astype(np.float32) + 0.3
+    x[:, ::7] = 0.0
+    for bits, gran, gs in [(4, oracle.GROUP, 32), (4, oracle.GROUP, 128), (8, oracle.ROW, 0)]:
+        q, s, z = oracle.quantize(x, bits, False, gran, gs)
+        xhat, xhat16 = oracle.dequantize(q, s, z, gran, gs)
+        assert np.all(xhat[x == 0] == 0.0)
+        assert np.all(xhat16[x == 0] == 0)
+
+
+def test_asymmetric_range_ends_and_all_positive_group():
+    """min -> 0 and max -> 2^b - 1; a group with only positive values has lo widened to 0, so z = 0."""
+    x = f32([[-1.0, 2.0, 0.25, 1.0] + [0.5] * 28, [0.5, 1.5, 3.0, 0.75] + [1.0] * 28])
+    q, s, z = oracle.quantize(x, 4, False, oracle.GROUP, 32)
+    assert s[0] == np.float32(3.0) / np.float32(15) and z[0] == 5
+    assert q[0, 0] == 0 and q[0, 1] == 15
+    assert s[1] == np.float32(3.0) / np.float32(15) and z[1] == 0
+    assert q[1, 2] == 15
+
+
+def test_zero_range_and_underflowing_groups():
+    """An all-zero group, and a group whose fp32 scale underflows to 0, get s = 1 (and z = 0)."""
+    tiny = np.float32(1.4e-45)  # smallest positive subnormal
+    x = np.zeros((3, 32), np.float32)
+    x[1, 5] = tiny
+    x[2, 5] = np.float32(1e-40)  # subnormal but large enough for a nonzero subnormal scale
+    for sym in (True, False):
+        q, s, z = oracle.quantize(x, 4, sym, oracle.GROUP, 32)
+        assert s[0] == 1.0 and s[1] == 1.0
+        assert np.all(q[0] == (0 if sym else 0)) and np.all(q[1] == 0)
+        assert 0 < s[2] < 1e-40
+        assert (q[2, 5] == 7) if sym else (q[2, 5] == 15)
+        if not sym:
+            assert z[0] == 0 and z[1] == 0
+
+
+# --------------------------------------------------------------------------- granularity special cases
+
+def test_granularity_reductions():
+    """GROUP with g = cols is ROW; ROW of a one-row tensor is TENSOR; TENSOR of a one-group tensor is GROUP."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((6, 128)).astype(np.float32)
+    for sym in (True, False):
+        a = oracle.quantize(x, 4, sym, oracle.GROUP, 128)
+        b = oracle.quantize(x, 4, sym, oracle.ROW)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        r1 = oracle.quantize(x[2:3], 8, sym, oracle.ROW)
+        t1 = oracle.quantize(x[2:3], 8, sym, oracle.TENSOR)
+        assert np.array_equal(r1[0], t1[0]) and np.array_equal(r1[1], t1[1])
+        g1 = oracle.quantize(x[4:5, :32], 8, sym, oracle.GROUP, 32)
+        t2 = oracle.quantize(x[4:5, :32], 8, sym, oracle.TENSOR)
+        assert np.array_equal(g1[0], t2[0]) and np.array_equal(g1[1], t2[1])
+
+
+def test_group_segments_are_independent():
+    """Changing one group's values changes only that group's scale and codes (no index bleed)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    q0, s0, _ = oracle.quantize(x, 4, True, oracle.GROUP, 64)
+    x2 = x.copy()
+    x2[2, 100] = 9.0  # a new absmax inside group 1 of row 2
+    q1, s1, _ = oracle.quantize(x2, 4, True, oracle.GROUP, 64)
+    changed = np.nonzero(s0 != s1)[0].tolist()
+    assert changed == [2 * 4 + 1]
+    diff_rows, diff_cols = np.nonzero(q0 != q1)
+    assert diff_rows.size > 0
+    assert set(diff_rows.tolist()) <= {2} and diff_cols.min() >= 64 and diff_cols.max() < 128
+
+
+# --------------------------------------------------------------------------- packing and dequantization
+
+def test_pack_nibble_order():
+    q = np.zeros((1, 8), np.int32)
+    cases = [((0, 1), 0x01, 0), ((1, 1), 0x10, 0), ((0, -1), 0x0F, 0), ((1, -7), 0x90, 0), ((2, 7), 0x07, 1),
+             ((3, -8), 0x80, 1)]
+    for (pos, val), byte, idx in cases:
+        qq = q.copy()
+        qq[0, pos] = val
+        p = oracle.pack_int4(qq)
+        assert p[0, idx] == byte, (pos, val)
+        assert np.count_nonzero(p) == 1
+
+
+def test_pack_roundtrip():
+    rng = np.random.default_rng(2)
+    qs = rng.integers(-7, 8, size=(5, 64)).astype(np.int32)
+    assert np.array_equal(oracle.unpack_int4(oracle.pack_int4(qs), 64, True), qs)
+    qu = rng.integers(0, 16, size=(5, 64)).astype(np.int32)
+    assert np.array_equal(oracle.unpack_int4(oracle.pack_int4(qu), 64, False), qu)
+
+
+def test_dequantize_values_and_bf16_rounding():
+    q = np.array([[-4, 3, 0, 7]], np.int32)
+    s = f32([0.5])
+    out, out16 = oracle.dequantize(q, s, None, oracle.TENSOR)
+    assert out[0].tolist() == [-2.0, 1.5, 0.0, 3.5]
+    # bf16 rounding, nearest-even: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> 1; 1 + 3*2^-8 -> 1 + 2^-6
+    t = oracle.f32_to_bf16(f32([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20, -1.0 - 2 ** -8]))
+    assert t.tolist() == [0x3F80, 0x3F82, 0x3F81, 0xBF80]
+    qa = np.array([[0, 15, 5, 6]], np.int32)
+    out, _ = oracle.dequantize(qa, f32([0.25]), np.array([5], np.uint8), oracle.ROW)
+    assert out[0].tolist() == [-1.25, 2.5, 0.0, 0.25]
+
+
+# --------------------------------------------------------------------------- W4A16 reference
+
+def test_w4a16_unit_scales_is_integer_matvec():
+    """With s = 1 and z = 0 the layer is an integer matrix times a bf16 vector: numpy float64 matmul."""
+    rng = np.random.default_rng(9)
+    q = rng.integers(-7, 8, size=(48, 256)).astype(np.int32)
+    x = workloads.bf16_bits(rng.standard_normal((3, 256)).astype(np.float32))
+    s = np.ones(48 * 2, np.float32)
+    y = oracle.w4a16(x, q, s, None, 128)
+    ref = workloads.bf16_to_f32(x).astype(np.float64) @ q.T.astype(np.float64)
+    assert np.allclose(y, ref, rtol=0, atol=1e-9)
+
+
+def test_w4a16_brute_force_exact():
+    """Tiny asymmetric case against exact rational arithmetic."""
+    rng = np.random.default_rng(4)
+    N, K, gsz = 3, 64, 32
+    q = rng.integers(0, 16, size=(N, K)).astype(np.int32)
+    s = rng.uniform(0.01, 0.2, size=N * K // gsz).astype(np.float32)
+    z = rng.integers(0, 16, size=N * K // gsz).astype(np.uint8)
+    x = workloads.bf16_bits(rng.standard_normal((2, K)).astype(np.float32))
+    xf = workloads.bf16_to_f32(x)
+    y = oracle.w4a16(x, q, s, z, gsz)
+    for m in range(2):
+        for n in range(N):
+            exact = sum(Fraction(float(xf[m, k])) * Fraction(float(s[n * 2 + k // gsz])) *
+                        (int(q[n, k]) - int(z[n * 2 + k // gsz])) for k in range(K))
+            assert abs(Fraction(y[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 60)
+
+
+# --------------------------------------------------------------------------- SmoothQuant factor
+
+def test_smooth_alpha_special_cases():
+    """§11.4.3 of "第11章 模型量化与压缩": alpha = 1 -> s_j = max|X_j|; alpha = 0 -> s_j = 1/max|W_j|."""
+    d = workloads.w8a8(m=64, n=96, k=256)
+    xf = workloads.bf16_to_f32(d["x"])
+    wf = workloads.bf16_to_f32(d["w"])
+    s1 = oracle.smooth(d["x"], d["w"], 1.0)
+    assert np.array_equal(s1, np.abs(xf).max(axis=0))
+    s0 = oracle.smooth(d["x"], d["w"], 0.0)
+    assert np.array_equal(s0, np.float32(1) / np.abs(wf).max(axis=0))
+
+
+def test_smooth_alpha_half_balances_columns():
+    """alpha = 0.5 is the balance point ("量化、蒸馏与模型压缩" §2.3 eq. (2)): after smoothing, max|X'_j| equals
+    max|W'_j| (here within a few ulps, from fp32 rounding)."""
+    d = workloads.w8a8(m=64, n=96, k=256)
+    xf = workloads.bf16_to_f32(d["x"]).astype(np.float64)
+    wf = workloads.bf16_to_f32(d["w"]).astype(np.float64)
+    s = oracle.smooth(d["x"], d["w"], 0.5).astype(np.float64)
+    ax = np.abs(xf / s).max(axis=0)
+    aw = np.abs(wf * s).max(axis=0)
+    assert np.all(np.abs(ax - aw) <= 4 * 2.0 ** -23 * ax)
+    # generic alpha agrees with the closed form to ~1 ulp
+    s3 = oracle.smooth(d["x"], d["w"], 0.3).astype(np.float64)
+    ref = np.abs(xf).max(axis=0) ** 0.3 / np.abs(wf).max(axis=0) ** 0.7
+    assert np.all(np.abs(s3 - ref) <= 2.0 ** -23 * ref)
+
+
+def test_smooth_zero_channel_and_equivalence():
+    """A zero channel gets s_j = 1; and X diag(s)^-1 . diag(s) W^T equals X W^T (§11.4.2 identity)."""
+    d = workloads.w8a8(m=32, n=48, k=128)
+    x = d["x"].copy()
+    x[:, 7] = 0
+    s = oracle.smooth(x, d["w"], 0.5)
+    assert s[7] == 1.0
+    xf = workloads.bf16_to_f32(x).astype(np.float64)
+    wf = workloads.bf16_to_f32(d["w"]).astype(np.float64)
+    sd = s.astype(np.float64)
+    assert np.allclose((xf / sd) @ (wf * sd).T, xf @ wf.T, rtol=1e-12, atol=1e-12)
+
+
+def test_outliers_starve_per_tensor_int8():
+    """"量化、蒸馏与模型压缩" §2.3: per-tensor INT8 on activations with outlier channels leaves the ordinary
+    channels only a few levels (2-3 bits). With x50 outlier channels they stay within |q| <= 7 here."""
+    d = workloads.w8a8(m=256, n=16, k=4096)
+    q, s, _ = oracle.quantize(d["x"], 8, True, oracle.TENSOR)
+    normal_cols = np.setdiff1d(np.arange(4096), d["outlier_chans"])
+    lvl = np.abs(q[:, normal_cols])
+    assert np.quantile(lvl, 0.999) <= 4 and lvl.max() <= 7
+    assert np.abs(q).max() == 127
+
+
+# --------------------------------------------------------------------------- INT8 GEMM and epilogue
+
+def test_gemm_brute_force_extremes():
+    a = np.array([[127, -127, 0, 5, -1], [1, 2, 3, 4, 5], [-127, -127, -127, -127, -127]], np.int8)
+    b = np.array([[127, 127, 127, 127, 127], [-127, 127, -127, 127, -127], [0, 0, 1, 0, 0],
+                  [1, -1, 1, -1, 1], [3, 1, 4, 1, 5], [-2, 7, -1, 8, -2], [127, -127, 127, -127, 127]], np.int8)
+    c = oracle.gemm_s8(a, b)
+    for i in range(3):
+        for j in range(7):
+            assert c[i, j] == sum(int(a[i, k]) * int(b[j, k]) for k in range(5))
+
+
+def test_gemm_matches_numpy_int64():
+    rng = np.random.default_rng(1)
+    a = rng.integers(-127, 128, size=(37, 300)).astype(np.int8)
+    b = rng.integers(-127, 128, size=(53, 300)).astype(np.int8)
+    assert np.array_equal(oracle.gemm_s8(a, b), a.astype(np.int64) @ b.astype(np.int64).T)
+
+
+def test_gemm_int32_bound():
+    """K * 127^2 stays inside int32 for K = 4096 (66,064,384 < 2^31)."""
+    a = np.full((1, 4096), 127, np.int8)
+    c = oracle.gemm_s8(a, a)
+    assert c[0, 0] == 4096 * 127 * 127 < 2 ** 31
+
+
+def test_w8a8_epilogue_and_pipeline():
+    d = workloads.w8a8(m=16, n=24, k=256)
+    r = oracle.w8a8(d["x"], d["w"], 0.5)
+    ref = r["acc"].astype(np.float64) * r["s_x"].astype(np.float64)[:, None] * r["s_w"].astype(np.float64)[None, :]
+    assert np.array_equal(r["y"], ref)
+    # the quantized layer approximates the float product X W^T
+    xf = workloads.bf16_to_f32(d["x"]).astype(np.float64)
+    wf = workloads.bf16_to_f32(d["w"]).astype(np.float64)
+    y_true = xf @ wf.T
+    assert np.linalg.norm(r["y"] - y_true) / np.linalg.norm(y_true) < 0.05
+    assert np.abs(r["q_x"]).max() <= 127 and np.abs(r["q_w"]).max() <= 127
