@@ -1,0 +1,182 @@
+/*
+ * pqg.h -- C ABI of the MI355X (gfx950) quantized linear layer.
+ *
+ * Operations, by the passage that defines them:
+ *   [P1] "量化、蒸馏与模型压缩" (LLM knowledge atlas, notes 03-05): core formula; §1.1 group quantization and
+ *        its metadata; §2.3 SmoothQuant, eq. (1)-(2).
+ *   [P2] "模型压缩：量化、ZeroQuant、LLM.int8() 与 SmoothQuant" (LLM tutorial, lesson 19): §3 basic formula,
+ *        §4 granularity, §11 vector-wise scaling, §13 alpha.
+ *   [P3] "第11章 模型量化与压缩" (AI infra guide, chapter 11): §11.1.1 affine quantization; §11.1.2
+ *        symmetric / asymmetric; §11.1.3 Table 11-1 granularity; §11.1.4 dynamic quantization; §11.1.6
+ *        INT4 group example; §11.4.3 smoothing factor; §11.4.5 W8A8 pipeline; §11.10.1 bandwidth model.
+ *   [P5] "大模型压缩：从研究到生产的完整攻略（1）" (CSDN blog): symmetric / asymmetric worked examples.
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers except `stream` are DEVICE pointers into memory the caller allocated and owns; the
+ *     library allocates nothing and keeps no state besides a thread-local error string.
+ *   - Tensors are row-major and contiguous. bf16 is the 16-bit brain float (upper half of a binary32).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is enqueued on it and never
+ *     synchronised: execution errors surface at the caller's next synchronisation.
+ *   - Every argument is checked on the host BEFORE anything is enqueued. On error nothing is launched and
+ *     the call returns PQG_EINVAL (bad argument) or PQG_EUNSUPPORTED (valid but not implemented); a failed
+ *     launch returns PQG_EHIP. pqg_last_error() then describes the problem.
+ *   - Device pointers must be 16-byte aligned (scale / zero / smoothing vectors: 4-byte aligned).
+ *   - A tensor with zero rows is accepted and nothing is launched.
+ *   - Inputs must be finite; NaN / Inf inputs give unspecified codes.
+ *   - Calls on one stream are ordered; calls that share output buffers on different streams race.
+ */
+#ifndef PQG_H
+#define PQG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PQG_ABI_VERSION 1
+
+/* status codes */
+#define PQG_OK 0
+#define PQG_EINVAL 1
+#define PQG_EUNSUPPORTED 2
+#define PQG_EHIP 3
+
+/* float element types */
+#define PQG_F32 0
+#define PQG_BF16 1
+
+/* granularity of the (scale, zero) parameters [P2 §4; P3 §11.1.3 Table 11-1]:
+ *   PQG_TENSOR : one pair for the whole tensor;
+ *   PQG_ROW    : one pair per row -- per output channel for a weight [N, K], per token for activations [M, K];
+ *   PQG_GROUP  : one pair per `group_size` consecutive elements of a row (along the input dimension),
+ *                rows*cols/group_size pairs [P1 §1.1; P3 §11.1.6]. */
+#define PQG_TENSOR 0
+#define PQG_ROW 1
+#define PQG_GROUP 2
+
+/* smoothing applied before quantization, per input channel j (column) [P3 §11.4.2, §11.4.5]:
+ *   PQG_SMOOTH_DIV : x'[.., j] = x[.., j] / s[j]  (activations, X diag(s)^-1)
+ *   PQG_SMOOTH_MUL : x'[.., j] = x[.., j] * s[j]  (weights, diag(s) W with W stored [N, K]) */
+#define PQG_SMOOTH_NONE 0
+#define PQG_SMOOTH_DIV 1
+#define PQG_SMOOTH_MUL 2
+
+/* Version of this ABI (PQG_ABI_VERSION). */
+int32_t pqg_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none). Valid until the thread's next pqg_* call. */
+const char *pqg_last_error(void);
+
+/*
+ * Workspace needed by pqg_quantize for this shape and granularity (bytes; 0 if none).
+ * Only PQG_TENSOR needs one (per-block partial ranges).
+ */
+size_t pqg_quantize_workspace_bytes(int64_t rows, int64_t cols, int32_t granularity);
+
+/*
+ * Affine quantization  q = clamp(round(x / s) + z, qmin, qmax)  [P1 core formula; P2 §3; P3 §11.1.1].
+ *   x            : [rows, cols] of x_dtype (PQG_F32 or PQG_BF16).
+ *   smooth       : [cols] fp32 smoothing vector, required iff smooth_mode != PQG_SMOOTH_NONE.
+ *   bits         : 4 or 8.
+ *   symmetric    : 1 -> z = 0, s = max|x| / qmax, codes in [-qmax, qmax], qmax = 2^(bits-1) - 1
+ *                  (INT4 [-7, 7], INT8 [-127, 127]) [P3 §11.1.2, §11.1.6; P5 symmetric example];
+ *                  0 -> unsigned codes [0, 2^bits - 1], s = (hi - lo) / (2^bits - 1), z = round(-lo / s),
+ *                  with the range [lo, hi] widened to contain 0 so that 0 is coded exactly
+ *                  [P3 §11.1.1; P5 asymmetric example].
+ *   granularity  : PQG_TENSOR / PQG_ROW / PQG_GROUP; group_size in {32, 64, 128} for PQG_GROUP (else ignored).
+ *   codes (out)  : bits == 8: int8 (symmetric) or uint8 (asymmetric) [rows, cols];
+ *                  bits == 4: uint8 [rows, cols / 2], two codes per byte, element 2i of a row in the low
+ *                  nibble of byte i, signed codes as two's-complement nibbles.
+ *   scales (out) : fp32 [1], [rows] or [rows * cols / group_size].
+ *   zeros (out)  : uint8, same count as scales; required iff symmetric == 0, must be NULL otherwise.
+ *   workspace    : device scratch of at least pqg_quantize_workspace_bytes() bytes (may be NULL if 0).
+ * Rounding is round-half-to-even of the correctly rounded fp32 quotient x / s; smoothing divides or
+ * multiplies in fp32; a segment whose step would be 0 gets s = 1, z = 0. Results are bit-identical to a
+ * strict-IEEE CPU evaluation of the same formulas.
+ * Requires cols % 32 == 0 and, for PQG_ROW, cols <= 65536.
+ */
+int32_t pqg_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols, const float *smooth,
+                     int32_t smooth_mode, int32_t bits, int32_t symmetric, int32_t granularity,
+                     int32_t group_size, void *codes, float *scales, uint8_t *zeros, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
+ * Dequantization  x_hat = s * (q - z)  [P1 core formula; P2 §3; P3 §11.1.1]: one fp32 multiply per element,
+ * rounded to nearest-even when out_dtype is PQG_BF16.
+ *   codes / scales / zeros / bits / symmetric / granularity / group_size: as produced by pqg_quantize
+ *   (zeros NULL iff symmetric). out: [rows, cols] of out_dtype.
+ */
+int32_t pqg_dequantize(const void *codes, const float *scales, const uint8_t *zeros, int64_t rows, int64_t cols,
+                       int32_t bits, int32_t symmetric, int32_t granularity, int32_t group_size, void *out,
+                       int32_t out_dtype, void *stream);
+
+/* Workspace needed by pqg_smooth (bytes). */
+size_t pqg_smooth_workspace_bytes(int64_t tokens, int64_t out_features, int64_t in_features);
+
+/*
+ * SmoothQuant factor  s_j = max_t |X[t, j]|^alpha / max_n |W[n, j]|^(1 - alpha)
+ * [P1 §2.3 eq. (1); P2 §13; P3 §11.4.3].
+ *   x : activations [tokens, in_features] (x_dtype); w : weights [out_features, in_features] (w_dtype);
+ *   s (out) : fp32 [in_features]; alpha in [0, 1].
+ * Evaluation in fp32: alpha = 0.5 -> sqrt(ax) / sqrt(aw) (correctly rounded); alpha = 1 -> ax;
+ * alpha = 0 -> 1 / aw; other alpha -> binary64 pow quotient rounded to fp32 (may differ by 1 ulp from
+ * another libm). A channel with ax = 0 or aw = 0 gets s_j = 1.
+ * Requires in_features % 8 == 0 and tokens, out_features >= 1.
+ */
+int32_t pqg_smooth(const void *x, int32_t x_dtype, int64_t tokens, const void *w, int32_t w_dtype,
+                   int64_t out_features, int64_t in_features, double alpha, float *s, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * Weight-only W4A16 linear  y[m, n] = sum_k x[m, k] * s[n, g(k)] * (q[n, k] - z[n, g(k)])
+ * [P3 §11.1.6 step 5 (dequantize and multiply with 16-bit activations); P3 §11.10.1 (decode streams every
+ * weight once per step)]. The dequantization happens in registers; no dequantized weight is written.
+ *   x        : bf16 [M, K].
+ *   w_packed : uint8 [N, K / 2], INT4 codes as pqg_quantize writes them (symmetric: two's complement).
+ *   scales   : fp32 [N, K / group_size]; zeros: uint8 [N, K / group_size], NULL iff symmetric.
+ *   group_size in {32, 64, 128}; K % group_size == 0.
+ *   y (out)  : [M, N] of y_dtype (PQG_F32 or PQG_BF16); fp32 accumulation.
+ * The sum is evaluated in a different order than a sequential loop; results agree with an exact
+ * evaluation to well within bf16 output rounding (and to ~1e-6 relative for fp32 output).
+ */
+int32_t pqg_qlinear_w4a16(const void *x, int64_t M, int64_t N, int64_t K, const uint8_t *w_packed,
+                          const float *scales, const uint8_t *zeros, int32_t group_size, int32_t symmetric,
+                          void *y, int32_t y_dtype, void *stream);
+
+/*
+ * W8A8 linear layer  y[m, n] = (sum_k q_x[m, k] q_w[n, k]) * s_x[m] * s_w[n]
+ * [P3 §11.4.5 steps 5-6 (INT8 GEMM, INT32 accumulation, dequantized output); P3 §11.1.4 dynamic
+ * activation statistics; P2 §11 vector-wise scales].
+ * The activations are quantized on the fly: per token (row), symmetric INT8 [-127, 127], after the
+ * smoothing division X diag(s)^-1 when `smooth` is non-NULL (exactly as pqg_quantize with PQG_ROW,
+ * bits 8, symmetric, PQG_SMOOTH_DIV); then the INT8 GEMM with exact INT32 accumulation and the epilogue
+ * y = bf16/fp32(float(acc) * (s_x[m] * s_w[n])).
+ *   x        : bf16 [M, K] activations.
+ *   smooth   : fp32 [K] or NULL.
+ *   w_q      : int8 [N, K] per-output-channel symmetric codes (pqg_quantize, PQG_ROW, bits 8; the
+ *              smoothing multiply diag(s) W is applied there, offline); w_scales: fp32 [N].
+ *   y (out)  : [M, N] of y_dtype (PQG_BF16 or PQG_F32).
+ *   x_q, x_scales (out): caller scratch int8 [M, K] and fp32 [M]; left holding the activation codes
+ *              and scales.
+ * Requires K % 32 == 0 and K <= 65536.
+ */
+int32_t pqg_qlinear_w8a8(const void *x, const float *smooth, const int8_t *w_q, const float *w_scales, int64_t M,
+                         int64_t N, int64_t K, void *y, int32_t y_dtype, int8_t *x_q, float *x_scales,
+                         void *stream);
+
+/*
+ * The INT8 x INT8 -> INT32 product of the W8A8 layer without the epilogue:
+ *   c[m, n] = sum_k a[m, k] * b[n, k]   (exact; |c| < 2^31 whenever K * 127^2 < 2^31, i.e. K <= 133,144).
+ *   a : int8 [M, K]; b : int8 [N, K]; c (out) : int32 [M, N]. Requires K % 16 == 0.
+ * Same kernel and tiling as pqg_qlinear_w8a8; exposed so the accumulators can be checked bit-exactly.
+ */
+int32_t pqg_gemm_s8s8s32(const int8_t *a, const int8_t *b, int64_t M, int64_t N, int64_t K, int32_t *c,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQG_H */

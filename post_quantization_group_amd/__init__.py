@@ -1,0 +1,215 @@
+"""MI355X (gfx950) quantized linear layer: thin Python binding over the C ABI in include/pqg.h.
+
+The functions below carry the names of the C entry points (without the ``pqg_`` prefix). They only
+marshal arguments: check tensor dtypes/devices, allocate outputs with ``torch.empty`` on the input's
+device, and pass raw device pointers plus the current HIP stream to libpqg.so. Every step of the
+computation runs in the library's HIP kernels; there is no CPU or PyTorch fallback, and a missing
+library is an error.
+
+Tensor conventions: bf16 tensors are ``torch.bfloat16``; packed INT4 codes are ``torch.uint8``
+[rows, cols/2]; INT8 codes are ``torch.int8`` (symmetric) or ``torch.uint8`` (asymmetric).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpqg.so")
+
+# constants of include/pqg.h
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+F32, BF16 = 0, 1
+TENSOR, ROW, GROUP = 0, 1, 2
+SMOOTH_NONE, SMOOTH_DIV, SMOOTH_MUL = 0, 1, 2
+ABI_VERSION = 1
+
+EXPORTS = [
+    "pqg_abi_version", "pqg_last_error", "pqg_quantize_workspace_bytes", "pqg_quantize", "pqg_dequantize",
+    "pqg_smooth_workspace_bytes", "pqg_smooth", "pqg_qlinear_w4a16", "pqg_qlinear_w8a8", "pqg_gemm_s8s8s32",
+]
+
+_lib = None
+
+
+class PqgError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("pqg status %d: %s" % (status, message))
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libpqg.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libpqg.so is not built (%s); run __graft_entry__.build() or "
+                          "python -m post_quantization_group_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    P, I64, I32, SZ, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
+    lib.pqg_abi_version.restype = I32
+    lib.pqg_abi_version.argtypes = []
+    lib.pqg_last_error.restype = ctypes.c_char_p
+    lib.pqg_last_error.argtypes = []
+    lib.pqg_quantize_workspace_bytes.restype = SZ
+    lib.pqg_quantize_workspace_bytes.argtypes = [I64, I64, I32]
+    lib.pqg_quantize.restype = I32
+    lib.pqg_quantize.argtypes = [P, I32, I64, I64, P, I32, I32, I32, I32, I32, P, P, P, P, SZ, P]
+    lib.pqg_dequantize.restype = I32
+    lib.pqg_dequantize.argtypes = [P, P, P, I64, I64, I32, I32, I32, I32, P, I32, P]
+    lib.pqg_smooth_workspace_bytes.restype = SZ
+    lib.pqg_smooth_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.pqg_smooth.restype = I32
+    lib.pqg_smooth.argtypes = [P, I32, I64, P, I32, I64, I64, D, P, P, SZ, P]
+    lib.pqg_qlinear_w4a16.restype = I32
+    lib.pqg_qlinear_w4a16.argtypes = [P, I64, I64, I64, P, P, P, I32, I32, P, I32, P]
+    lib.pqg_qlinear_w8a8.restype = I32
+    lib.pqg_qlinear_w8a8.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, P, P]
+    lib.pqg_gemm_s8s8s32.restype = I32
+    lib.pqg_gemm_s8s8s32.argtypes = [P, P, I64, I64, I64, P, P]
+    if lib.pqg_abi_version() != ABI_VERSION:
+        raise ImportError("libpqg.so ABI %d != binding ABI %d" % (lib.pqg_abi_version(), ABI_VERSION))
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != OK:
+        raise PqgError(status, load().pqg_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _float_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("expected a bfloat16 or float32 tensor, got %s" % t.dtype)
+
+
+def _dev(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.device
+
+
+def n_segments(rows: int, cols: int, granularity: int, group_size: int) -> int:
+    if granularity == TENSOR:
+        return 1
+    if granularity == ROW:
+        return rows
+    return rows * cols // group_size
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def quantize(x: torch.Tensor, bits: int, symmetric: bool, granularity: int, group_size: int = 0,
+             smooth: torch.Tensor | None = None, smooth_mode: int = SMOOTH_NONE, out=None):
+    """pqg_quantize. Returns (codes, scales, zeros-or-None). `out` may pass preallocated (codes, scales, zeros)."""
+    lib = load()
+    dev = _dev(x)
+    rows, cols = x.shape
+    nseg = n_segments(rows, cols, granularity, group_size) if (granularity != GROUP or group_size > 0) else 0
+    if out is None:
+        if bits == 4:
+            codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        else:
+            codes = torch.empty((rows, cols), dtype=torch.int8 if symmetric else torch.uint8, device=dev)
+        scales = torch.empty(max(nseg, 1), dtype=torch.float32, device=dev)[:nseg]
+        zeros = None if symmetric else torch.empty(max(nseg, 1), dtype=torch.uint8, device=dev)[:nseg]
+    else:
+        codes, scales, zeros = out
+    ws_bytes = lib.pqg_quantize_workspace_bytes(rows, cols, granularity)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if smooth is not None:
+        _dev(smooth)
+    _check(lib.pqg_quantize(_ptr(x), _float_dtype(x), rows, cols, _ptr(smooth), smooth_mode, bits, int(symmetric),
+                            granularity, group_size, _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(ws), ws_bytes,
+                            _stream(dev)))
+    return codes, scales, zeros
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, zeros, rows: int, cols: int, bits: int, symmetric: bool,
+               granularity: int, group_size: int = 0, out_dtype=torch.float32):
+    """pqg_dequantize -> [rows, cols] tensor of out_dtype (float32 or bfloat16)."""
+    lib = load()
+    dev = _dev(codes)
+    out = torch.empty((rows, cols), dtype=out_dtype, device=dev)
+    _check(lib.pqg_dequantize(_ptr(codes), _ptr(scales), _ptr(zeros), rows, cols, bits, int(symmetric), granularity,
+                              group_size, _ptr(out), _float_dtype(out), _stream(dev)))
+    return out
+
+
+def smooth(x: torch.Tensor, w: torch.Tensor, alpha: float = 0.5):
+    """pqg_smooth -> float32 [in_features] smoothing factor."""
+    lib = load()
+    dev = _dev(x)
+    _dev(w)
+    tokens, k = x.shape
+    n, k2 = w.shape
+    if k != k2:
+        raise ValueError("x and w disagree on in_features")
+    s = torch.empty(k, dtype=torch.float32, device=dev)
+    ws_bytes = lib.pqg_smooth_workspace_bytes(tokens, n, k)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    _check(lib.pqg_smooth(_ptr(x), _float_dtype(x), tokens, _ptr(w), _float_dtype(w), n, k, float(alpha), _ptr(s),
+                          _ptr(ws), ws_bytes, _stream(dev)))
+    return s
+
+
+def qlinear_w4a16(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor, zeros, group_size: int,
+                  symmetric: bool, out_dtype=torch.bfloat16, out=None):
+    """pqg_qlinear_w4a16: y = x @ dequant(w)^T for bf16 x [M, K] and packed INT4 w [N, K/2]."""
+    lib = load()
+    dev = _dev(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    M, K = x.shape
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 2 != K:
+        raise ValueError("w_packed must be [N, K/2]")
+    y = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    _check(lib.pqg_qlinear_w4a16(_ptr(x), M, N, K, _ptr(w_packed), _ptr(scales), _ptr(zeros), group_size,
+                                 int(symmetric), _ptr(y), _float_dtype(y), _stream(dev)))
+    return y
+
+
+def qlinear_w8a8(x: torch.Tensor, smooth_s, w_q: torch.Tensor, w_scales: torch.Tensor, out_dtype=torch.bfloat16,
+                 out=None, x_q=None, x_scales=None):
+    """pqg_qlinear_w8a8: dynamic per-token INT8 activations (after X diag(s)^-1), INT8 GEMM, s_x*s_w epilogue.
+    Returns (y, x_q, x_scales)."""
+    lib = load()
+    dev = _dev(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    M, K = x.shape
+    N = w_q.shape[0]
+    y = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    x_q = torch.empty((M, K), dtype=torch.int8, device=dev) if x_q is None else x_q
+    x_scales = torch.empty(M, dtype=torch.float32, device=dev) if x_scales is None else x_scales
+    _check(lib.pqg_qlinear_w8a8(_ptr(x), _ptr(smooth_s), _ptr(w_q), _ptr(w_scales), M, N, K, _ptr(y),
+                                _float_dtype(y), _ptr(x_q), _ptr(x_scales), _stream(dev)))
+    return y, x_q, x_scales
+
+
+def gemm_s8s8s32(a: torch.Tensor, b: torch.Tensor, out=None):
+    """pqg_gemm_s8s8s32: exact int32 [M, N] = a [M, K] (int8) x b [N, K]^T (int8)."""
+    lib = load()
+    dev = _dev(a)
+    M, K = a.shape
+    N = b.shape[0]
+    c = torch.empty((M, N), dtype=torch.int32, device=dev) if out is None else out
+    _check(lib.pqg_gemm_s8s8s32(_ptr(a), _ptr(b), M, N, K, _ptr(c), _stream(dev)))
+    return c

@@ -1,0 +1,255 @@
+// api.cpp -- the C ABI (include/pqg.h): argument validation, dispatch, error reporting.
+//
+// Every check runs on the host before anything is enqueued, so a rejected call leaves the stream
+// untouched. The library holds no device state and allocates nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/pqg.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int32_t hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(PQG_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return PQG_OK;
+}
+
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+bool valid_float_dtype(int32_t d) { return d == PQG_F32 || d == PQG_BF16; }
+
+int32_t check_qspec(int32_t bits, int32_t symmetric, int32_t granularity, int32_t group_size, int64_t cols)
+{
+    if (bits != 4 && bits != 8)
+        return fail(PQG_EINVAL, "bits must be 4 or 8 (got %d)", bits);
+    if (symmetric != 0 && symmetric != 1)
+        return fail(PQG_EINVAL, "symmetric must be 0 or 1 (got %d)", symmetric);
+    if (granularity != PQG_TENSOR && granularity != PQG_ROW && granularity != PQG_GROUP)
+        return fail(PQG_EINVAL, "unknown granularity %d", granularity);
+    if (granularity == PQG_GROUP) {
+        if (group_size != 32 && group_size != 64 && group_size != 128)
+            return fail(PQG_EINVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+        if (cols % group_size != 0)
+            return fail(PQG_EINVAL, "cols (%lld) must be a multiple of group_size (%d)", (long long)cols,
+                        group_size);
+    }
+    return PQG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pqg_abi_version(void) { return PQG_ABI_VERSION; }
+
+const char *pqg_last_error(void) { return g_err; }
+
+size_t pqg_quantize_workspace_bytes(int64_t rows, int64_t cols, int32_t granularity)
+{
+    (void)rows;
+    (void)cols;
+    return pqg::quantize_workspace_bytes(granularity);
+}
+
+int32_t pqg_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols, const float *smooth,
+                     int32_t smooth_mode, int32_t bits, int32_t symmetric, int32_t granularity, int32_t group_size,
+                     void *codes, float *scales, uint8_t *zeros, void *workspace, size_t workspace_bytes,
+                     void *stream)
+{
+    g_err[0] = 0;
+    if (rows < 0 || cols < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (!valid_float_dtype(x_dtype))
+        return fail(PQG_EINVAL, "unknown x_dtype %d", x_dtype);
+    if (int32_t e = check_qspec(bits, symmetric, granularity, group_size, cols))
+        return e;
+    if (smooth_mode != PQG_SMOOTH_NONE && smooth_mode != PQG_SMOOTH_DIV && smooth_mode != PQG_SMOOTH_MUL)
+        return fail(PQG_EINVAL, "unknown smooth_mode %d", smooth_mode);
+    if (cols % 32 != 0)
+        return fail(PQG_EINVAL, "cols (%lld) must be a multiple of 32", (long long)cols);
+    if (granularity == PQG_ROW && cols > 65536)
+        return fail(PQG_EUNSUPPORTED, "per-row quantization supports cols <= 65536 (got %lld)", (long long)cols);
+    if (rows == 0 || cols == 0)
+        return PQG_OK;
+    if (!x || !codes || !scales)
+        return fail(PQG_EINVAL, "x, codes and scales are required");
+    if (smooth_mode != PQG_SMOOTH_NONE && !smooth)
+        return fail(PQG_EINVAL, "smooth vector required for smooth_mode %d", smooth_mode);
+    if (smooth_mode == PQG_SMOOTH_NONE && smooth)
+        return fail(PQG_EINVAL, "smooth vector given with PQG_SMOOTH_NONE");
+    if (symmetric && zeros)
+        return fail(PQG_EINVAL, "zeros must be NULL for symmetric quantization");
+    if (!symmetric && !zeros)
+        return fail(PQG_EINVAL, "zeros is required for asymmetric quantization");
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || (smooth && !aligned(smooth, 16)))
+        return fail(PQG_EINVAL, "misaligned pointer (x, codes: 16 bytes; smooth: 16 bytes; scales: 4 bytes)");
+    const size_t need = pqg::quantize_workspace_bytes(granularity);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return fail(PQG_EINVAL, "workspace of %zu bytes (16-byte aligned) required", need);
+    pqg::QuantArgs a{x, x_dtype == PQG_BF16, rows, cols, smooth, smooth_mode, bits, symmetric != 0,
+                     granularity, group_size, codes, scales, zeros, workspace};
+    return hip_status(pqg::launch_quantize(a, as_stream(stream)), "pqg_quantize launch");
+}
+
+int32_t pqg_dequantize(const void *codes, const float *scales, const uint8_t *zeros, int64_t rows, int64_t cols,
+                       int32_t bits, int32_t symmetric, int32_t granularity, int32_t group_size, void *out,
+                       int32_t out_dtype, void *stream)
+{
+    g_err[0] = 0;
+    if (rows < 0 || cols < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (!valid_float_dtype(out_dtype))
+        return fail(PQG_EINVAL, "unknown out_dtype %d", out_dtype);
+    if (int32_t e = check_qspec(bits, symmetric, granularity, group_size, cols))
+        return e;
+    if (cols % 32 != 0)
+        return fail(PQG_EINVAL, "cols (%lld) must be a multiple of 32", (long long)cols);
+    if (rows == 0 || cols == 0)
+        return PQG_OK;
+    if (!codes || !scales || !out)
+        return fail(PQG_EINVAL, "codes, scales and out are required");
+    if (symmetric && zeros)
+        return fail(PQG_EINVAL, "zeros must be NULL for symmetric codes");
+    if (!symmetric && !zeros)
+        return fail(PQG_EINVAL, "zeros is required for asymmetric codes");
+    if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(scales, 4))
+        return fail(PQG_EINVAL, "misaligned pointer (codes, out: 16 bytes; scales: 4 bytes)");
+    pqg::DequantArgs a{codes, scales, zeros, rows, cols, bits, symmetric != 0, granularity, group_size, out,
+                       out_dtype == PQG_BF16};
+    return hip_status(pqg::launch_dequantize(a, as_stream(stream)), "pqg_dequantize launch");
+}
+
+size_t pqg_smooth_workspace_bytes(int64_t tokens, int64_t out_features, int64_t in_features)
+{
+    if (tokens < 0 || out_features < 0 || in_features < 0)
+        return 0;
+    return pqg::smooth_workspace_bytes(tokens, out_features, in_features);
+}
+
+int32_t pqg_smooth(const void *x, int32_t x_dtype, int64_t tokens, const void *w, int32_t w_dtype,
+                   int64_t out_features, int64_t in_features, double alpha, float *s, void *workspace,
+                   size_t workspace_bytes, void *stream)
+{
+    g_err[0] = 0;
+    if (!valid_float_dtype(x_dtype) || !valid_float_dtype(w_dtype))
+        return fail(PQG_EINVAL, "unknown dtype");
+    if (tokens < 1 || out_features < 1 || in_features < 0)
+        return fail(PQG_EINVAL, "tokens and out_features must be >= 1");
+    if (in_features % 8 != 0)
+        return fail(PQG_EINVAL, "in_features (%lld) must be a multiple of 8", (long long)in_features);
+    if (!(alpha >= 0.0 && alpha <= 1.0))
+        return fail(PQG_EINVAL, "alpha must lie in [0, 1]");
+    if (in_features == 0)
+        return PQG_OK;
+    if (!x || !w || !s)
+        return fail(PQG_EINVAL, "x, w and s are required");
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(s, 4))
+        return fail(PQG_EINVAL, "misaligned pointer (x, w: 16 bytes; s: 4 bytes)");
+    const size_t need = pqg::smooth_workspace_bytes(tokens, out_features, in_features);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+        return fail(PQG_EINVAL, "workspace of %zu bytes (16-byte aligned) required", need);
+    pqg::SmoothArgs a{x, x_dtype == PQG_BF16, tokens, w, w_dtype == PQG_BF16, out_features, in_features, alpha, s,
+                      workspace};
+    return hip_status(pqg::launch_smooth(a, as_stream(stream)), "pqg_smooth launch");
+}
+
+int32_t pqg_qlinear_w4a16(const void *x, int64_t M, int64_t N, int64_t K, const uint8_t *w_packed,
+                          const float *scales, const uint8_t *zeros, int32_t group_size, int32_t symmetric, void *y,
+                          int32_t y_dtype, void *stream)
+{
+    g_err[0] = 0;
+    if (M < 0 || N < 0 || K < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (!valid_float_dtype(y_dtype))
+        return fail(PQG_EINVAL, "unknown y_dtype %d", y_dtype);
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(PQG_EINVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+    if (K % group_size != 0)
+        return fail(PQG_EINVAL, "K (%lld) must be a multiple of group_size (%d)", (long long)K, group_size);
+    if (symmetric != 0 && symmetric != 1)
+        return fail(PQG_EINVAL, "symmetric must be 0 or 1");
+    if (M == 0 || N == 0)
+        return PQG_OK;
+    if (K == 0)
+        return fail(PQG_EUNSUPPORTED, "K == 0");
+    if (!x || !w_packed || !scales || !y)
+        return fail(PQG_EINVAL, "x, w_packed, scales and y are required");
+    if (symmetric && zeros)
+        return fail(PQG_EINVAL, "zeros must be NULL for symmetric codes");
+    if (!symmetric && !zeros)
+        return fail(PQG_EINVAL, "zeros is required for asymmetric codes");
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(scales, 4) || !aligned(y, 4))
+        return fail(PQG_EINVAL, "misaligned pointer (x, w_packed: 16 bytes; scales, y: 4 bytes)");
+    pqg::W4A16Args a{static_cast<const uint16_t *>(x), M, N, K, w_packed, scales, zeros, group_size, symmetric != 0,
+                     y, y_dtype == PQG_BF16};
+    return hip_status(pqg::launch_w4a16(a, as_stream(stream)), "pqg_qlinear_w4a16 launch");
+}
+
+int32_t pqg_qlinear_w8a8(const void *x, const float *smooth, const int8_t *w_q, const float *w_scales, int64_t M,
+                         int64_t N, int64_t K, void *y, int32_t y_dtype, int8_t *x_q, float *x_scales, void *stream)
+{
+    g_err[0] = 0;
+    if (M < 0 || N < 0 || K < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (!valid_float_dtype(y_dtype))
+        return fail(PQG_EINVAL, "unknown y_dtype %d", y_dtype);
+    if (K % 32 != 0)
+        return fail(PQG_EINVAL, "K (%lld) must be a multiple of 32", (long long)K);
+    if (K > 65536)
+        return fail(PQG_EUNSUPPORTED, "K (%lld) above 65536", (long long)K);
+    if (M == 0 || N == 0)
+        return PQG_OK;
+    if (K == 0)
+        return fail(PQG_EUNSUPPORTED, "K == 0");
+    if (!x || !w_q || !w_scales || !y || !x_q || !x_scales)
+        return fail(PQG_EINVAL, "x, w_q, w_scales, y, x_q and x_scales are required");
+    if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(x_q, 16) || !aligned(w_scales, 4) ||
+        !aligned(x_scales, 4) || !aligned(y, 4) || (smooth && !aligned(smooth, 16)))
+        return fail(PQG_EINVAL, "misaligned pointer (x, w_q, x_q, smooth: 16 bytes; scales, y: 4 bytes)");
+    hipStream_t st = as_stream(stream);
+    pqg::QuantArgs q{x, true, M, K, smooth, smooth ? pqg::SMOOTH_DIV : pqg::SMOOTH_NONE, 8, true, pqg::QG_ROW, 0,
+                     x_q, x_scales, nullptr, nullptr};
+    if (int32_t e = hip_status(pqg::launch_quantize(q, st), "pqg_qlinear_w8a8 activation quantize launch"))
+        return e;
+    pqg::GemmI8Args g{x_q, w_q, M, N, K, x_scales, w_scales, y, y_dtype == PQG_BF16};
+    return hip_status(pqg::launch_gemm_i8(g, st), "pqg_qlinear_w8a8 gemm launch");
+}
+
+int32_t pqg_gemm_s8s8s32(const int8_t *a, const int8_t *b, int64_t M, int64_t N, int64_t K, int32_t *c,
+                         void *stream)
+{
+    g_err[0] = 0;
+    if (M < 0 || N < 0 || K < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (K % 16 != 0)
+        return fail(PQG_EINVAL, "K (%lld) must be a multiple of 16", (long long)K);
+    if (M == 0 || N == 0)
+        return PQG_OK;
+    if (!a || !b || !c)
+        return fail(PQG_EINVAL, "a, b and c are required");
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 4))
+        return fail(PQG_EINVAL, "misaligned pointer (a, b: 16 bytes; c: 4 bytes)");
+    pqg::GemmI8Args g{a, b, M, N, K, nullptr, nullptr, c, false};
+    return hip_status(pqg::launch_gemm_i8(g, as_stream(stream)), "pqg_gemm_s8s8s32 launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of the quantized linear layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pqg {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Load 8 consecutive elements (bf16 or fp32) as fp32. `p` must be 16-byte aligned.
+template <typename XT>
+__device__ __forceinline__ void load8(const XT *__restrict__ p, float v[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t *__restrict__ p, float v[8])
+{
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    v[0] = bf16_lo(u.x);
+    v[1] = bf16_hi(u.x);
+    v[2] = bf16_lo(u.y);
+    v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z);
+    v[5] = bf16_hi(u.z);
+    v[6] = bf16_lo(u.w);
+    v[7] = bf16_hi(u.w);
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float *__restrict__ p, float v[8])
+{
+    float4 a = reinterpret_cast<const float4 *>(p)[0];
+    float4 b = reinterpret_cast<const float4 *>(p)[1];
+    v[0] = a.x;
+    v[1] = a.y;
+    v[2] = a.z;
+    v[3] = a.w;
+    v[4] = b.x;
+    v[5] = b.y;
+    v[6] = b.z;
+    v[7] = b.w;
+}
+
+// ------------------------------------------------------------------ exact rounding of a quotient
+
+// round-half-to-even of the correctly rounded fp32 quotient v / s, given r = 1/s (correctly rounded).
+//
+// Fast path: t = v * r differs from fl(v / s) by at most |v/s| * (3 * 2^-24) (one rounding in r, one in
+// the product, one in the reference quotient). If t is farther than |t| * 2^-20 from the nearest
+// half-integer, fl(v / s) lies strictly inside the same rounding interval as t and both round to the same
+// integer. t - rint(t) and 0.5 - |.| are exact in that regime (Sterbenz), so the test itself is exact.
+// Otherwise (a near-tie, or a non-finite t when s is subnormal) the correctly rounded division decides.
+__device__ __forceinline__ float rne_quotient(float v, float s, float r)
+{
+    float t = v * r;
+    float q = __builtin_rintf(t);
+    float margin = 0.5f - __builtin_fabsf(t - q);
+    if (!(margin > __builtin_fabsf(t) * 0x1p-20f))
+        q = __builtin_rintf(v / s);
+    return q;
+}
+
+// ------------------------------------------------------------------ segment parameters
+
+// Scale / zero / code range of one segment from its range statistics. Mirrors the definition:
+// symmetric: s = absmax / qmax; asymmetric: range widened to contain 0, s = (hi - lo) / (2^b - 1),
+// z = rne(-lo / s) clamped. A step of 0 (all-zero or underflowing range) becomes s = 1, z = 0.
+struct SegParams {
+    float s, r;  // scale and its correctly rounded reciprocal
+    float z;     // zero point (integer valued)
+    float qmin, qmax;
+};
+
+template <int BITS, bool SYM>
+__device__ __forceinline__ SegParams seg_params(float absmax, float lo, float hi)
+{
+    SegParams p;
+    if (SYM) {
+        constexpr int qm = (1 << (BITS - 1)) - 1;
+        p.qmax = (float)qm;
+        p.qmin = -(float)qm;
+        p.z = 0.0f;
+        p.s = absmax / (float)qm;
+        if (!(p.s > 0.0f))
+            p.s = 1.0f;
+    } else {
+        constexpr int qm = (1 << BITS) - 1;
+        p.qmax = (float)qm;
+        p.qmin = 0.0f;
+        lo = lo > 0.0f ? 0.0f : lo;
+        hi = hi < 0.0f ? 0.0f : hi;
+        p.s = (hi - lo) / (float)qm;
+        if (!(p.s > 0.0f)) {
+            p.s = 1.0f;
+            p.z = 0.0f;
+        } else {
+            float z = __builtin_rintf(-lo / p.s);
+            p.z = __builtin_fminf(__builtin_fmaxf(z, 0.0f), (float)qm);
+        }
+    }
+    p.r = 1.0f / p.s;
+    return p;
+}
+
+// Integer code of one (smoothed) value: clamp(rne(v / s) + z, qmin, qmax).
+__device__ __forceinline__ int code_of(float v, const SegParams &p)
+{
+    float q = rne_quotient(v, p.s, p.r) + p.z;
+    q = __builtin_fminf(__builtin_fmaxf(q, p.qmin), p.qmax);
+    return (int)q;
+}
+
+// ------------------------------------------------------------------ wave reductions
+
+template <int WIDTH>
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1)
+        v = __builtin_fmaxf(v, __shfl_xor(v, off, WIDTH));
+    return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float wave_min(float v)
+{
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1)
+        v = __builtin_fminf(v, __shfl_xor(v, off, WIDTH));
+    return v;
+}
+
+// Sum over a full wave; every lane receives the total. Order is fixed (butterfly), so the result is
+// deterministic.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+}  // namespace pqg

@@ -1,0 +1,396 @@
+// quantize.hip -- affine quantize / dequantize kernels for gfx950.
+//
+// Defines  q = clamp(round(x / s) + z, qmin, qmax)  and  x_hat = s (q - z)  ("量化、蒸馏与模型压缩", core
+// formula; "第11章 模型量化与压缩" §11.1.1) at tensor, row and group granularity (§11.1.3 Table 11-1), with
+// the optional SmoothQuant scaling of the input channels applied first (§11.4.2, §11.4.5).
+//
+// Layout on the device. Every kernel walks the tensor in chunks of 8 consecutive elements of a row: one
+// 16-byte load of bf16 (two of fp32), 8 codes -> one 32-bit store (INT4, 8 nibbles) or 64-bit store
+// (INT8). Groups of g elements are contiguous in row-major order (cols % g == 0), so a group is g/8
+// consecutive lanes of one wave and its range is reduced with in-wave shuffles; no LDS, no barrier.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace pqg {
+
+// ------------------------------------------------------------------ shared per-chunk pieces
+
+template <typename XT, int SMOOTH>
+__device__ __forceinline__ void load_smoothed8(const XT *__restrict__ x, const float *__restrict__ smooth,
+                                               int64_t elem, int64_t cols, float v[8])
+{
+    load8<XT>(x + elem, v);
+    if (SMOOTH != SMOOTH_NONE) {
+        float sv[8];
+        load8<float>(smooth + (elem % cols), sv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = (SMOOTH == SMOOTH_DIV) ? v[i] / sv[i] : v[i] * sv[i];
+    }
+}
+
+template <bool SYM>
+__device__ __forceinline__ void range8(const float v[8], float &absmax, float &lo, float &hi)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (SYM) {
+            absmax = __builtin_fmaxf(absmax, __builtin_fabsf(v[i]));
+        } else {
+            lo = __builtin_fminf(lo, v[i]);
+            hi = __builtin_fmaxf(hi, v[i]);
+        }
+    }
+}
+
+// Quantize 8 values and store their codes at element offset `elem` of the code tensor.
+template <int BITS>
+__device__ __forceinline__ void store_codes8(const float v[8], const SegParams &p, void *__restrict__ codes,
+                                             int64_t elem)
+{
+    if (BITS == 4) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            packed |= ((uint32_t)code_of(v[i], p) & 0xFu) << (4 * i);
+        reinterpret_cast<uint32_t *>(codes)[elem / 8] = packed;
+    } else {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo |= ((uint32_t)code_of(v[i], p) & 0xFFu) << (8 * i);
+            hi |= ((uint32_t)code_of(v[i + 4], p) & 0xFFu) << (8 * i);
+        }
+        reinterpret_cast<uint2 *>(codes)[elem / 8] = make_uint2(lo, hi);
+    }
+}
+
+// ------------------------------------------------------------------ per-group
+
+// One thread per chunk of 8; a group is LPG = g/8 consecutive lanes.
+template <typename XT, int BITS, bool SYM, int SMOOTH, int G>
+__global__ __launch_bounds__(256) void k_quant_group(const XT *__restrict__ x, const float *__restrict__ smooth,
+                                                     int64_t n_chunks, int64_t cols, void *__restrict__ codes,
+                                                     float *__restrict__ scales, uint8_t *__restrict__ zeros)
+{
+    constexpr int LPG = G / 8;
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // n_chunks is a multiple of LPG and groups are lane-aligned, so a group is either wholly in range or
+    // wholly out of it; the shuffles below only read lanes of the same group.
+    if (c >= n_chunks)
+        return;
+    float v[8];
+    load_smoothed8<XT, SMOOTH>(x, smooth, c * 8, cols, v);
+    float absmax = 0.0f, lo = v[0], hi = v[0];
+    range8<SYM>(v, absmax, lo, hi);
+    if (SYM) {
+        absmax = wave_max<LPG>(absmax);
+    } else {
+        lo = wave_min<LPG>(lo);
+        hi = wave_max<LPG>(hi);
+    }
+    const SegParams p = seg_params<BITS, SYM>(absmax, lo, hi);
+    store_codes8<BITS>(v, p, codes, c * 8);
+    if ((c % LPG) == 0) {
+        scales[c / LPG] = p.s;
+        if (!SYM)
+            zeros[c / LPG] = (uint8_t)p.z;
+    }
+}
+
+// ------------------------------------------------------------------ per-row
+
+constexpr int kRowCache = 8;  // chunks of 8 kept in registers per thread: cols <= 1024 * 8 * 8
+
+template <int BITS, bool SYM, int NT>
+__device__ __forceinline__ void block_range(float &absmax, float &lo, float &hi, float *red)
+{
+    // red: LDS of 3 * (NT / 64) floats
+    constexpr int NW = NT / kWave;
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    if (SYM) {
+        absmax = wave_max<kWave>(absmax);
+    } else {
+        lo = wave_min<kWave>(lo);
+        hi = wave_max<kWave>(hi);
+    }
+    if (lane == 0) {
+        red[wv] = absmax;
+        red[NW + wv] = lo;
+        red[2 * NW + wv] = hi;
+    }
+    __syncthreads();
+    absmax = red[0];
+    lo = red[NW];
+    hi = red[2 * NW];
+    for (int i = 1; i < NW; ++i) {
+        absmax = __builtin_fmaxf(absmax, red[i]);
+        lo = __builtin_fminf(lo, red[NW + i]);
+        hi = __builtin_fmaxf(hi, red[2 * NW + i]);
+    }
+}
+
+// One block of NT threads per row. The smoothed values are computed once and kept in registers between
+// the range pass and the code pass.
+template <typename XT, int BITS, bool SYM, int SMOOTH, int NT>
+__global__ __launch_bounds__(NT) void k_quant_row(const XT *__restrict__ x, const float *__restrict__ smooth,
+                                                  int64_t cols, void *__restrict__ codes,
+                                                  float *__restrict__ scales, uint8_t *__restrict__ zeros)
+{
+    __shared__ float red[3 * (NT / kWave)];
+    const int64_t row = blockIdx.x;
+    const int64_t nch = cols / 8;
+    const int64_t base = row * cols;
+    float v[kRowCache][8];
+    float absmax = 0.0f, lo = 0.0f, hi = 0.0f;
+    bool first = true;
+#pragma unroll
+    for (int i = 0; i < kRowCache; ++i) {
+        const int64_t ch = threadIdx.x + (int64_t)i * NT;
+        if (ch < nch) {
+            load_smoothed8<XT, SMOOTH>(x, smooth, base + ch * 8, cols, v[i]);
+            if (first) {
+                lo = hi = v[i][0];
+                first = false;
+            }
+            range8<SYM>(v[i], absmax, lo, hi);
+        }
+    }
+    if (first) {  // a thread without elements must not disturb the reduction
+        lo = __builtin_huge_valf();
+        hi = -__builtin_huge_valf();
+    }
+    block_range<BITS, SYM, NT>(absmax, lo, hi, red);
+    const SegParams p = seg_params<BITS, SYM>(absmax, lo, hi);
+#pragma unroll
+    for (int i = 0; i < kRowCache; ++i) {
+        const int64_t ch = threadIdx.x + (int64_t)i * NT;
+        if (ch < nch)
+            store_codes8<BITS>(v[i], p, codes, base + ch * 8);
+    }
+    if (threadIdx.x == 0) {
+        scales[row] = p.s;
+        if (!SYM)
+            zeros[row] = (uint8_t)p.z;
+    }
+}
+
+// ------------------------------------------------------------------ per-tensor (two launches)
+
+constexpr int kTensorBlocks = 1024;
+
+// Pass 1: per-block range over a grid-stride range of chunks -> ws[3 * blockIdx.x + {0,1,2}].
+template <typename XT, bool SYM, int SMOOTH>
+__global__ __launch_bounds__(256) void k_tensor_range(const XT *__restrict__ x, const float *__restrict__ smooth,
+                                                      int64_t n_chunks, int64_t cols, float *__restrict__ ws)
+{
+    __shared__ float red[3 * 4];
+    float absmax = 0.0f, lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n_chunks; c += (int64_t)gridDim.x * 256) {
+        float v[8];
+        load_smoothed8<XT, SMOOTH>(x, smooth, c * 8, cols, v);
+        range8<SYM>(v, absmax, lo, hi);
+    }
+    block_range<8, SYM, 256>(absmax, lo, hi, red);
+    if (threadIdx.x == 0) {
+        ws[3 * blockIdx.x + 0] = absmax;
+        ws[3 * blockIdx.x + 1] = lo;
+        ws[3 * blockIdx.x + 2] = hi;
+    }
+}
+
+// Pass 2: every block reduces the partial ranges itself (max / min are exact and order independent, so
+// all blocks agree), then quantizes its grid-stride share.
+template <typename XT, int BITS, bool SYM, int SMOOTH>
+__global__ __launch_bounds__(256) void k_tensor_quant(const XT *__restrict__ x, const float *__restrict__ smooth,
+                                                      int64_t n_chunks, int64_t cols, const float *__restrict__ ws,
+                                                      int n_partials, void *__restrict__ codes,
+                                                      float *__restrict__ scales, uint8_t *__restrict__ zeros)
+{
+    __shared__ float red[3 * 4];
+    float absmax = 0.0f, lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+    for (int i = threadIdx.x; i < n_partials; i += 256) {
+        absmax = __builtin_fmaxf(absmax, ws[3 * i + 0]);
+        lo = __builtin_fminf(lo, ws[3 * i + 1]);
+        hi = __builtin_fmaxf(hi, ws[3 * i + 2]);
+    }
+    block_range<BITS, SYM, 256>(absmax, lo, hi, red);
+    const SegParams p = seg_params<BITS, SYM>(absmax, lo, hi);
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n_chunks; c += (int64_t)gridDim.x * 256) {
+        float v[8];
+        load_smoothed8<XT, SMOOTH>(x, smooth, c * 8, cols, v);
+        store_codes8<BITS>(v, p, codes, c * 8);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        scales[0] = p.s;
+        if (!SYM)
+            zeros[0] = (uint8_t)p.z;
+    }
+}
+
+// ------------------------------------------------------------------ dequantize
+
+template <int BITS, bool SYM, int GRAN, bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_dequant(const void *__restrict__ codes, const float *__restrict__ scales,
+                                                 const uint8_t *__restrict__ zeros, int64_t n_chunks,
+                                                 int64_t cols, int group_size, void *__restrict__ out)
+{
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= n_chunks)
+        return;
+    const int64_t e = c * 8;
+    const int64_t seg = (GRAN == QG_TENSOR) ? 0 : (GRAN == QG_ROW) ? e / cols : e / group_size;
+    const float s = scales[seg];
+    const int z = SYM ? 0 : (int)zeros[seg];
+    int q[8];
+    if (BITS == 4) {
+        const uint32_t w = reinterpret_cast<const uint32_t *>(codes)[c];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int nib = (int)((w >> (4 * i)) & 0xFu);
+            q[i] = (SYM && nib >= 8) ? nib - 16 : nib;
+        }
+    } else {
+        const uint2 w = reinterpret_cast<const uint2 *>(codes)[c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int b0 = (int)((w.x >> (8 * i)) & 0xFFu), b1 = (int)((w.y >> (8 * i)) & 0xFFu);
+            q[i] = (SYM && b0 >= 128) ? b0 - 256 : b0;
+            q[i + 4] = (SYM && b1 >= 128) ? b1 - 256 : b1;
+        }
+    }
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = s * (float)(q[i] - z);
+    if (OUT_BF16) {
+        uint4 o = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                             pack_bf16x2(v[6], v[7]));
+        reinterpret_cast<uint4 *>(out)[c] = o;
+    } else {
+        float4 *o = reinterpret_cast<float4 *>(out) + 2 * c;
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
+// ------------------------------------------------------------------ host-side dispatch
+
+namespace {
+
+inline unsigned nblocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+template <typename XT, int BITS, bool SYM, int SMOOTH>
+hipError_t quant_dispatch_gran(const QuantArgs &a, hipStream_t st)
+{
+    const int64_t n_chunks = a.rows * a.cols / 8;
+    const XT *x = static_cast<const XT *>(a.x);
+    if (a.granularity == QG_GROUP) {
+        const unsigned nb = nblocks(n_chunks, 256);
+        switch (a.group_size) {
+        case 32:
+            k_quant_group<XT, BITS, SYM, SMOOTH, 32><<<nb, 256, 0, st>>>(x, a.smooth, n_chunks, a.cols, a.codes,
+                                                                         a.scales, a.zeros);
+            break;
+        case 64:
+            k_quant_group<XT, BITS, SYM, SMOOTH, 64><<<nb, 256, 0, st>>>(x, a.smooth, n_chunks, a.cols, a.codes,
+                                                                         a.scales, a.zeros);
+            break;
+        default:
+            k_quant_group<XT, BITS, SYM, SMOOTH, 128><<<nb, 256, 0, st>>>(x, a.smooth, n_chunks, a.cols, a.codes,
+                                                                          a.scales, a.zeros);
+            break;
+        }
+    } else if (a.granularity == QG_ROW) {
+        // threads per row: enough that each keeps at most kRowCache chunks in registers
+        const int64_t nch = a.cols / 8;
+        const unsigned grid = (unsigned)a.rows;
+        if (nch <= 256 * kRowCache / 4)  // short rows: 64 threads
+            k_quant_row<XT, BITS, SYM, SMOOTH, 64><<<grid, 64, 0, st>>>(x, a.smooth, a.cols, a.codes, a.scales,
+                                                                       a.zeros);
+        else if (nch <= 256 * kRowCache)
+            k_quant_row<XT, BITS, SYM, SMOOTH, 256><<<grid, 256, 0, st>>>(x, a.smooth, a.cols, a.codes, a.scales,
+                                                                         a.zeros);
+        else
+            k_quant_row<XT, BITS, SYM, SMOOTH, 1024><<<grid, 1024, 0, st>>>(x, a.smooth, a.cols, a.codes, a.scales,
+                                                                           a.zeros);
+    } else {
+        float *ws = static_cast<float *>(a.workspace);
+        const int nb = (int)std::min<int64_t>(kTensorBlocks, std::max<int64_t>(1, (n_chunks + 255) / 256));
+        k_tensor_range<XT, SYM, SMOOTH><<<nb, 256, 0, st>>>(x, a.smooth, n_chunks, a.cols, ws);
+        k_tensor_quant<XT, BITS, SYM, SMOOTH><<<nb, 256, 0, st>>>(x, a.smooth, n_chunks, a.cols, ws, nb, a.codes,
+                                                                  a.scales, a.zeros);
+    }
+    return hipGetLastError();
+}
+
+template <typename XT, int BITS, bool SYM>
+hipError_t quant_dispatch_smooth(const QuantArgs &a, hipStream_t st)
+{
+    switch (a.smooth_mode) {
+    case SMOOTH_DIV:
+        return quant_dispatch_gran<XT, BITS, SYM, SMOOTH_DIV>(a, st);
+    case SMOOTH_MUL:
+        return quant_dispatch_gran<XT, BITS, SYM, SMOOTH_MUL>(a, st);
+    default:
+        return quant_dispatch_gran<XT, BITS, SYM, SMOOTH_NONE>(a, st);
+    }
+}
+
+template <typename XT>
+hipError_t quant_dispatch_type(const QuantArgs &a, hipStream_t st)
+{
+    if (a.bits == 4)
+        return a.symmetric ? quant_dispatch_smooth<XT, 4, true>(a, st) : quant_dispatch_smooth<XT, 4, false>(a, st);
+    return a.symmetric ? quant_dispatch_smooth<XT, 8, true>(a, st) : quant_dispatch_smooth<XT, 8, false>(a, st);
+}
+
+template <int BITS, bool SYM, int GRAN>
+hipError_t dequant_out(const DequantArgs &a, hipStream_t st)
+{
+    const int64_t n_chunks = a.rows * a.cols / 8;
+    const unsigned nb = nblocks(n_chunks, 256);
+    if (a.out_bf16)
+        k_dequant<BITS, SYM, GRAN, true><<<nb, 256, 0, st>>>(a.codes, a.scales, a.zeros, n_chunks, a.cols,
+                                                             a.group_size, a.out);
+    else
+        k_dequant<BITS, SYM, GRAN, false><<<nb, 256, 0, st>>>(a.codes, a.scales, a.zeros, n_chunks, a.cols,
+                                                              a.group_size, a.out);
+    return hipGetLastError();
+}
+
+template <int BITS, bool SYM>
+hipError_t dequant_gran(const DequantArgs &a, hipStream_t st)
+{
+    switch (a.granularity) {
+    case QG_TENSOR:
+        return dequant_out<BITS, SYM, QG_TENSOR>(a, st);
+    case QG_ROW:
+        return dequant_out<BITS, SYM, QG_ROW>(a, st);
+    default:
+        return dequant_out<BITS, SYM, QG_GROUP>(a, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t st)
+{
+    if (a.x_bf16)
+        return quant_dispatch_type<uint16_t>(a, st);
+    return quant_dispatch_type<float>(a, st);
+}
+
+size_t quantize_workspace_bytes(int32_t granularity)
+{
+    return granularity == QG_TENSOR ? (size_t)kTensorBlocks * 3 * sizeof(float) : 0;
+}
+
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st)
+{
+    if (a.bits == 4)
+        return a.symmetric ? dequant_gran<4, true>(a, st) : dequant_gran<4, false>(a, st);
+    return a.symmetric ? dequant_gran<8, true>(a, st) : dequant_gran<8, false>(a, st);
+}
+
+}  // namespace pqg

@@ -1,0 +1,110 @@
+"""The C ABI library on the host (no GPU): it loads, exports every entry point include/pqg.h declares, and
+rejects bad arguments with a status and a message before anything is enqueued. No call here reaches a
+kernel launch: every one fails validation or is an empty (zero-row) no-op."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pqg.h")
+
+pqg = pytest.importorskip("post_quantization_group_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pqg.LIB_PATH):
+        pytest.fail("libpqg.so is not built; run __graft_entry__.build()")
+    return pqg.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(pqg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(pqg.EXPORTS)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.pqg_abi_version() == pqg.ABI_VERSION
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10001)
+
+
+def q(lib, **kw):
+    a = dict(x=FAKE, x_dtype=1, rows=4, cols=256, smooth=None, smooth_mode=0, bits=4, symmetric=1, gran=2, gs=128,
+             codes=FAKE, scales=FAKE, zeros=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.pqg_quantize(a["x"], a["x_dtype"], a["rows"], a["cols"], a["smooth"], a["smooth_mode"], a["bits"],
+                            a["symmetric"], a["gran"], a["gs"], a["codes"], a["scales"], a["zeros"], a["ws"],
+                            a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(bits=5), "bits"), (dict(gs=48), "group_size"), (dict(cols=200, gran=1), "multiple of 32"),
+    (dict(cols=288, gs=128), "multiple of group_size"), (dict(x_dtype=7), "x_dtype"), (dict(gran=9), "granularity"),
+    (dict(symmetric=0), "zeros"), (dict(zeros=FAKE), "zeros must be NULL"), (dict(x=None), "required"),
+    (dict(x=MISALIGNED), "misaligned"), (dict(smooth_mode=1), "smooth vector"), (dict(smooth_mode=4), "smooth_mode"),
+    (dict(gran=0), "workspace"), (dict(rows=-1), "negative"), (dict(gran=1, cols=65568), "65536"),
+])
+def test_quantize_rejects(lib, kw, needle):
+    rc = q(lib, **kw)
+    assert rc in (pqg.EINVAL, pqg.EUNSUPPORTED)
+    assert needle in lib.pqg_last_error().decode()
+
+
+def test_quantize_empty_is_ok(lib):
+    assert q(lib, rows=0, x=None, codes=None, scales=None) == pqg.OK
+    assert lib.pqg_last_error().decode() == ""
+
+
+def test_workspace_sizes(lib):
+    assert lib.pqg_quantize_workspace_bytes(100, 256, pqg.GROUP) == 0
+    assert lib.pqg_quantize_workspace_bytes(100, 256, pqg.ROW) == 0
+    assert lib.pqg_quantize_workspace_bytes(100, 256, pqg.TENSOR) > 0
+    assert lib.pqg_smooth_workspace_bytes(2048, 11008, 4096) >= 2 * 4096 * 4
+
+
+def test_dequantize_rejects(lib):
+    rc = lib.pqg_dequantize(FAKE, FAKE, None, 4, 256, 4, 0, 2, 128, FAKE, 0, None)
+    assert rc == pqg.EINVAL and "zeros" in lib.pqg_last_error().decode()
+    rc = lib.pqg_dequantize(FAKE, FAKE, None, 4, 256, 4, 1, 2, 128, FAKE, 3, None)
+    assert rc == pqg.EINVAL and "out_dtype" in lib.pqg_last_error().decode()
+
+
+def test_smooth_rejects(lib):
+    rc = lib.pqg_smooth(FAKE, 1, 16, FAKE, 1, 16, 256, 1.5, FAKE, FAKE, 1 << 20, None)
+    assert rc == pqg.EINVAL and "alpha" in lib.pqg_last_error().decode()
+    rc = lib.pqg_smooth(FAKE, 1, 16, FAKE, 1, 16, 256, 0.5, FAKE, FAKE, 8, None)
+    assert rc == pqg.EINVAL and "workspace" in lib.pqg_last_error().decode()
+    rc = lib.pqg_smooth(FAKE, 1, 16, FAKE, 1, 16, 252, 0.5, FAKE, FAKE, 1 << 20, None)
+    assert rc == pqg.EINVAL and "multiple of 8" in lib.pqg_last_error().decode()
+
+
+def test_w4a16_rejects(lib):
+    rc = lib.pqg_qlinear_w4a16(FAKE, 1, 64, 256, FAKE, FAKE, None, 96, 1, FAKE, 1, None)
+    assert rc == pqg.EINVAL and "group_size" in lib.pqg_last_error().decode()
+    rc = lib.pqg_qlinear_w4a16(FAKE, 1, 64, 200, FAKE, FAKE, None, 32, 1, FAKE, 1, None)
+    assert rc == pqg.EINVAL and "multiple of group_size" in lib.pqg_last_error().decode()
+    rc = lib.pqg_qlinear_w4a16(FAKE, 1, 64, 256, FAKE, FAKE, None, 32, 0, FAKE, 1, None)
+    assert rc == pqg.EINVAL and "zeros" in lib.pqg_last_error().decode()
+    assert lib.pqg_qlinear_w4a16(None, 0, 64, 256, None, None, None, 32, 1, None, 1, None) == pqg.OK
+
+
+def test_w8a8_and_gemm_reject(lib):
+    rc = lib.pqg_qlinear_w8a8(FAKE, None, FAKE, FAKE, 4, 64, 100, FAKE, 1, FAKE, FAKE, None)
+    assert rc == pqg.EINVAL and "multiple of 32" in lib.pqg_last_error().decode()
+    rc = lib.pqg_qlinear_w8a8(FAKE, None, FAKE, FAKE, 4, 64, 256, FAKE, 1, None, FAKE, None)
+    assert rc == pqg.EINVAL and "required" in lib.pqg_last_error().decode()
+    rc = lib.pqg_gemm_s8s8s32(FAKE, FAKE, 4, 4, 24, FAKE, None)
+    assert rc == pqg.EINVAL and "multiple of 16" in lib.pqg_last_error().decode()
+    rc = lib.pqg_gemm_s8s8s32(MISALIGNED, FAKE, 4, 4, 32, FAKE, None)
+    assert rc == pqg.EINVAL and "misaligned" in lib.pqg_last_error().decode()

@@ -1,0 +1,339 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle, on the same seeded inputs.
+
+Bar: integer codes, packed bytes, fp32 scales, zero points, smoothing factors (alpha in {0, 0.5, 1}) and
+INT32 accumulators bit-exact; float outputs within a normwise relative error of 5e-3 (bf16 outputs) or
+1e-5 (fp32 outputs). Full-size workloads are checked on sampled rows the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import announce, bf16_tensor_bits, normwise, to_f64, to_gpu, to_gpu_bf16
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 5e-3
+TOL_F32 = 1e-5
+
+
+def gpu_quant(pqg, x_gpu, bits, sym, gran, gs=0, smooth=None, mode=0):
+    codes, s, z = pqg.quantize(x_gpu, bits, sym, gran, gs, smooth, mode)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), s.cpu().numpy(), None if z is None else z.cpu().numpy()
+
+
+def oracle_codes_bytes(q, bits, sym):
+    """The oracle's codes in the library's storage format (packed nibbles or plain bytes)."""
+    if bits == 4:
+        return oracle.pack_int4(q)
+    return q.astype(np.int8) if sym else q.astype(np.uint8)
+
+
+def assert_quant_equal(gpu, ora, bits, sym):
+    codes, s, z = gpu
+    q, so, zo = ora
+    assert np.array_equal(s.view(np.uint32), so.view(np.uint32)), "scales differ"
+    if not sym:
+        assert np.array_equal(z, zo), "zero points differ"
+    want = oracle_codes_bytes(q, bits, sym)
+    assert codes.shape == want.shape
+    bad = np.nonzero(codes.view(np.uint8) != want.view(np.uint8))
+    assert bad[0].size == 0, "codes differ at %s" % (list(zip(*[b[:5] for b in bad])),)
+
+
+# --------------------------------------------------------------------------- quantize / dequantize
+
+QUANT_CASES = [
+    # bits, sym, gran, gs, smooth_mode
+    (4, True, 2, 128, 0), (4, True, 2, 64, 0), (4, True, 2, 32, 0),
+    (4, False, 2, 128, 0), (4, False, 2, 64, 0), (4, False, 2, 32, 0),
+    (8, True, 2, 128, 0), (8, False, 2, 32, 0),
+    (8, True, 1, 0, 0), (8, False, 1, 0, 0), (4, True, 1, 0, 0), (4, False, 1, 0, 0),
+    (8, True, 0, 0, 0), (8, False, 0, 0, 0), (4, True, 0, 0, 0), (4, False, 0, 0, 0),
+    (8, True, 1, 0, 1), (8, True, 1, 0, 2), (4, True, 2, 128, 1), (8, False, 0, 0, 2),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", QUANT_CASES)
+@pytest.mark.parametrize("shape", [(37, 256), (3, 2112), (1, 32)])
+def test_quantize_bitexact_small(gpu_lib, case, dtype, shape):
+    bits, sym, gran, gs, mode = case
+    rows, cols = shape
+    if gran == 2 and cols % gs:
+        pytest.skip("cols not a multiple of g")
+    announce("quantize %s %s %s" % (case, dtype, shape))
+    rng = np.random.default_rng(hash((case, dtype, shape)) % 2 ** 32)
+    x32 = (rng.standard_normal(shape) * rng.uniform(0.01, 2.0, size=(rows, 1))).astype(np.float32)
+    x32[0, : min(cols, 64)] += 1.5  # a shifted block: one-signed groups for the asymmetric path
+    if rows > 2:
+        x32[2, :] = 0.0  # an all-zero row / groups
+    if dtype == "bf16":
+        xh = W.bf16_bits(x32)
+        xg = to_gpu_bf16(xh)
+    else:
+        xh = x32
+        xg = to_gpu(x32)
+    sm = None
+    if mode:
+        sm = rng.uniform(0.25, 4.0, size=cols).astype(np.float32)
+    gpu = gpu_quant(gpu_lib, xg, bits, sym, gran, gs, None if sm is None else to_gpu(sm), mode)
+    ora = oracle.quantize(xh, bits, sym, gran, gs, sm, mode)
+    assert_quant_equal(gpu, ora, bits, sym)
+
+
+def test_quantize_tiny_config(gpu_lib):
+    """256x512 fp32 with 0.5 % x20 outliers, symmetric INT4 g=128: codes, packed bytes and scales exact."""
+    announce("tiny quantize")
+    d = W.tiny()
+    gpu = gpu_quant(gpu_lib, to_gpu(d["w"]), 4, True, 2, 128)
+    ora = oracle.quantize(d["w"], 4, True, 2, 128)
+    assert_quant_equal(gpu, ora, 4, True)
+    assert gpu[1].size == 256 * 512 // 128
+
+
+def test_quantize_attn7b_full(gpu_lib):
+    """4096x4096 bf16, symmetric INT4 g=128: all 131,072 groups bit-exact."""
+    announce("attn7b quantize")
+    d = W.attn7b(ms=(1,))
+    gpu = gpu_quant(gpu_lib, to_gpu_bf16(d["w"]), 4, True, 2, 128)
+    ora = oracle.quantize(d["w"], 4, True, 2, 128)
+    assert_quant_equal(gpu, ora, 4, True)
+
+
+@pytest.mark.parametrize("gs", [32, 128])
+def test_quantize_ffn7b_asym_full(gpu_lib, gs):
+    """11008x4096 bf16 with 41 columns x10, asymmetric UINT4: codes, zeros and scales bit-exact."""
+    announce("ffn7b quantize g=%d" % gs)
+    d = W.ffn7b(ms=(1,))
+    gpu = gpu_quant(gpu_lib, to_gpu_bf16(d["w"]), 4, False, 2, gs)
+    ora = oracle.quantize(d["w"], 4, False, 2, gs)
+    assert_quant_equal(gpu, ora, 4, False)
+
+
+@pytest.mark.parametrize("case", [(4, True, 2, 128), (4, False, 2, 32), (8, True, 1, 0), (8, False, 0, 0),
+                                  (4, False, 1, 0), (8, True, 2, 64)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_dequantize_bitexact(gpu_lib, case, out):
+    bits, sym, gran, gs = case
+    announce("dequantize %s %s" % (case, out))
+    rng = np.random.default_rng(17)
+    rows, cols = 19, 384
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    q, s, z = oracle.quantize(x, bits, sym, gran, gs)
+    codes = oracle_codes_bytes(q, bits, sym)
+    ref32, ref16 = oracle.dequantize(q, s, z, gran, gs)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    y = gpu_lib.dequantize(to_gpu(codes), to_gpu(s), None if z is None else to_gpu(z), rows, cols, bits, sym, gran,
+                           gs, out_dtype=odt)
+    torch.cuda.synchronize()
+    if out == "f32":
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), ref32.view(np.uint32))
+    else:
+        assert np.array_equal(bf16_tensor_bits(y), ref16)
+
+
+def test_empty_tensors_are_noops(gpu_lib):
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    codes, s, z = gpu_lib.quantize(x, 4, True, 2, 128)
+    assert codes.shape == (0, 128) and s.numel() == 0
+    y = gpu_lib.qlinear_w4a16(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"),
+                              torch.zeros((8, 128), dtype=torch.uint8, device="cuda"),
+                              torch.ones(16, dtype=torch.float32, device="cuda"), None, 128, True)
+    assert y.shape == (0, 8)
+
+
+# --------------------------------------------------------------------------- W4A16
+
+def w4a16_case(pqg, w_host, w_is_bf16, x_u16, sym, gs, out_dtype):
+    """GPU: quantize + pack + W4A16; oracle: quantize + binary64 product. Returns (y_gpu, y_ref, gpu quant, ora quant)."""
+    wg = to_gpu_bf16(w_host) if w_is_bf16 else to_gpu(w_host)
+    codes, s, z = pqg.quantize(wg, 4, sym, 2, gs)
+    y = pqg.qlinear_w4a16(to_gpu_bf16(x_u16), codes, s, z, gs, sym, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    q, so, zo = oracle.quantize(w_host, 4, sym, 2, gs)
+    y_ref = oracle.w4a16(x_u16, q, so, zo, gs)
+    gq = (codes.cpu().numpy(), s.cpu().numpy(), None if z is None else z.cpu().numpy())
+    return to_f64(y), y_ref, gq, (q, so, zo)
+
+
+def test_w4a16_tiny_fp32_out(gpu_lib):
+    announce("w4a16 tiny")
+    d = W.tiny()
+    y, y_ref, gq, oq = w4a16_case(gpu_lib, d["w"], False, d["x"], True, 128, torch.float32)
+    assert_quant_equal(gq, oq, 4, True)
+    err = normwise(y, y_ref)
+    assert err <= TOL_F32, err
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_w4a16_attn7b(gpu_lib, m):
+    announce("w4a16 attn7b M=%d" % m)
+    d = W.attn7b(ms=(1, 16))
+    y, y_ref, _, _ = w4a16_case(gpu_lib, d["w"], True, d["x"][:m], True, 128, torch.bfloat16)
+    err = normwise(y, y_ref)
+    assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("gs", [32, 128])
+@pytest.mark.parametrize("m", [1, 8, 64])
+def test_w4a16_ffn7b_asym(gpu_lib, gs, m):
+    announce("w4a16 ffn7b asym g=%d M=%d" % (gs, m))
+    d = W.ffn7b(ms=(1, 8, 64))
+    y, y_ref, _, _ = w4a16_case(gpu_lib, d["w"], True, d["x"][:m], False, gs, torch.bfloat16)
+    err = normwise(y, y_ref)
+    assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("shape", [(1, 257, 96, 32), (3, 7, 4096, 64), (5, 130, 2080, 32), (2, 1, 32, 32),
+                                   (4, 513, 640, 128)])
+@pytest.mark.parametrize("sym", [True, False])
+def test_w4a16_ragged_fp32(gpu_lib, shape, sym):
+    """Ragged N (not a multiple of the row block), K with a partial last iteration, all M in 1..5."""
+    m, n, k, gs = shape
+    if k % gs:
+        pytest.skip()
+    announce("w4a16 ragged %s sym=%s" % (shape, sym))
+    rng = np.random.default_rng(n * 7 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = W.bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    y, y_ref, gq, oq = w4a16_case(gpu_lib, w, False, x, sym, gs, torch.float32)
+    assert_quant_equal(gq, oq, 4, sym)
+    err = normwise(y, y_ref)
+    assert err <= TOL_F32, err
+
+
+@pytest.mark.parametrize("proj", range(len(W.L70B_PROJ)))
+def test_w4a16_l70b_sampled(gpu_lib, proj):
+    """Full-size 70B projection: GPU quantizes all of it and runs the GEMV at M=1, 8, 32; the oracle checks
+    64 sampled rows (codes and scales bit-exact, outputs within the bf16 tolerance on those rows)."""
+    name, n, k = W.L70B_PROJ[proj]
+    announce("w4a16 l70b %s" % name)
+    w = W.l70b_weight(proj)
+    wg = to_gpu_bf16(w)
+    codes, s, _ = gpu_lib.quantize(wg, 4, True, 2, 128)
+    del wg
+    rng = np.random.default_rng(proj)
+    rows = np.unique(np.concatenate([rng.choice(n, size=62, replace=False), [0, n - 1]]))
+    wrows = w[rows]
+    q, so, _ = oracle.quantize(wrows, 4, True, 2, 128)
+    cg = codes.cpu().numpy()[rows]
+    sg = s.cpu().numpy().reshape(n, -1)[rows].reshape(-1)
+    assert np.array_equal(cg, oracle.pack_int4(q))
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+    x = W.l70b_x(proj, 32)
+    for m in (1, 8, 32):
+        y = gpu_lib.qlinear_w4a16(to_gpu_bf16(x[:m]), codes, s, None, 128, True, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        ys = to_f64(y)[:, rows]
+        y_ref = oracle.w4a16(x[:m], q, so, None, 128)
+        err = normwise(ys, y_ref)
+        assert err <= TOL_BF16, (m, err)
+
+
+# --------------------------------------------------------------------------- smoothing and W8A8
+
+@pytest.mark.parametrize("alpha", [0.5, 1.0, 0.0])
+def test_smooth_bitexact(gpu_lib, alpha):
+    announce("smooth alpha=%s" % alpha)
+    d = W.w8a8()
+    s = gpu_lib.smooth(to_gpu_bf16(d["x"]), to_gpu_bf16(d["w"]), alpha)
+    torch.cuda.synchronize()
+    so = oracle.smooth(d["x"], d["w"], alpha)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+
+
+def test_smooth_generic_alpha_within_ulp(gpu_lib):
+    announce("smooth alpha=0.3")
+    d = W.w8a8(m=256, n=512, k=1024)
+    s = gpu_lib.smooth(to_gpu_bf16(d["x"]), to_gpu_bf16(d["w"]), 0.3).cpu().numpy()
+    so = oracle.smooth(d["x"], d["w"], 0.3)
+    ulps = np.abs(s.view(np.int32).astype(np.int64) - so.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+
+
+def test_smooth_zero_channel(gpu_lib):
+    d = W.w8a8(m=64, n=64, k=256)
+    x = d["x"].copy()
+    x[:, 5] = 0
+    s = gpu_lib.smooth(to_gpu_bf16(x), to_gpu_bf16(d["w"]), 0.5).cpu().numpy()
+    assert s[5] == 1.0
+    assert np.array_equal(s.view(np.uint32), oracle.smooth(x, d["w"], 0.5).view(np.uint32))
+
+
+@pytest.mark.parametrize("mnk", [(1, 1, 16), (3, 5, 32), (128, 128, 64), (129, 257, 80), (200, 1000, 4096),
+                                 (64, 11008, 4096), (2048, 130, 4096)])
+def test_gemm_s8_bitexact(gpu_lib, mnk):
+    m, n, k = mnk
+    announce("gemm s8 %s" % (mnk,))
+    rng = np.random.default_rng(m * 1000 + n + k)
+    a = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    b = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    a[0, :] = 127
+    b[0, :] = -127  # extreme accumulators
+    c = gpu_lib.gemm_s8s8s32(to_gpu(a), to_gpu(b))
+    torch.cuda.synchronize()
+    ref = oracle.gemm_s8(a, b)
+    assert np.array_equal(c.cpu().numpy().astype(np.int64), ref)
+
+
+def test_w8a8_full_layer(gpu_lib):
+    """The whole W8A8 path at 2048x11008x4096: smoothing factor, weight codes/scales, activation codes/scales
+    bit-exact; int32 accumulators bit-exact and bf16 outputs within tolerance on 96 sampled tokens."""
+    announce("w8a8 full layer")
+    d = W.w8a8()
+    xg, wg = to_gpu_bf16(d["x"]), to_gpu_bf16(d["w"])
+    s = gpu_lib.smooth(xg, wg, 0.5)
+    w_q, s_w, _ = gpu_lib.quantize(wg, 8, True, 1, 0, s, 2)
+    y, x_q, s_x = gpu_lib.qlinear_w8a8(xg, s, w_q, s_w, out_dtype=torch.bfloat16)
+    acc = gpu_lib.gemm_s8s8s32(x_q, w_q)
+    torch.cuda.synchronize()
+    so = oracle.smooth(d["x"], d["w"], 0.5)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    qw, sw, _ = oracle.quantize(d["w"], 8, True, 1, 0, so, 2)
+    assert np.array_equal(w_q.cpu().numpy(), qw.astype(np.int8))
+    assert np.array_equal(s_w.cpu().numpy().view(np.uint32), sw.view(np.uint32))
+    qx, sx, _ = oracle.quantize(d["x"], 8, True, 1, 0, so, 1)
+    assert np.array_equal(x_q.cpu().numpy(), qx.astype(np.int8))
+    assert np.array_equal(s_x.cpu().numpy().view(np.uint32), sx.view(np.uint32))
+    rng = np.random.default_rng(4)
+    toks = np.unique(np.concatenate([rng.choice(2048, size=94, replace=False), [0, 2047]]))
+    acc_ref = oracle.gemm_s8(qx[toks].astype(np.int8), qw.astype(np.int8))
+    assert np.array_equal(acc.cpu().numpy()[toks].astype(np.int64), acc_ref)
+    y_ref = oracle.w8a8_epilogue(acc_ref, sx[toks], sw)
+    err = normwise(to_f64(y)[toks], y_ref)
+    assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("mnk", [(5, 77, 96), (130, 200, 512)])
+def test_w8a8_small_fp32_out(gpu_lib, mnk):
+    m, n, k = mnk
+    announce("w8a8 small %s" % (mnk,))
+    d = W.w8a8(m=m, n=n, k=k)
+    r = oracle.w8a8(d["x"], d["w"], 0.5)
+    xg, wg = to_gpu_bf16(d["x"]), to_gpu_bf16(d["w"])
+    s = gpu_lib.smooth(xg, wg, 0.5)
+    w_q, s_w, _ = gpu_lib.quantize(wg, 8, True, 1, 0, s, 2)
+    y, x_q, s_x = gpu_lib.qlinear_w8a8(xg, s, w_q, s_w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(x_q.cpu().numpy(), r["q_x"])
+    assert np.array_equal(w_q.cpu().numpy(), r["q_w"])
+    err = normwise(to_f64(y), r["y"])
+    assert err <= TOL_F32, err
+
+
+# --------------------------------------------------------------------------- determinism
+
+def test_reruns_are_bit_identical(gpu_lib):
+    d = W.ffn7b(ms=(8,))
+    wg = to_gpu_bf16(d["w"])
+    xg = to_gpu_bf16(d["x"][:8])
+    outs = []
+    for _ in range(3):
+        codes, s, z = gpu_lib.quantize(wg, 4, False, 2, 32)
+        y = gpu_lib.qlinear_w4a16(xg, codes, s, z, 32, False)
+        outs.append((codes.cpu().numpy(), bf16_tensor_bits(y)))
+    for o in outs[1:]:
+        assert np.array_equal(o[0], outs[0][0]) and np.array_equal(o[1], outs[0][1])
