@@ -1,0 +1,300 @@
+"""Benchmark of the MI355X quantized linear layer.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass over every stage of the quantized linear layer on synthetic inputs resident in HBM:
+  quantize   Llama-70B-shaped decoder layer (q, k, v, o, gate, up, down; 855.6 M bf16 weights) to symmetric
+             INT4, g = 128, packed                                                  (range, scale, codes, pack)
+  dequantize the packed layer back to bf16                                          (standalone dequantize)
+  w4a16_m1   the seven projections at batch 1 (decode)       <- the headline weight-stream GB/s
+  w4a16_m32  the seven projections at batch 32
+  smooth     SmoothQuant factor, alpha = 0.5, X 2048x4096 (41 channels x50), W 11008x4096
+  wquant     W' = W diag(s) -> INT8 per output channel
+  w8a8       dynamic per-token INT8 activations + INT8 GEMM + s_x*s_w epilogue, 2048x11008x4096
+                                                             <- the INT8 GEMM TOPS
+The packed layer exists twice and the decode pass reads the copy written one step earlier, with the
+standalone dequantize (1.7 GB of writes) in between, so the 455 MB weight stream comes from HBM and not
+from the 256 MB last-level cache.
+
+Output: one JSON line. `value` = the decode weight stream (packed INT4 bytes + fp32 scales of all seven
+projections) divided by the wall time of the seven back-to-back W4A16 launches, in GB/s. Per-launch kernel
+times come from HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, 5.0 POP/s
+GEMV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_gemv_l70b_m1_traffic.md")
+GEMV_SOURCE = os.path.join(ROOT, "post_quantization_group_amd", "csrc", "w4a16.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per decode GEMV launch measured with rocprofv3 counters (profiles/...traffic.md), or None
+    when the file is missing or was taken on a different version of the kernel source."""
+    try:
+        text = open(GEMV_TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != source_hash(GEMV_SOURCE):
+        return None
+    return float(t.group(1))
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (each GPU would run the same "
+              "kernels on its own shard of the output rows); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import post_quantization_group_amd as pqg
+    import workloads as W
+
+    pqg.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_setup = time.time()
+    # ---------------------------------------------------------------- inputs (resident in HBM)
+    projs = []
+    for i, (name, n, k) in enumerate(W.L70B_PROJ):
+        w = bf16(W.l70b_weight(i))
+        x = bf16(W.l70b_x(i, 32))
+        packed = [torch.empty((n, k // 2), dtype=torch.uint8, device=dev) for _ in range(2)]
+        scales = [torch.empty(n * k // 128, dtype=torch.float32, device=dev) for _ in range(2)]
+        for c in range(2):
+            pqg.quantize(w, 4, True, pqg.GROUP, 128, out=(packed[c], scales[c], None))
+        projs.append(dict(name=name, n=n, k=k, w=w, x=x, packed=packed, scales=scales,
+                          y1=torch.empty((1, n), dtype=torch.bfloat16, device=dev),
+                          y32=torch.empty((32, n), dtype=torch.bfloat16, device=dev)))
+    deq = torch.empty(max(p["n"] * p["k"] for p in projs), dtype=torch.bfloat16, device=dev)
+    d8 = W.w8a8()
+    X8, W8 = bf16(d8["x"]), bf16(d8["w"])
+    M8, K8 = X8.shape
+    N8 = W8.shape[0]
+    s8 = pqg.smooth(X8, W8, 0.5)
+    wq8, sw8, _ = pqg.quantize(W8, 8, True, pqg.ROW, 0, s8, pqg.SMOOTH_MUL)
+    y8 = torch.empty((M8, N8), dtype=torch.bfloat16, device=dev)
+    xq8 = torch.empty((M8, K8), dtype=torch.int8, device=dev)
+    sx8 = torch.empty(M8, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    gemv_bytes = sum(p["n"] * p["k"] // 2 + p["n"] * (p["k"] // 128) * 4 for p in projs)
+    gemv_bytes_total = gemv_bytes + sum(p["k"] * 2 + p["n"] * 2 for p in projs)  # + x and y
+    w8a8_ops = 2.0 * M8 * N8 * K8
+
+    parts = ["quantize", "dequantize", "w4a16_m1", "w4a16_m32", "smooth", "wquant", "w8a8_actquant", "w8a8_gemm"]
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def run_step(i, rec):
+        c, o = i % 2, 1 - i % 2
+        marks = {}
+        if rec:
+            marks["start"] = ev()
+            marks["start"].record(stream)
+        for p in projs:  # S1-S4: range, scale, codes, pack
+            pqg.quantize(p["w"], 4, True, pqg.GROUP, 128, out=(p["packed"][c], p["scales"][c], None))
+        if rec:
+            marks["quantize"] = ev()
+            marks["quantize"].record(stream)
+        for p in projs:  # S5: standalone dequantize
+            out = deq[: p["n"] * p["k"]].view(p["n"], p["k"])
+            pqg.dequantize(p["packed"][c], p["scales"][c], None, p["n"], p["k"], 4, True, pqg.GROUP, 128, out=out)
+        if rec:
+            marks["dequantize"] = ev()
+            marks["dequantize"].record(stream)
+        gemv_ev = []
+        for p in projs:  # S6: decode GEMV over the copy written one step earlier
+            if rec:
+                e0 = ev()
+                e0.record(stream)
+            pqg.qlinear_w4a16(p["x"][:1], p["packed"][o], p["scales"][o], None, 128, True, out=p["y1"])
+            if rec:
+                e1 = ev()
+                e1.record(stream)
+                gemv_ev.append((e0, e1))
+        if rec:
+            marks["w4a16_m1"] = ev()
+            marks["w4a16_m1"].record(stream)
+        for p in projs:  # S7: batch 32
+            pqg.qlinear_w4a16(p["x"], p["packed"][c], p["scales"][c], None, 128, True, out=p["y32"])
+        if rec:
+            marks["w4a16_m32"] = ev()
+            marks["w4a16_m32"].record(stream)
+        s = pqg.smooth(X8, W8, 0.5)  # S8
+        if rec:
+            marks["smooth"] = ev()
+            marks["smooth"].record(stream)
+        pqg.quantize(W8, 8, True, pqg.ROW, 0, s, pqg.SMOOTH_MUL, out=(wq8, sw8, None))  # S9
+        if rec:
+            marks["wquant"] = ev()
+            marks["wquant"].record(stream)
+        # S10: dynamic per-token INT8 activations after X diag(s)^-1
+        pqg.quantize(X8, 8, True, pqg.ROW, 0, s, pqg.SMOOTH_DIV, out=(xq8, sx8, None))
+        if rec:
+            marks["w8a8_actquant"] = ev()
+            marks["w8a8_actquant"].record(stream)
+        pqg.qlinear_w8a8(None, None, wq8, sw8, out=y8, x_q=xq8, x_scales=sx8)  # S11-S12: INT8 GEMM + epilogue
+        if rec:
+            marks["w8a8_gemm"] = ev()
+            marks["w8a8_gemm"].record(stream)
+        return marks, gemv_ev
+
+    for i in range(args.warmup):
+        run_step(i, False)
+    torch.cuda.synchronize()
+
+    records = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        records.append(run_step(args.warmup + i, True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_part = {k: [] for k in parts}
+    gemv_launch_ms = []
+    gemv_seq_ms = []
+    for marks, gemv_ev in records:
+        prev = marks["start"]
+        for k in parts:
+            per_part[k].append(prev.elapsed_time(marks[k]))
+            prev = marks[k]
+        gemv_launch_ms.append([a.elapsed_time(b) for a, b in gemv_ev])
+        gemv_seq_ms.append(gemv_ev[0][0].elapsed_time(gemv_ev[-1][1]))
+    med = lambda v: float(np.median(v))  # noqa: E731
+    part_ms = {k: med(v) for k, v in per_part.items()}
+    launch_ms = np.median(np.array(gemv_launch_ms), axis=0)  # per projection
+    seq_ms = med(gemv_seq_ms)
+    gemm_ms = part_ms["w8a8_gemm"]  # one launch per step: event pair around the GEMM + epilogue kernel
+
+    value = gemv_bytes / (seq_ms * 1e-3) / 1e9
+    achieved = gemv_bytes / (float(launch_ms.sum()) * 1e-3) / 1e9
+    tops = w8a8_ops / (gemm_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+
+    out = {
+        "metric": "W4A16 GEMV weight GB/s (% HBM peak); W8A8 GEMM TOPS (% int8 MFMA peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xbf16->f32 (W4A16); int8xint8->int32 (W8A8)",
+        "data": "synthetic (seeded N(0, 0.02) weights / N(0, 1) activations; no trained weights)",
+        "config": {
+            "workload": "llama70b_layer_w4a16_decode_m1 + w8a8_2048x11008x4096",
+            "w4a16": {"projections": [[p["name"], p["n"], p["k"]] for p in projs], "M": 1, "group_size": 128,
+                      "symmetric": True, "weight_bytes_per_step": gemv_bytes},
+            "w8a8": {"M": M8, "N": N8, "K": K8, "alpha": 0.5, "outlier_channels": int(d8["outlier_chans"].size)},
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_w4a16_gemv (M=1, seven 70B-layer projections)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": gemv_bytes / len(projs),
+            "avg_launch_us": round(float(launch_ms.mean()) * 1e3, 3),
+        },
+        "w8a8_gemm": {
+            "value": round(tops, 1),
+            "unit": "TOPS",
+            "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                         "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                         "ops_per_launch": w8a8_ops, "avg_launch_us": round(gemm_ms * 1e3, 2)},
+        },
+        "per_projection_us": {p["name"]: round(float(t) * 1e3, 2) for p, t in zip(projs, launch_ms)},
+        "stage_ms": {k: round(v, 4) for k, v in part_ms.items()},
+        "setup_s": round(setup_s, 1),
+    }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = 1 << 30
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(target_s):
+    """The oracle timed on the host cores over a bounded sample of the decode workload: INT4 group quantize
+    of the first rows of each 70B projection, then the binary64 W4A16 product at M=1, in weight GB/s."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    threads = oracle.num_threads()
+    rows = 64
+    done_bytes = 0
+    t_total = 0.0
+    sample_rows = 0
+    while t_total < target_s and rows <= 32768:
+        for i, (name, n, k) in enumerate(W.L70B_PROJ):
+            r = min(rows, n)
+            w = W.l70b_weight(i, rows=np.arange(r))
+            x = W.l70b_x(i, 1)
+            t0 = time.perf_counter()
+            q, s, _ = oracle.quantize(w, 4, True, oracle.GROUP, 128)
+            oracle.w4a16(x, q, s, None, 128)
+            t_total += time.perf_counter() - t0
+            done_bytes += r * k // 2 + r * (k // 128) * 4
+            sample_rows += r
+        rows *= 2
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "first rows of each of the seven 70B projections (%d rows in total, doubling from 64), "
+                      "INT4 g=128 quantize + binary64 W4A16 at M=1; %.1f s" % (sample_rows, t_total)}
+
+
+if __name__ == "__main__":
+    main()

@@ -153,13 +153,15 @@ int32_t pqg_qlinear_w4a16(const void *x, int64_t M, int64_t N, int64_t K, const 
  * smoothing division X diag(s)^-1 when `smooth` is non-NULL (exactly as pqg_quantize with PQG_ROW,
  * bits 8, symmetric, PQG_SMOOTH_DIV); then the INT8 GEMM with exact INT32 accumulation and the epilogue
  * y = bf16/fp32(float(acc) * (s_x[m] * s_w[n])).
- *   x        : bf16 [M, K] activations.
- *   smooth   : fp32 [K] or NULL.
+ *   x        : bf16 [M, K] activations, or NULL: the activations are then already quantized and x_q /
+ *              x_scales are INPUTS (e.g. codes from pqg_quantize with PQG_ROW, bits 8, symmetric), and only
+ *              the GEMM + epilogue launch is enqueued.
+ *   smooth   : fp32 [K] or NULL (must be NULL when x is NULL).
  *   w_q      : int8 [N, K] per-output-channel symmetric codes (pqg_quantize, PQG_ROW, bits 8; the
  *              smoothing multiply diag(s) W is applied there, offline); w_scales: fp32 [N].
  *   y (out)  : [M, N] of y_dtype (PQG_BF16 or PQG_F32).
- *   x_q, x_scales (out): caller scratch int8 [M, K] and fp32 [M]; left holding the activation codes
- *              and scales.
+ *   x_q, x_scales : int8 [M, K] and fp32 [M]. With x given they are caller scratch that the call fills
+ *              with the activation codes and scales (and leaves readable); with x NULL they are inputs.
  * Requires K % 32 == 0 and K <= 65536.
  */
 int32_t pqg_qlinear_w8a8(const void *x, const float *smooth, const int8_t *w_q, const float *w_scales, int64_t M,

@@ -142,11 +142,12 @@ def quantize(x: torch.Tensor, bits: int, symmetric: bool, granularity: int, grou
 
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, zeros, rows: int, cols: int, bits: int, symmetric: bool,
-               granularity: int, group_size: int = 0, out_dtype=torch.float32):
-    """pqg_dequantize -> [rows, cols] tensor of out_dtype (float32 or bfloat16)."""
+               granularity: int, group_size: int = 0, out_dtype=torch.float32, out=None):
+    """pqg_dequantize -> [rows, cols] tensor of out_dtype (float32 or bfloat16); `out` may be preallocated."""
     lib = load()
     dev = _dev(codes)
-    out = torch.empty((rows, cols), dtype=out_dtype, device=dev)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=dev)
     _check(lib.pqg_dequantize(_ptr(codes), _ptr(scales), _ptr(zeros), rows, cols, bits, int(symmetric), granularity,
                               group_size, _ptr(out), _float_dtype(out), _stream(dev)))
     return out
@@ -186,19 +187,26 @@ def qlinear_w4a16(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
     return y
 
 
-def qlinear_w8a8(x: torch.Tensor, smooth_s, w_q: torch.Tensor, w_scales: torch.Tensor, out_dtype=torch.bfloat16,
-                 out=None, x_q=None, x_scales=None):
+def qlinear_w8a8(x, smooth_s, w_q: torch.Tensor, w_scales: torch.Tensor, out_dtype=torch.bfloat16, out=None,
+                 x_q=None, x_scales=None):
     """pqg_qlinear_w8a8: dynamic per-token INT8 activations (after X diag(s)^-1), INT8 GEMM, s_x*s_w epilogue.
-    Returns (y, x_q, x_scales)."""
+    With x None the activations are already quantized: x_q [M, K] int8 and x_scales [M] are inputs and only
+    the GEMM + epilogue runs. Returns (y, x_q, x_scales)."""
     lib = load()
-    dev = _dev(x)
-    if x.dtype != torch.bfloat16:
-        raise TypeError("x must be bfloat16")
-    M, K = x.shape
-    N = w_q.shape[0]
+    dev = _dev(w_q)
+    N, K = w_q.shape
+    if x is not None:
+        _dev(x)
+        if x.dtype != torch.bfloat16:
+            raise TypeError("x must be bfloat16")
+        M = x.shape[0]
+        x_q = torch.empty((M, K), dtype=torch.int8, device=dev) if x_q is None else x_q
+        x_scales = torch.empty(M, dtype=torch.float32, device=dev) if x_scales is None else x_scales
+    else:
+        if x_q is None or x_scales is None:
+            raise ValueError("x_q and x_scales are required when x is None")
+        M = x_q.shape[0]
     y = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
-    x_q = torch.empty((M, K), dtype=torch.int8, device=dev) if x_q is None else x_q
-    x_scales = torch.empty(M, dtype=torch.float32, device=dev) if x_scales is None else x_scales
     _check(lib.pqg_qlinear_w8a8(_ptr(x), _ptr(smooth_s), _ptr(w_q), _ptr(w_scales), M, N, K, _ptr(y),
                                 _float_dtype(y), _ptr(x_q), _ptr(x_scales), _stream(dev)))
     return y, x_q, x_scales

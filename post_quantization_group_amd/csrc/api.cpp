@@ -220,16 +220,20 @@ int32_t pqg_qlinear_w8a8(const void *x, const float *smooth, const int8_t *w_q, 
         return PQG_OK;
     if (K == 0)
         return fail(PQG_EUNSUPPORTED, "K == 0");
-    if (!x || !w_q || !w_scales || !y || !x_q || !x_scales)
-        return fail(PQG_EINVAL, "x, w_q, w_scales, y, x_q and x_scales are required");
-    if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(x_q, 16) || !aligned(w_scales, 4) ||
+    if (!w_q || !w_scales || !y || !x_q || !x_scales)
+        return fail(PQG_EINVAL, "w_q, w_scales, y, x_q and x_scales are required");
+    if (!x && smooth)
+        return fail(PQG_EINVAL, "smooth must be NULL when x is NULL (x_q / x_scales are then inputs)");
+    if ((x && !aligned(x, 16)) || !aligned(w_q, 16) || !aligned(x_q, 16) || !aligned(w_scales, 4) ||
         !aligned(x_scales, 4) || !aligned(y, 4) || (smooth && !aligned(smooth, 16)))
         return fail(PQG_EINVAL, "misaligned pointer (x, w_q, x_q, smooth: 16 bytes; scales, y: 4 bytes)");
     hipStream_t st = as_stream(stream);
-    pqg::QuantArgs q{x, true, M, K, smooth, smooth ? pqg::SMOOTH_DIV : pqg::SMOOTH_NONE, 8, true, pqg::QG_ROW, 0,
-                     x_q, x_scales, nullptr, nullptr};
-    if (int32_t e = hip_status(pqg::launch_quantize(q, st), "pqg_qlinear_w8a8 activation quantize launch"))
-        return e;
+    if (x) {
+        pqg::QuantArgs q{x, true, M, K, smooth, smooth ? pqg::SMOOTH_DIV : pqg::SMOOTH_NONE, 8, true, pqg::QG_ROW, 0,
+                         x_q, x_scales, nullptr, nullptr};
+        if (int32_t e = hip_status(pqg::launch_quantize(q, st), "pqg_qlinear_w8a8 activation quantize launch"))
+            return e;
+    }
     pqg::GemmI8Args g{x_q, w_q, M, N, K, x_scales, w_scales, y, y_dtype == PQG_BF16};
     return hip_status(pqg::launch_gemm_i8(g, st), "pqg_qlinear_w8a8 gemm launch");
 }

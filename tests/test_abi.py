@@ -104,6 +104,8 @@ def test_w8a8_and_gemm_reject(lib):
     assert rc == pqg.EINVAL and "multiple of 32" in lib.pqg_last_error().decode()
     rc = lib.pqg_qlinear_w8a8(FAKE, None, FAKE, FAKE, 4, 64, 256, FAKE, 1, None, FAKE, None)
     assert rc == pqg.EINVAL and "required" in lib.pqg_last_error().decode()
+    rc = lib.pqg_qlinear_w8a8(None, FAKE, FAKE, FAKE, 4, 64, 256, FAKE, 1, FAKE, FAKE, None)
+    assert rc == pqg.EINVAL and "smooth must be NULL" in lib.pqg_last_error().decode()
     rc = lib.pqg_gemm_s8s8s32(FAKE, FAKE, 4, 4, 24, FAKE, None)
     assert rc == pqg.EINVAL and "multiple of 16" in lib.pqg_last_error().decode()
     rc = lib.pqg_gemm_s8s8s32(MISALIGNED, FAKE, 4, 4, 32, FAKE, None)

@@ -322,6 +322,10 @@ def test_w8a8_small_fp32_out(gpu_lib, mnk):
     assert np.array_equal(w_q.cpu().numpy(), r["q_w"])
     err = normwise(to_f64(y), r["y"])
     assert err <= TOL_F32, err
+    # pre-quantized activations (x = NULL): only the GEMM + epilogue runs, same result bit for bit
+    y2, _, _ = gpu_lib.qlinear_w8a8(None, None, w_q, s_w, out_dtype=torch.float32, x_q=x_q, x_scales=s_x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
 
 
 # --------------------------------------------------------------------------- determinism
