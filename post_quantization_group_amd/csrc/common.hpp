@@ -157,4 +157,27 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over a full wave, returned as a wave-uniform value. Within each 16-lane row the sum is a
+// butterfly of DPP moves (swap neighbours, swap pairs, mirror halves, mirror the row), so every lane of
+// the row holds its row total; the four row totals are then read out and added in a fixed order.
+// No LDS traffic, deterministic.
+__device__ __forceinline__ float wave_sum_uniform(float v)
+{
+    v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141>(v);  // row_half_mirror
+    v += dpp_f32<0x140>(v);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 }  // namespace pqg

@@ -5,18 +5,22 @@
 // every weight is read once per step, so the layer is bound by the weight stream.)
 //
 // Design (small M, the decode case):
-//   * A wave owns R output rows and a contiguous slice of K; each lane reads 16 bytes (32 codes) of each
-//     of its R rows per iteration, so one wave instruction streams 1 KB of a row (fully coalesced 128-bit
-//     loads). S waves of a block split K for the same R rows and are combined once, through LDS, in a
-//     fixed order (deterministic).
-//   * Dequantization stays in registers and costs about one VALU instruction per code: a nibble u is
-//     moved into the top four mantissa bits of a bf16 whose exponent encodes 16, giving the exact value
-//     16 + u; two codes (j, j+4) of a 32-bit word share one shift and one and-or. The activations are
-//     re-paired to match with v_perm, once per chunk, shared by the R rows.
+//   * A block owns R output rows; its S waves split K into contiguous slices. Each lane reads 16 bytes
+//     (32 codes) of each of the R rows per iteration, so one wave instruction streams 1 KB of a row
+//     (fully coalesced 128-bit loads). Row base pointers are uniform (scalar registers) and lanes add
+//     32-bit offsets, so addressing costs almost no vector instructions. The S partial sums of a row
+//     are combined once, through LDS, in a fixed order (deterministic).
+//   * Two register stages alternate, so the next chunk's loads are in flight while the current one is
+//     reduced.
+//   * Dequantization stays in registers and costs one shift and one v_bitop3_b32 per pair of codes: the
+//     nibble pair (j, j + 4) of a packed word is moved to bits [3, 7) of each 16-bit half and merged with
+//     the bf16 pattern of 16.0, giving the exact value 16 + u. For two's-complement codes the same
+//     instruction flips the nibble's sign bit, turning q into its offset binary q + 8.
 //   * The products use v_dot2_f32_bf16 (two bf16 products, fp32 accumulation). The code offset is removed
-//     once per 32 codes: sum x (u - off) = sum x (16 + u) - (16 + off) sum x, with off = 8 for symmetric
-//     codes (two's-complement nibbles are flipped to offset binary with one xor per word) and off = z for
-//     asymmetric ones. The per-group scale multiplies each 32-code partial sum.
+//     once per 32 codes: sum x (u - off) = sum x (16 + u) - (16 + off) sum x, with off = 8 (symmetric)
+//     or z (asymmetric). The group scale multiplies each 32-code partial sum. The offset 16 keeps the
+//     accumulated magnitudes within a few times those of the true partial sums, so little precision is
+//     lost to the subtraction.
 //   * No dequantized weight is ever written to memory.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -31,40 +35,148 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
                                            false);
 }
 
-// bf16 pair holding 16 + nibble for the two nibbles selected by the shift (low half, high half).
-__device__ __forceinline__ uint32_t nib_pair_shl3(uint32_t w) { return ((w << 3) & 0x00780078u) | 0x41804180u; }
-template <int SHR>
-__device__ __forceinline__ uint32_t nib_pair_shr(uint32_t w)
+// A loop-invariant constant held in a VGPR. gfx9 VOP3 instructions take no literal and at most one scalar
+// operand, so the three-input bit operation below needs its mask and magic in vector registers.
+__device__ __forceinline__ uint32_t vreg_const(uint32_t c)
 {
-    return ((w >> SHR) & 0x00780078u) | 0x41804180u;
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+    return r;
 }
 
-constexpr uint32_t kBf16OnePair = 0x3F803F80u;
-constexpr int kMaxWavesPerRow = 16;
+constexpr uint32_t kPairMask = 0x00780078u;
+constexpr uint32_t kMagic16 = 0x41804180u;      // bf16 16.0 | 16.0
+constexpr uint32_t kSignFlip = 0x00400040u;     // bit 6 of each half: the nibble's top bit
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // bf16 1.0 | 1.0
+constexpr int kMaxWavesPerRow = 8;
 
-// MT activation rows (1..4), R weight rows per block; S = blockDim.x / 64 waves split K.
-template <int MT, int R, bool SYM, bool OUT_BF16>
-__global__ __launch_bounds__(1024) void k_w4a16_gemv(const uint16_t *__restrict__ x, int64_t N, int64_t K,
-                                                     const uint8_t *__restrict__ w, const float *__restrict__ scales,
-                                                     const uint8_t *__restrict__ zeros, int group_size,
-                                                     void *__restrict__ y, int64_t y_ld)
+__device__ __forceinline__ uint32_t pair_bits(uint32_t shifted, uint32_t mask, uint32_t magic)
+{
+    return __builtin_amdgcn_bitop3_b32(shifted, mask, magic, 0x6A);  // (a & b) ^ c
+}
+
+// Everything one lane loads for one 32-code chunk: R rows of packed codes, their scales and zero
+// points, and MT rows of activations.
+template <int MT, int R>
+struct Stage {
+    uint4 w[R];
+    float s[R];
+    float z[R];
+    uint4 x[MT][4];
+};
+
+// Uniform (per block) base pointers of the R weight rows, their metadata and the MT activation rows.
+template <int MT, int R>
+struct Bases {
+    const uint8_t *w[R];
+    const float *s[R];
+    const uint8_t *z[R];
+    const uint16_t *x[MT];
+};
+
+template <int MT, int R, int G, bool SYM>
+__device__ __forceinline__ void stage_load(Stage<MT, R> &st, const Bases<MT, R> &b, uint32_t c)
+{
+    constexpr int kGroupShift = (G == 128) ? 2 : (G == 64) ? 1 : 0;  // chunk -> group index
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        st.w[r] = *reinterpret_cast<const uint4 *>(b.w[r] + c * 16u);
+    const uint32_t gi = c >> kGroupShift;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        st.s[r] = b.s[r][gi];
+        st.z[r] = SYM ? 8.0f : (float)b.z[r][gi];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const uint4 *xv = reinterpret_cast<const uint4 *>(b.x[m] + c * 32u);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            st.x[m][d] = xv[d];
+    }
+}
+
+template <int MT, int R>
+__device__ __forceinline__ void stage_compute(const Stage<MT, R> &st, float acc[R][MT], uint32_t mask, uint32_t magic)
+{
+    // activations re-paired as (x_j, x_{j+4}) per 8-element block, and their sum
+    uint32_t xp[MT][16];
+    float xsum[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        float s = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint4 u = st.x[m][d];
+            xp[m][4 * d + 0] = __builtin_amdgcn_perm(u.z, u.x, 0x05040100u);
+            xp[m][4 * d + 1] = __builtin_amdgcn_perm(u.z, u.x, 0x07060302u);
+            xp[m][4 * d + 2] = __builtin_amdgcn_perm(u.w, u.y, 0x05040100u);
+            xp[m][4 * d + 3] = __builtin_amdgcn_perm(u.w, u.y, 0x07060302u);
+            s = dot2(u.x, kBf16OnePair, s);
+            s = dot2(u.y, kBf16OnePair, s);
+            s = dot2(u.z, kBf16OnePair, s);
+            s = dot2(u.w, kBf16OnePair, s);
+        }
+        xsum[m] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t wd[4] = {st.w[r].x, st.w[r].y, st.w[r].z, st.w[r].w};
+        float part[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            part[m] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t b0 = pair_bits(wd[d] << 3, mask, magic);
+            const uint32_t b1 = pair_bits(wd[d] >> 1, mask, magic);
+            const uint32_t b2 = pair_bits(wd[d] >> 5, mask, magic);
+            const uint32_t b3 = pair_bits(wd[d] >> 9, mask, magic);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                part[m] = dot2(xp[m][4 * d + 0], b0, part[m]);
+                part[m] = dot2(xp[m][4 * d + 1], b1, part[m]);
+                part[m] = dot2(xp[m][4 * d + 2], b2, part[m]);
+                part[m] = dot2(xp[m][4 * d + 3], b3, part[m]);
+            }
+        }
+        // sum_k x (u - off) = sum_k x (16 + u) - (16 + off) sum_k x, then the group scale
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            acc[r][m] = __builtin_fmaf(st.s[r], __builtin_fmaf(-(16.0f + st.z[r]), xsum[m], part[m]), acc[r][m]);
+    }
+}
+
+// MT activation rows (1..4), R weight rows per block, group size G; S = blockDim.x / 64 waves split K.
+template <int MT, int R, int G, bool SYM, bool OUT_BF16>
+__global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__ x, int64_t N, int64_t K,
+                                                    const uint8_t *__restrict__ w, const float *__restrict__ scales,
+                                                    const uint8_t *__restrict__ zeros, void *__restrict__ y,
+                                                    int64_t y_ld)
 {
     __shared__ float red[kMaxWavesPerRow][R * MT];
     const int lane = threadIdx.x % kWave;
     const int wv = threadIdx.x / kWave;
     const int S = blockDim.x / kWave;
     const int64_t row0 = (int64_t)blockIdx.x * R;
-    const int64_t chunks = K / 32;                 // 32 codes = 16 bytes per lane
-    const int64_t c_begin = chunks * wv / S;
-    const int64_t c_end = chunks * (wv + 1) / S;
-    const int64_t groups = K / group_size;
-    const int64_t wrow_bytes = K / 2;
+    const int chunks = (int)(K / 32);  // 32 codes = 16 bytes per lane
+    const int s_shift = __builtin_ctz(S);  // S is a power of two
+    const int c_begin = (chunks * wv) >> s_shift;
+    const int c_end = (chunks * (wv + 1)) >> s_shift;
+    const uint32_t mask = vreg_const(kPairMask);
+    const uint32_t magic = vreg_const(SYM ? (kMagic16 ^ kSignFlip) : kMagic16);
 
-    // rows past N (last block) read row N-1 and are never stored
-    int64_t rows[R];
+    Bases<MT, R> bp;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        rows[r] = row0 + r < N ? row0 + r : N - 1;
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = row0 + r < N ? row0 + r : N - 1;  // rows past N read row N-1, never stored
+        bp.w[r] = w + row * (K / 2);
+        bp.s[r] = scales + row * (K / G);
+        bp.z[r] = SYM ? nullptr : zeros + row * (K / G);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        bp.x[m] = x + (int64_t)m * K;
 
     float acc[R][MT];
 #pragma unroll
@@ -73,73 +185,33 @@ __global__ __launch_bounds__(1024) void k_w4a16_gemv(const uint16_t *__restrict_
         for (int m = 0; m < MT; ++m)
             acc[r][m] = 0.0f;
 
-    for (int64_t c = c_begin + lane; c < c_end; c += kWave) {
-        uint4 wq[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            wq[r] = *reinterpret_cast<const uint4 *>(w + rows[r] * wrow_bytes + c * 16);
-        float sc[R], cf[R];
-        const int64_t gi = (c * 32) / group_size;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            sc[r] = scales[rows[r] * groups + gi];
-            cf[r] = SYM ? 24.0f : 16.0f + (float)zeros[rows[r] * groups + gi];
-        }
-        // activations for this chunk, re-paired as (x_j, x_{j+4}) per 8-element block
-        uint32_t xp[MT][16];
-        float xsum[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const uint4 *xv = reinterpret_cast<const uint4 *>(x + (int64_t)m * K + c * 32);
-            float s = 0.0f;
-#pragma unroll
-            for (int d2 = 0; d2 < 4; ++d2) {  // one 8-element block per 16-byte load
-                const uint4 u = xv[d2];
-                xp[m][4 * d2 + 0] = __builtin_amdgcn_perm(u.z, u.x, 0x05040100u);
-                xp[m][4 * d2 + 1] = __builtin_amdgcn_perm(u.z, u.x, 0x07060302u);
-                xp[m][4 * d2 + 2] = __builtin_amdgcn_perm(u.w, u.y, 0x05040100u);
-                xp[m][4 * d2 + 3] = __builtin_amdgcn_perm(u.w, u.y, 0x07060302u);
-                s = dot2(u.x, kBf16OnePair, s);
-                s = dot2(u.y, kBf16OnePair, s);
-                s = dot2(u.z, kBf16OnePair, s);
-                s = dot2(u.w, kBf16OnePair, s);
-            }
-            xsum[m] = s;
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            uint32_t wd[4] = {wq[r].x, wq[r].y, wq[r].z, wq[r].w};
-            float part[MT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                part[m] = 0.0f;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t word = SYM ? (wd[d] ^ 0x88888888u) : wd[d];
-                const uint32_t b0 = nib_pair_shl3(word);
-                const uint32_t b1 = nib_pair_shr<1>(word);
-                const uint32_t b2 = nib_pair_shr<5>(word);
-                const uint32_t b3 = nib_pair_shr<9>(word);
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    part[m] = dot2(xp[m][4 * d + 0], b0, part[m]);
-                    part[m] = dot2(xp[m][4 * d + 1], b1, part[m]);
-                    part[m] = dot2(xp[m][4 * d + 2], b2, part[m]);
-                    part[m] = dot2(xp[m][4 * d + 3], b3, part[m]);
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                acc[r][m] = __builtin_fmaf(sc[r], __builtin_fmaf(-cf[r], xsum[m], part[m]), acc[r][m]);
-        }
+    // two register stages, alternating: loads of chunk c + 64 are in flight while chunk c is reduced
+    Stage<MT, R> sa, sb;
+    int c = c_begin + lane;
+    if (c < c_end)
+        stage_load<MT, R, G, SYM>(sa, bp, (uint32_t)c);
+    while (c < c_end) {
+        const int c1 = c + kWave;
+        if (c1 < c_end)
+            stage_load<MT, R, G, SYM>(sb, bp, (uint32_t)c1);
+        stage_compute<MT, R>(sa, acc, mask, magic);
+        if (c1 >= c_end)
+            break;
+        const int c2 = c1 + kWave;
+        if (c2 < c_end)
+            stage_load<MT, R, G, SYM>(sa, bp, (uint32_t)c2);
+        stage_compute<MT, R>(sb, acc, mask, magic);
+        c = c2;
     }
 
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            acc[r][m] = wave_sum(acc[r][m]);
+            acc[r][m] = wave_sum_uniform(acc[r][m]);
 
+    float *yf = reinterpret_cast<float *>(y);
+    uint16_t *yh = reinterpret_cast<uint16_t *>(y);
     if (S > 1) {
         if (lane == 0) {
 #pragma unroll
@@ -156,9 +228,9 @@ __global__ __launch_bounds__(1024) void k_w4a16_gemv(const uint16_t *__restrict_
                 t += red[i][threadIdx.x];
             if (row0 + r < N) {
                 if (OUT_BF16)
-                    reinterpret_cast<uint16_t *>(y)[m * y_ld + row0 + r] = (uint16_t)f32_to_bf16_bits(t);
+                    yh[m * y_ld + row0 + r] = (uint16_t)f32_to_bf16_bits(t);
                 else
-                    reinterpret_cast<float *>(y)[m * y_ld + row0 + r] = t;
+                    yf[m * y_ld + row0 + r] = t;
             }
         }
     } else if (lane == 0) {
@@ -168,58 +240,370 @@ __global__ __launch_bounds__(1024) void k_w4a16_gemv(const uint16_t *__restrict_
             for (int m = 0; m < MT; ++m)
                 if (row0 + r < N) {
                     if (OUT_BF16)
-                        reinterpret_cast<uint16_t *>(y)[m * y_ld + row0 + r] = (uint16_t)f32_to_bf16_bits(acc[r][m]);
+                        yh[m * y_ld + row0 + r] = (uint16_t)f32_to_bf16_bits(acc[r][m]);
                     else
-                        reinterpret_cast<float *>(y)[m * y_ld + row0 + r] = acc[r][m];
+                        yf[m * y_ld + row0 + r] = acc[r][m];
                 }
+    }
+}
+
+// ------------------------------------------------------------------ matrix-core variant (any M <= 64)
+//
+// v_mfma_f32_16x16x32_bf16 computes D[i][j] += sum_k A[i][k] B[k][j] on 16x32 / 32x16 bf16 tiles. Here
+// A is the activation tile (i = token m) and B the dequantized weight tile (j = output row n), so lane
+// l holds B for row n = l % 16 and k-block l / 16, and D for row n at tokens m = 4 (l / 16) + r: each lane
+// owns one weight row, whose scale and zero point it loads itself.
+//   * k-step = 128 codes. With g = 128 a lane loads 16 bytes (its quarter of the k-step) and word t feeds
+//     MFMA t; all four MFMAs stay inside the one group. With g = 32 / 64 a lane loads the word of k-block
+//     t for each MFMA t, so that each MFMA covers 32 consecutive codes of a single group.
+//   * Weight words become B operands with the same nibble-pair dequantization as the vector kernel
+//     (element 2j + h of the operand is code j + 4h of the word, value 16 + u); the activations are
+//     re-paired to match with v_perm.
+//   * Per group, one more MFMA against a B of ones gives sum_k x[m, k] for the lane's tokens; then
+//     acc += s * (D - (16 + off) * xsum). Tokens past M reuse row M - 1 and are never stored.
+//   * TT row tiles of 16 share each activation operand; MTILES tiles of 16 tokens share each weight
+//     operand, so the weight stream is read once for up to 64 tokens. S waves of a block split K and are
+//     combined through LDS in a fixed order.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    return __builtin_bit_cast(bf16x8_t, make_uint4(a, b, c, d));
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// B operand (8 weights, value 16 + u each) from one packed word.
+__device__ __forceinline__ bf16x8_t dequant_word(uint32_t wd, uint32_t mask, uint32_t magic)
+{
+    return as_bf16x8(pair_bits(wd << 3, mask, magic), pair_bits(wd >> 1, mask, magic), pair_bits(wd >> 5, mask, magic),
+                     pair_bits(wd >> 9, mask, magic));
+}
+
+// A operand from 8 consecutive activations, re-paired as (x_j, x_{j+4}).
+__device__ __forceinline__ bf16x8_t pair_x(uint4 u)
+{
+    return as_bf16x8(__builtin_amdgcn_perm(u.z, u.x, 0x05040100u), __builtin_amdgcn_perm(u.z, u.x, 0x07060302u),
+                     __builtin_amdgcn_perm(u.w, u.y, 0x05040100u), __builtin_amdgcn_perm(u.w, u.y, 0x07060302u));
+}
+
+constexpr int kMfmaMaxWaves = 4;
+
+template <int MTILES, int TT, int G>
+struct MStage {
+    static constexpr int GPS = G == 128 ? 1 : 128 / G;  // groups per k-step
+    uint32_t w[TT][4];
+    float s[TT][GPS];
+    float z[TT][GPS];
+    uint4 x[MTILES][4];
+};
+
+template <int MTILES, int TT, int G, bool SYM>
+__device__ __forceinline__ void mstage_load(MStage<MTILES, TT, G> &st, const uint8_t *const wrow[TT],
+                                            const float *const srow[TT], const uint8_t *const zrow[TT],
+                                            const uint16_t *const xrow[MTILES], int kbase, int K, int kb)
+{
+    constexpr bool WIDE = (G == 128);
+    constexpr int GPS = MStage<MTILES, TT, G>::GPS;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        if (WIDE) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(wrow[tt] + (kbase / 2 + 16 * kb));
+            st.w[tt][0] = v.x;
+            st.w[tt][1] = v.y;
+            st.w[tt][2] = v.z;
+            st.w[tt][3] = v.w;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                st.w[tt][t] = (kbase + 32 * t < K)
+                                  ? *reinterpret_cast<const uint32_t *>(wrow[tt] + (kbase / 2 + 16 * t + 4 * kb))
+                                  : 0u;
+        }
+#pragma unroll
+        for (int g = 0; g < GPS; ++g) {
+            const int gi = (kbase + g * (128 / GPS)) / G;
+            const bool ok = kbase + g * (128 / GPS) < K;
+            st.s[tt][g] = ok ? srow[tt][gi] : 0.0f;
+            st.z[tt][g] = SYM ? 8.0f : (ok ? (float)zrow[tt][gi] : 0.0f);
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MTILES; ++mt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = WIDE ? kbase + 32 * kb + 8 * t : kbase + 32 * t + 8 * kb;
+            st.x[mt][t] = (k < K) ? *reinterpret_cast<const uint4 *>(xrow[mt] + k) : make_uint4(0, 0, 0, 0);
+        }
+}
+
+template <int MTILES, int TT, int G>
+__device__ __forceinline__ void mstage_compute(const MStage<MTILES, TT, G> &st, f32x4_t acc[TT][MTILES], uint32_t mask,
+                                               uint32_t magic)
+{
+    constexpr int GPS = MStage<MTILES, TT, G>::GPS;
+    constexpr int TPG = 4 / GPS;  // k-blocks (MFMAs) per group
+    const bf16x8_t ones = as_bf16x8(kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair);
+    bf16x8_t a[MTILES][4];
+#pragma unroll
+    for (int mt = 0; mt < MTILES; ++mt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            a[mt][t] = pair_x(st.x[mt][t]);
+    bf16x8_t b[TT][4];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            b[tt][t] = dequant_word(st.w[tt][t], mask, magic);
+#pragma unroll
+    for (int g = 0; g < GPS; ++g) {
+        f32x4_t xs[MTILES];
+#pragma unroll
+        for (int mt = 0; mt < MTILES; ++mt) {
+            xs[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = g * TPG; t < (g + 1) * TPG; ++t)
+                xs[mt] = mfma_bf16(a[mt][t], ones, xs[mt]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const float cf = -(16.0f + st.z[tt][g]);
+            const float sc = st.s[tt][g];
+#pragma unroll
+            for (int mt = 0; mt < MTILES; ++mt) {
+                f32x4_t d = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = g * TPG; t < (g + 1) * TPG; ++t)
+                    d = mfma_bf16(a[mt][t], b[tt][t], d);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[tt][mt][r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[mt][r], d[r]), acc[tt][mt][r]);
+            }
+        }
+    }
+}
+
+template <int MTILES, int TT, int G, bool SYM, bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__ x, int64_t M, int64_t N, int64_t K,
+                                                    const uint8_t *__restrict__ w, const float *__restrict__ scales,
+                                                    const uint8_t *__restrict__ zeros, void *__restrict__ y)
+{
+    __shared__ float red[kMfmaMaxWaves - 1][TT * MTILES * 4][kWave];
+    const int lane = threadIdx.x % kWave;
+    const int wv = threadIdx.x / kWave;
+    const int S = blockDim.x / kWave;
+    const int nl = lane % 16, kb = lane / 16;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * TT;
+    const int ksteps = (int)((K + 127) / 128);
+    const int ks_begin = ksteps * wv / S, ks_end = ksteps * (wv + 1) / S;
+    const uint32_t mask = vreg_const(kPairMask);
+    const uint32_t magic = vreg_const(SYM ? (kMagic16 ^ kSignFlip) : kMagic16);
+
+    const uint8_t *wrow[TT];
+    const float *srow[TT];
+    const uint8_t *zrow[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const int64_t n = std::min<int64_t>(n0 + 16 * tt + nl, N - 1);
+        wrow[tt] = w + n * (K / 2);
+        srow[tt] = scales + n * (K / G);
+        zrow[tt] = SYM ? nullptr : zeros + n * (K / G);
+    }
+    const uint16_t *xrow[MTILES];
+#pragma unroll
+    for (int mt = 0; mt < MTILES; ++mt)
+        xrow[mt] = x + std::min<int64_t>(mt * 16 + nl, M - 1) * K;
+
+    f32x4_t acc[TT][MTILES];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int mt = 0; mt < MTILES; ++mt)
+            acc[tt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    MStage<MTILES, TT, G> sa, sb;
+    int ks = ks_begin;
+    if (ks < ks_end)
+        mstage_load<MTILES, TT, G, SYM>(sa, wrow, srow, zrow, xrow, ks * 128, (int)K, kb);
+    while (ks < ks_end) {
+        if (ks + 1 < ks_end)
+            mstage_load<MTILES, TT, G, SYM>(sb, wrow, srow, zrow, xrow, (ks + 1) * 128, (int)K, kb);
+        mstage_compute<MTILES, TT, G>(sa, acc, mask, magic);
+        if (ks + 1 >= ks_end)
+            break;
+        if (ks + 2 < ks_end)
+            mstage_load<MTILES, TT, G, SYM>(sa, wrow, srow, zrow, xrow, (ks + 2) * 128, (int)K, kb);
+        mstage_compute<MTILES, TT, G>(sb, acc, mask, magic);
+        ks += 2;
+    }
+
+    // combine the S K-slices in wave order, then store: lane holds rows n = n0 + 16 tt + nl at tokens
+    // m = 16 mt + 4 kb + r
+    if (S > 1) {
+        if (wv > 0) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int mt = 0; mt < MTILES; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        red[wv - 1][(tt * MTILES + mt) * 4 + r][lane] = acc[tt][mt][r];
+        }
+        __syncthreads();
+        if (wv > 0)
+            return;
+        for (int i = 1; i < S; ++i)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int mt = 0; mt < MTILES; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[tt][mt][r] += red[i - 1][(tt * MTILES + mt) * 4 + r][lane];
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const int64_t n = n0 + 16 * tt + nl;
+        if (n >= N)
+            continue;
+#pragma unroll
+        for (int mt = 0; mt < MTILES; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = mt * 16 + 4 * kb + r;
+                if (m < M) {
+                    if (OUT_BF16)
+                        reinterpret_cast<uint16_t *>(y)[m * N + n] = (uint16_t)f32_to_bf16_bits(acc[tt][mt][r]);
+                    else
+                        reinterpret_cast<float *>(y)[m * N + n] = acc[tt][mt][r];
+                }
+            }
     }
 }
 
 namespace {
 
-template <int MT, int R, bool SYM>
+// Waves per block: split K until the grid holds about `target_waves` waves, keeping at least one full
+// 2048-code iteration per wave.
+inline int waves_per_row_block(int64_t rowblocks, int64_t K, int64_t target_waves)
+{
+    const int64_t chunks = K / 32;
+    int S = 1;
+    while (S < kMaxWavesPerRow && rowblocks * S < target_waves && chunks / (2 * S) >= kWave)
+        S *= 2;
+    return S;
+}
+
+template <int MT, int R, int G, bool SYM>
 hipError_t gemv_launch(const W4A16Args &a, const uint16_t *x, void *y, hipStream_t st)
 {
     const int64_t rowblocks = (a.N + R - 1) / R;
-    const int64_t chunks = a.K / 32;
-    int S = 1;
-    while (S < kMaxWavesPerRow && rowblocks * S < 4096 && chunks / (2 * S) >= kWave)
-        S *= 2;
+    const int S = waves_per_row_block(rowblocks, a.K, 4096);
     const dim3 grid((unsigned)rowblocks), block(kWave * S);
     if (a.y_bf16)
-        k_w4a16_gemv<MT, R, SYM, true><<<grid, block, 0, st>>>(x, a.N, a.K, a.w, a.scales, a.zeros, a.group_size, y,
-                                                               a.N);
+        k_w4a16_gemv<MT, R, G, SYM, true><<<grid, block, 0, st>>>(x, a.N, a.K, a.w, a.scales, a.zeros, y, a.N);
     else
-        k_w4a16_gemv<MT, R, SYM, false><<<grid, block, 0, st>>>(x, a.N, a.K, a.w, a.scales, a.zeros, a.group_size,
-                                                                y, a.N);
+        k_w4a16_gemv<MT, R, G, SYM, false><<<grid, block, 0, st>>>(x, a.N, a.K, a.w, a.scales, a.zeros, y, a.N);
     return hipGetLastError();
 }
 
-template <bool SYM>
+template <int G, bool SYM>
 hipError_t gemv_mt(const W4A16Args &a, int mt, const uint16_t *x, void *y, hipStream_t st)
 {
     switch (mt) {
     case 1:
-        return gemv_launch<1, 4, SYM>(a, x, y, st);
+        return gemv_launch<1, 4, G, SYM>(a, x, y, st);
     case 2:
-        return gemv_launch<2, 4, SYM>(a, x, y, st);
+        return gemv_launch<2, 4, G, SYM>(a, x, y, st);
     case 3:
-        return gemv_launch<3, 2, SYM>(a, x, y, st);
+        return gemv_launch<3, 2, G, SYM>(a, x, y, st);
     default:
-        return gemv_launch<4, 2, SYM>(a, x, y, st);
+        return gemv_launch<4, 2, G, SYM>(a, x, y, st);
+    }
+}
+
+// Matrix-core launch for up to 16 * MTILES tokens.
+template <int MTILES, int TT, int G, bool SYM>
+hipError_t mfma_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
+{
+    const int64_t blocks = (a.N + 16 * TT - 1) / (16 * TT);
+    const int64_t ksteps = (a.K + 127) / 128;
+    int S = 1;
+    while (S < kMfmaMaxWaves && blocks * S < 4096 && ksteps / (2 * S) >= 4)
+        S *= 2;
+    const dim3 grid((unsigned)blocks), block(kWave * S);
+    if (a.y_bf16)
+        k_w4a16_mfma<MTILES, TT, G, SYM, true><<<grid, block, 0, st>>>(x, M, a.N, a.K, a.w, a.scales, a.zeros, y);
+    else
+        k_w4a16_mfma<MTILES, TT, G, SYM, false><<<grid, block, 0, st>>>(x, M, a.N, a.K, a.w, a.scales, a.zeros, y);
+    return hipGetLastError();
+}
+
+template <int G, bool SYM>
+hipError_t mfma_m(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
+{
+    if (M <= 16)
+        return mfma_launch<1, 2, G, SYM>(a, x, M, y, st);
+    if (M <= 32)
+        return mfma_launch<2, 2, G, SYM>(a, x, M, y, st);
+    return mfma_launch<4, 2, G, SYM>(a, x, M, y, st);
+}
+
+template <bool SYM>
+hipError_t mfma_g(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
+{
+    switch (a.group_size) {
+    case 32:
+        return mfma_m<32, SYM>(a, x, M, y, st);
+    case 64:
+        return mfma_m<64, SYM>(a, x, M, y, st);
+    default:
+        return mfma_m<128, SYM>(a, x, M, y, st);
+    }
+}
+
+template <bool SYM>
+hipError_t gemv_g(const W4A16Args &a, int mt, const uint16_t *x, void *y, hipStream_t st)
+{
+    switch (a.group_size) {
+    case 32:
+        return gemv_mt<32, SYM>(a, mt, x, y, st);
+    case 64:
+        return gemv_mt<64, SYM>(a, mt, x, y, st);
+    default:
+        return gemv_mt<128, SYM>(a, mt, x, y, st);
     }
 }
 
 }  // namespace
 
+// Tokens at or above which the matrix-core kernel replaces the vector kernel.
+constexpr int64_t kMfmaMinTokens = 5;
+
 hipError_t launch_w4a16(const W4A16Args &a, hipStream_t st)
 {
     const size_t ysz = a.y_bf16 ? 2 : 4;
+    if (a.M >= kMfmaMinTokens) {
+        for (int64_t m0 = 0; m0 < a.M; m0 += 64) {
+            const int64_t mc = std::min<int64_t>(64, a.M - m0);
+            const uint16_t *x = a.x + m0 * a.K;
+            void *y = static_cast<char *>(a.y) + (size_t)m0 * (size_t)a.N * ysz;
+            hipError_t e = a.symmetric ? mfma_g<true>(a, x, mc, y, st) : mfma_g<false>(a, x, mc, y, st);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
     for (int64_t m0 = 0; m0 < a.M; m0 += 4) {
         const int mt = (int)std::min<int64_t>(4, a.M - m0);
         const uint16_t *x = a.x + m0 * a.K;
         void *y = static_cast<char *>(a.y) + (size_t)m0 * (size_t)a.N * ysz;
-        hipError_t e = a.symmetric ? gemv_mt<true>(a, mt, x, y, st) : gemv_mt<false>(a, mt, x, y, st);
+        hipError_t e = a.symmetric ? gemv_g<true>(a, mt, x, y, st) : gemv_g<false>(a, mt, x, y, st);
         if (e != hipSuccess)
             return e;
     }
