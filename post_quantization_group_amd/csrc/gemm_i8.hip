@@ -5,171 +5,226 @@
 // accumulation, dequantized output; "模型压缩：量化、ZeroQuant、LLM.int8() 与 SmoothQuant" §11: one scale per
 // row of the left operand and one per column of the right operand).
 //
-// Tiling. v_mfma_i32_16x16x64_i8 multiplies a 16x64 by a 64x16 int8 tile. The weight tile is fed as the
-// MFMA "A" operand and the activation tile as "B", so the 16x16 result lands with each lane holding four
-// consecutive output channels n of one token m: the epilogue writes 16 bytes (int32) or 8 bytes (bf16)
-// per lane, contiguous along the output row.
-//   block: 256 threads = 4 waves in a 2 (n) x 2 (m) arrangement; block tile 128 (n) x 128 (m), K step 64
-//   wave : 64 (n) x 64 (m) = 4 x 4 MFMA tiles, 16 int32 accumulators of 4 registers
-//   LDS  : two stages of [128][64 + 16 pad] bytes for each operand; global -> register -> LDS staging with
-//          the next K step's loads in flight while the current one is multiplied.
-// Both operands are read from LDS with one 16-byte read per lane per 16x64 fragment: lane l takes row
-// l % 16 and bytes [16 (l / 16), 16 (l / 16) + 16) of the 64-byte K slice. A and B use the same
-// lane-to-k assignment, so the products pair up whatever k order the instruction uses internally.
+// Instruction. v_mfma_i32_32x32x32_i8 (32x32 output, 32 deep) sustains about twice the int8 rate of the
+// 16x16x64 form on gfx950, so it is the building block. The weight tile is the MFMA "A" operand and the
+// activation tile "B": lane l holds output column m = l % 32 and, in accumulator register r, output row
+// n = 8 (r / 4) + 4 (l / 32) + r % 4, i.e. four consecutive output channels per group of four registers;
+// the epilogue writes them as one 16-byte (int32) or 8-byte (bf16) store.
+// Tiling.
+//   block: BN (n) x BM (m) output tile, split into waves of WN x WM; K step of BK bytes (BK / 32 MFMA
+//          depths; 64 or 128).
+//   wave : (WN/32) x (WM/32) MFMA tiles; per K step 2 (WN/32 + WM/32) 16-byte fragment reads from LDS.
+//   LDS  : two stages of [BN][BK] (weights) and [BM][BK] (activations) bytes, swizzled; the next K step's
+//          global loads are in flight (in registers) while the current one is multiplied.
+// A fragment of depth 32 at sub-step s is row l % 32, 16-byte piece 2 s + l / 32 of the 64-byte K slice
+// for both operands, so the products pair up whatever k order the instruction uses internally.
+// Blocks are dispatched round-robin over the 8 XCDs; block b is remapped so that each XCD walks a
+// contiguous range of tiles, token tiles fastest, and its L2 keeps reusing the same weight tiles.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace pqg {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kBN = 128;           // output channels per block (MFMA A side)
-constexpr int kBM = 128;           // tokens per block (MFMA B side)
-constexpr int kBK = 64;            // K bytes per step
-constexpr int kLdsStride = kBK + 16;  // padded row stride (bytes)
+constexpr int kXcds = 8;
 
-template <int MODE>  // 0: raw int32, 1: bf16 epilogue, 2: fp32 epilogue
-__global__ __launch_bounds__(256) void k_gemm_i8(const int8_t *__restrict__ a, const int8_t *__restrict__ b,
-                                                 int64_t M, int64_t N, int64_t K, const float *__restrict__ sa,
-                                                 const float *__restrict__ sb, void *__restrict__ c)
+// LDS offset of 16-byte piece c of tile row r, for rows of BK bytes (64 or 128). gfx950 LDS serves a
+// 128-bit access over 64 banks of 4 bytes, 16 lanes per cycle: writes take 16 consecutive lanes (whole
+// rows of consecutive pieces); reads take lanes 0-7 with 16-23, 8-15 with 24-31, and so on, which for a
+// 32-row fragment means 16 rows r .. r + 7, r + 16 .. r + 23 reading the same piece. An xor of the piece
+// index with bits of the row spreads those rows over all 16 bank quads:
+//   64-byte rows (4 pieces, 4 rows share a bank pattern mod 256 B): row bits 2 and 4;
+//   128-byte rows (8 pieces, 2 rows per 256 B): row bits 1, 2 and 4.
+template <int BK>
+__device__ __forceinline__ int lds_off(int r, int c)
 {
-    __shared__ __attribute__((aligned(16))) int8_t sW[2][kBN * kLdsStride];
-    __shared__ __attribute__((aligned(16))) int8_t sX[2][kBM * kLdsStride];
+    if (BK == 64)
+        return r * BK + 16 * (c ^ (((r >> 2) & 1) | ((r >> 3) & 2)));
+    return r * BK + 16 * (c ^ (((r >> 1) & 3) | ((r >> 2) & 4)));
+}
+
+// Epilogue for four consecutive output channels nb .. nb + 3 at token m.
+template <int MODE>
+__device__ __forceinline__ void store4(const int v[4], int64_t m, int64_t nb, int64_t M, int64_t N, float sxm,
+                                       const float *__restrict__ sb, void *__restrict__ c, bool vec_ok)
+{
+    if (m >= M)
+        return;
+    if (MODE == 0) {
+        int32_t *out = static_cast<int32_t *>(c) + m * N + nb;
+        if (vec_ok && nb + 3 < N) {
+            *reinterpret_cast<v4i *>(out) = v4i{v[0], v[1], v[2], v[3]};
+        } else {
+            for (int r = 0; r < 4; ++r)
+                if (nb + r < N)
+                    out[r] = v[r];
+        }
+        return;
+    }
+    float f[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float swn = (nb + r < N) ? sb[nb + r] : 0.0f;
+        f[r] = (float)v[r] * (sxm * swn);
+    }
+    if (MODE == 1) {
+        uint16_t *out = static_cast<uint16_t *>(c) + m * N + nb;
+        if (vec_ok && nb + 3 < N) {
+            *reinterpret_cast<uint2 *>(out) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+        } else {
+            for (int r = 0; r < 4; ++r)
+                if (nb + r < N)
+                    out[r] = (uint16_t)f32_to_bf16_bits(f[r]);
+        }
+    } else {
+        float *out = static_cast<float *>(c) + m * N + nb;
+        if (vec_ok && nb + 3 < N) {
+            *reinterpret_cast<float4 *>(out) = make_float4(f[0], f[1], f[2], f[3]);
+        } else {
+            for (int r = 0; r < 4; ++r)
+                if (nb + r < N)
+                    out[r] = f[r];
+        }
+    }
+}
+
+template <int BN, int BM, int WN, int WM, int BK, int MODE>  // MODE 0: raw int32, 1: bf16, 2: fp32 epilogue
+__global__ __launch_bounds__((BN / WN) * (BM / WM) * 64) void k_gemm_i8(
+    const int8_t *__restrict__ a, const int8_t *__restrict__ b, int64_t M, int64_t N, int64_t K,
+    const float *__restrict__ sa, const float *__restrict__ sb, void *__restrict__ c, int tiles)
+{
+    constexpr int NT = (BN / WN) * (BM / WM) * 64;  // threads
+    constexpr int TN = WN / 32, TM = WM / 32;
+    constexpr int NP = BK / 16;                          // 16-byte pieces per tile row
+    constexpr int WP = BN * NP, XP = BM * NP;            // pieces per K step
+    constexpr int WLOADS = (WP + NT - 1) / NT;            // per thread
+    constexpr int XLOADS = (XP + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) int8_t sW[2][BN * BK];
+    __shared__ __attribute__((aligned(16))) int8_t sX[2][BM * BK];
+
+    // XCD-aware tile order: XCD x = blockIdx % 8 takes tiles [x * per, (x + 1) * per)
+    const int per = (tiles + kXcds - 1) / kXcds;
+    const int t = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+    if (t >= tiles)
+        return;
+    const int m_tiles = (int)((M + BM - 1) / BM);
+    const int64_t n0 = (int64_t)(t / m_tiles) * BN;
+    const int64_t m0 = (int64_t)(t % m_tiles) * BM;
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wv = tid / kWave;
-    const int wn = wv % 2, wm = wv / 2;
-    const int64_t n_tiles = (N + kBN - 1) / kBN;
-    const int64_t n0 = (int64_t)(blockIdx.x % n_tiles) * kBN;
-    const int64_t m0 = (int64_t)(blockIdx.x / n_tiles) * kBM;
+    const int wn = wv % (BN / WN), wm = wv / (BN / WN);
 
-    // global -> LDS assignment: each operand tile is 128 rows x 4 pieces of 16 bytes = 512 pieces,
-    // two per thread: piece p = tid + 256 i -> row p / 4, piece p % 4.
-    int ldr[2], ldp[2];
+    // global -> LDS assignment: piece p = tid + NT i -> row p / NP, 16-byte piece p % NP of the K slice
+    auto load_tiles = [&](int64_t k0, uint4 rw[WLOADS], uint4 rx[XLOADS]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int p = tid + 256 * i;
-        ldr[i] = p / 4;
-        ldp[i] = p % 4;
-    }
-    auto load_tiles = [&](int64_t k0, uint4 rw[2], uint4 rx[2]) {
+        for (int i = 0; i < WLOADS; ++i) {
+            const int p = tid + NT * i;
+            const int64_t nr = n0 + p / NP, kk = k0 + (p % NP) * 16;
+            rw[i] = (p < WP && nr < N && kk < K) ? *reinterpret_cast<const uint4 *>(b + nr * K + kk)
+                                                 : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t kk = k0 + ldp[i] * 16;
-            const int64_t nr = n0 + ldr[i], mr = m0 + ldr[i];
-            rw[i] = (nr < N && kk < K) ? *reinterpret_cast<const uint4 *>(b + nr * K + kk) : make_uint4(0, 0, 0, 0);
-            rx[i] = (mr < M && kk < K) ? *reinterpret_cast<const uint4 *>(a + mr * K + kk) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < XLOADS; ++i) {
+            const int p = tid + NT * i;
+            const int64_t mr = m0 + p / NP, kk = k0 + (p % NP) * 16;
+            rx[i] = (p < XP && mr < M && kk < K) ? *reinterpret_cast<const uint4 *>(a + mr * K + kk)
+                                                 : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_tiles = [&](int st, const uint4 rw[2], const uint4 rx[2]) {
+    auto store_tiles = [&](int st, const uint4 rw[WLOADS], const uint4 rx[XLOADS]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<uint4 *>(&sW[st][ldr[i] * kLdsStride + ldp[i] * 16]) = rw[i];
-            *reinterpret_cast<uint4 *>(&sX[st][ldr[i] * kLdsStride + ldp[i] * 16]) = rx[i];
+        for (int i = 0; i < WLOADS; ++i) {
+            const int p = tid + NT * i;
+            if (p < WP)
+                *reinterpret_cast<uint4 *>(&sW[st][lds_off<BK>(p / NP, p % NP)]) = rw[i];
+        }
+#pragma unroll
+        for (int i = 0; i < XLOADS; ++i) {
+            const int p = tid + NT * i;
+            if (p < XP)
+                *reinterpret_cast<uint4 *>(&sX[st][lds_off<BK>(p / NP, p % NP)]) = rx[i];
         }
     };
 
-    v4i acc[4][4];
+    v16i acc[TN][TM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0;
 
-    uint4 rw[2], rx[2];
+    uint4 rw[WLOADS], rx[XLOADS];
     load_tiles(0, rw, rx);
     store_tiles(0, rw, rx);
     __syncthreads();
 
-    const int frow = lane % 16;
-    const int fcol = (lane / 16) * 16;
-    const int nsteps = (int)((K + kBK - 1) / kBK);
+    const int frow = lane % 32;
+    const int fhalf = lane / 32;
+    const int nsteps = (int)((K + BK - 1) / BK);
     for (int step = 0; step < nsteps; ++step) {
         const int cur = step & 1;
         if (step + 1 < nsteps)
-            load_tiles((int64_t)(step + 1) * kBK, rw, rx);
-        v4i fa[4], fb[4];
+            load_tiles((int64_t)(step + 1) * BK, rw, rx);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[i] = *reinterpret_cast<const v4i *>(&sW[cur][(wn * 64 + i * 16 + frow) * kLdsStride + fcol]);
+        for (int s = 0; s < BK / 32; ++s) {
+            v4i fb[TM];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            fb[j] = *reinterpret_cast<const v4i *>(&sX[cur][(wm * 64 + j * 16 + frow) * kLdsStride + fcol]);
+            for (int j = 0; j < TM; ++j)
+                fb[j] = *reinterpret_cast<const v4i *>(&sX[cur][lds_off<BK>(wm * WM + j * 32 + frow, 2 * s + fhalf)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < TN; ++i) {
+                const v4i fa =
+                    *reinterpret_cast<const v4i *>(&sW[cur][lds_off<BK>(wn * WN + i * 32 + frow, 2 * s + fhalf)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < TM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa, fb[j], acc[i][j], 0, 0, 0);
+            }
+        }
         if (step + 1 < nsteps)
             store_tiles(cur ^ 1, rw, rx);
         __syncthreads();
     }
 
-    // epilogue: lane holds acc rows n = 4 (lane / 16) + r (r = 0..3) of each 16x16 tile, column m = lane % 16
-    // vector stores need every row start 16-byte (int32 / fp32) or 8-byte (bf16) aligned
+    // epilogue: register group g (4 registers) of a 32x32 tile holds rows 8 g + 4 (lane / 32) + 0..3 at
+    // token column lane % 32
     const bool vec_ok = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(c) % (MODE == 1 ? 8 : 16)) == 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 64 + j * 16 + (lane % 16);
-        if (m >= M)
-            continue;
-        const float sxm = (MODE == 0) ? 0.0f : sa[m];
+    for (int j = 0; j < TM; ++j) {
+        const int64_t m = m0 + wm * WM + j * 32 + frow;
+        const float sxm = (MODE == 0 || m >= M) ? 0.0f : sa[m];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t nb = n0 + wn * 64 + i * 16 + 4 * (lane / 16);
-            const v4i v = acc[i][j];
-            if (MODE == 0) {
-                int32_t *out = static_cast<int32_t *>(c) + m * N + nb;
-                if (vec_ok && nb + 3 < N) {
-                    *reinterpret_cast<v4i *>(out) = v;
-                } else {
-                    for (int r = 0; r < 4; ++r)
-                        if (nb + r < N)
-                            out[r] = v[r];
-                }
-            } else {
-                float f[4];
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float swn = (nb + r < N) ? sb[nb + r] : 0.0f;
-                    f[r] = (float)v[r] * (sxm * swn);
-                }
-                if (MODE == 1) {
-                    uint16_t *out = static_cast<uint16_t *>(c) + m * N + nb;
-                    if (vec_ok && nb + 3 < N) {
-                        *reinterpret_cast<uint2 *>(out) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
-                    } else {
-                        for (int r = 0; r < 4; ++r)
-                            if (nb + r < N)
-                                out[r] = (uint16_t)f32_to_bf16_bits(f[r]);
-                    }
-                } else {
-                    float *out = static_cast<float *>(c) + m * N + nb;
-                    if (vec_ok && nb + 3 < N) {
-                        *reinterpret_cast<float4 *>(out) = make_float4(f[0], f[1], f[2], f[3]);
-                    } else {
-                        for (int r = 0; r < 4; ++r)
-                            if (nb + r < N)
-                                out[r] = f[r];
-                    }
-                }
+            for (int g = 0; g < 4; ++g) {
+                const int v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                const int64_t nb = n0 + wn * WN + i * 32 + 8 * g + 4 * fhalf;
+                store4<MODE>(v, m, nb, M, N, sxm, sb, c, vec_ok);
             }
-        }
     }
 }
 
-hipError_t launch_gemm_i8(const GemmI8Args &g, hipStream_t st)
+template <int BN, int BM, int WN, int WM, int BK = 64>
+hipError_t gemm_launch(const GemmI8Args &g, hipStream_t st)
 {
-    const int64_t tiles = ((g.N + kBN - 1) / kBN) * ((g.M + kBM - 1) / kBM);
-    const dim3 grid((unsigned)tiles), block(256);
+    constexpr int NT = (BN / WN) * (BM / WM) * 64;
+    const int64_t tiles = ((g.N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
+    const int64_t per = (tiles + kXcds - 1) / kXcds;
+    const dim3 grid((unsigned)(per * kXcds)), block(NT);
     if (g.sa == nullptr)
-        k_gemm_i8<0><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, nullptr, nullptr, g.c);
+        k_gemm_i8<BN, BM, WN, WM, BK, 0><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, nullptr, nullptr, g.c, (int)tiles);
     else if (g.c_bf16)
-        k_gemm_i8<1><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, g.sa, g.sb, g.c);
+        k_gemm_i8<BN, BM, WN, WM, BK, 1><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, g.sa, g.sb, g.c, (int)tiles);
     else
-        k_gemm_i8<2><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, g.sa, g.sb, g.c);
+        k_gemm_i8<BN, BM, WN, WM, BK, 2><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, g.sa, g.sb, g.c, (int)tiles);
     return hipGetLastError();
 }
+
+hipError_t launch_gemm_i8(const GemmI8Args &g, hipStream_t st) { return gemm_launch<128, 128, 32, 64, 64>(g, st); }
 
 }  // namespace pqg
