@@ -7,20 +7,23 @@
 // Design (small M, the decode case):
 //   * A block owns R output rows; its S waves split K into contiguous slices. Each lane reads 16 bytes
 //     (32 codes) of each of the R rows per iteration, so one wave instruction streams 1 KB of a row
-//     (fully coalesced 128-bit loads). Row base pointers are uniform (scalar registers) and lanes add
-//     32-bit offsets, so addressing costs almost no vector instructions. The S partial sums of a row
-//     are combined once, through LDS, in a fixed order (deterministic).
+//     (fully coalesced 128-bit loads, non-temporal: the weight stream is read once and should not evict
+//     the activations from the caches). Row base pointers are uniform (scalar registers) and lanes add
+//     32-bit offsets, so addressing costs almost no vector instructions. The S partial sums of a row are
+//     combined once, through LDS, in a fixed order (deterministic).
 //   * Two register stages alternate, so the next chunk's loads are in flight while the current one is
-//     reduced.
-//   * Dequantization stays in registers and costs one shift and one v_bitop3_b32 per pair of codes: the
-//     nibble pair (j, j + 4) of a packed word is moved to bits [3, 7) of each 16-bit half and merged with
-//     the bf16 pattern of 16.0, giving the exact value 16 + u. For two's-complement codes the same
-//     instruction flips the nibble's sign bit, turning q into its offset binary q + 8.
+//     reduced. The loop has a uniform trip count and no branches: every iteration loads (addresses past
+//     the slice are clamped to its last chunk) and computes, and chunks outside the slice get a zero
+//     scale. Divergent branches around the loads would make the compiler drain all outstanding loads at
+//     their joins.
+//   * Dequantization stays in registers and costs at most one shift and one v_bitop3_b32 per pair of
+//     codes: the nibble pair (j, j + 4) of a packed word is moved to bits [0, 4) of each 16-bit half and
+//     merged with the bf16 pattern of 128.0, giving the exact value 128 + u (the bf16 mantissa step at 128
+//     is 1). For two's-complement codes the same instruction flips the nibble's sign bit, turning q into
+//     its offset binary q + 8. Pair 0 needs no shift.
 //   * The products use v_dot2_f32_bf16 (two bf16 products, fp32 accumulation). The code offset is removed
-//     once per 32 codes: sum x (u - off) = sum x (16 + u) - (16 + off) sum x, with off = 8 (symmetric)
-//     or z (asymmetric). The group scale multiplies each 32-code partial sum. The offset 16 keeps the
-//     accumulated magnitudes within a few times those of the true partial sums, so little precision is
-//     lost to the subtraction.
+//     once per 32 codes: sum x (u - off) = sum x (128 + u) - (128 + off) sum x, with off = 8 (symmetric)
+//     or z (asymmetric), then the group scale multiplies the 32-code partial sum.
 //   * No dequantized weight is ever written to memory.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -28,6 +31,7 @@
 namespace pqg {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {
@@ -44,9 +48,14 @@ __device__ __forceinline__ uint32_t vreg_const(uint32_t c)
     return r;
 }
 
+// 16 + u form (nibbles at bits [3, 7)), used by the matrix-core kernel
 constexpr uint32_t kPairMask = 0x00780078u;
 constexpr uint32_t kMagic16 = 0x41804180u;      // bf16 16.0 | 16.0
 constexpr uint32_t kSignFlip = 0x00400040u;     // bit 6 of each half: the nibble's top bit
+// 128 + u form (nibbles at bits [0, 4)), used by the vector kernel
+constexpr uint32_t kNibbleMask = 0x000F000Fu;
+constexpr uint32_t kMagic128 = 0x43004300u;     // bf16 128.0 | 128.0
+constexpr uint32_t kSignFlip128 = 0x00080008u;  // bit 3 of each half
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // bf16 1.0 | 1.0
 constexpr int kMaxWavesPerRow = 8;
 
@@ -79,8 +88,10 @@ __device__ __forceinline__ void stage_load(Stage<MT, R> &st, const Bases<MT, R> 
 {
     constexpr int kGroupShift = (G == 128) ? 2 : (G == 64) ? 1 : 0;  // chunk -> group index
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        st.w[r] = *reinterpret_cast<const uint4 *>(b.w[r] + c * 16u);
+    for (int r = 0; r < R; ++r) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(b.w[r] + c * 16u));
+        st.w[r] = make_uint4(v.x, v.y, v.z, v.w);
+    }
     const uint32_t gi = c >> kGroupShift;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -128,10 +139,10 @@ __device__ __forceinline__ void stage_compute(const Stage<MT, R> &st, float acc[
             part[m] = 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const uint32_t b0 = pair_bits(wd[d] << 3, mask, magic);
-            const uint32_t b1 = pair_bits(wd[d] >> 1, mask, magic);
-            const uint32_t b2 = pair_bits(wd[d] >> 5, mask, magic);
-            const uint32_t b3 = pair_bits(wd[d] >> 9, mask, magic);
+            const uint32_t b0 = pair_bits(wd[d], mask, magic);
+            const uint32_t b1 = pair_bits(wd[d] >> 4, mask, magic);
+            const uint32_t b2 = pair_bits(wd[d] >> 8, mask, magic);
+            const uint32_t b3 = pair_bits(wd[d] >> 12, mask, magic);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 part[m] = dot2(xp[m][4 * d + 0], b0, part[m]);
@@ -140,10 +151,10 @@ __device__ __forceinline__ void stage_compute(const Stage<MT, R> &st, float acc[
                 part[m] = dot2(xp[m][4 * d + 3], b3, part[m]);
             }
         }
-        // sum_k x (u - off) = sum_k x (16 + u) - (16 + off) sum_k x, then the group scale
+        // sum_k x (u - off) = sum_k x (128 + u) - (128 + off) sum_k x, then the group scale
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            acc[r][m] = __builtin_fmaf(st.s[r], __builtin_fmaf(-(16.0f + st.z[r]), xsum[m], part[m]), acc[r][m]);
+            acc[r][m] = __builtin_fmaf(st.s[r], __builtin_fmaf(-(128.0f + st.z[r]), xsum[m], part[m]), acc[r][m]);
     }
 }
 
@@ -156,15 +167,16 @@ __global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__
 {
     __shared__ float red[kMaxWavesPerRow][R * MT];
     const int lane = threadIdx.x % kWave;
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar loop bounds
     const int S = blockDim.x / kWave;
     const int64_t row0 = (int64_t)blockIdx.x * R;
     const int chunks = (int)(K / 32);  // 32 codes = 16 bytes per lane
     const int s_shift = __builtin_ctz(S);  // S is a power of two
     const int c_begin = (chunks * wv) >> s_shift;
     const int c_end = (chunks * (wv + 1)) >> s_shift;
-    const uint32_t mask = vreg_const(kPairMask);
-    const uint32_t magic = vreg_const(SYM ? (kMagic16 ^ kSignFlip) : kMagic16);
+    const int c_last = c_end - 1;
+    const uint32_t mask = vreg_const(kNibbleMask);
+    const uint32_t magic = vreg_const(SYM ? (kMagic128 ^ kSignFlip128) : kMagic128);
 
     Bases<MT, R> bp;
 #pragma unroll
@@ -185,23 +197,27 @@ __global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__
         for (int m = 0; m < MT; ++m)
             acc[r][m] = 0.0f;
 
-    // two register stages, alternating: loads of chunk c + 64 are in flight while chunk c is reduced
-    Stage<MT, R> sa, sb;
-    int c = c_begin + lane;
-    if (c < c_end)
-        stage_load<MT, R, G, SYM>(sa, bp, (uint32_t)c);
-    while (c < c_end) {
-        const int c1 = c + kWave;
-        if (c1 < c_end)
-            stage_load<MT, R, G, SYM>(sb, bp, (uint32_t)c1);
-        stage_compute<MT, R>(sa, acc, mask, magic);
-        if (c1 >= c_end)
-            break;
-        const int c2 = c1 + kWave;
-        if (c2 < c_end)
-            stage_load<MT, R, G, SYM>(sa, bp, (uint32_t)c2);
-        stage_compute<MT, R>(sb, acc, mask, magic);
-        c = c2;
+    // two register stages: the loads of iteration it + 1 are in flight while iteration it is reduced
+    const int iters = (c_end - c_begin + kWave - 1) / kWave;
+    const int iters2 = (iters + 1) & ~1;
+    Stage<MT, R> st[2];
+    {
+        const int c = c_begin + lane;
+        stage_load<MT, R, G, SYM>(st[0], bp, (uint32_t)(c < c_last ? c : c_last));
+    }
+    for (int it = 0; it < iters2; it += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int cn = c_begin + lane + kWave * (it + h + 1);
+            stage_load<MT, R, G, SYM>(st[h ^ 1], bp, (uint32_t)(cn < c_last ? cn : c_last));
+            __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of this chunk's math
+            const bool ok = c_begin + lane + kWave * (it + h) < c_end;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                st[h].s[r] = ok ? st[h].s[r] : 0.0f;
+            stage_compute<MT, R>(st[h], acc, mask, magic);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
 #pragma unroll
@@ -291,7 +307,7 @@ __device__ __forceinline__ bf16x8_t pair_x(uint4 u)
                      __builtin_amdgcn_perm(u.w, u.y, 0x05040100u), __builtin_amdgcn_perm(u.w, u.y, 0x07060302u));
 }
 
-constexpr int kMfmaMaxWaves = 4;
+constexpr int kMfmaMaxWaves = 8;
 
 template <int MTILES, int TT, int G>
 struct MStage {
@@ -302,45 +318,52 @@ struct MStage {
     uint4 x[MTILES][4];
 };
 
+// Loads of one k-step. Every address is clamped into the tensor, so the loads are unconditional; parts of
+// a k-step past K (possible when g < 128) get a zero scale and add nothing.
 template <int MTILES, int TT, int G, bool SYM>
 __device__ __forceinline__ void mstage_load(MStage<MTILES, TT, G> &st, const uint8_t *const wrow[TT],
                                             const float *const srow[TT], const uint8_t *const zrow[TT],
-                                            const uint16_t *const xrow[MTILES], int kbase, int K, int kb)
+                                            const uint16_t *const xrow[MTILES], int kbase, int K, int kb, bool valid)
 {
     constexpr bool WIDE = (G == 128);
     constexpr int GPS = MStage<MTILES, TT, G>::GPS;
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
         if (WIDE) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(wrow[tt] + (kbase / 2 + 16 * kb));
+            const u32x4_t v =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(wrow[tt] + (kbase / 2 + 16 * kb)));
             st.w[tt][0] = v.x;
             st.w[tt][1] = v.y;
             st.w[tt][2] = v.z;
             st.w[tt][3] = v.w;
         } else {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                st.w[tt][t] = (kbase + 32 * t < K)
-                                  ? *reinterpret_cast<const uint32_t *>(wrow[tt] + (kbase / 2 + 16 * t + 4 * kb))
-                                  : 0u;
+            for (int t = 0; t < 4; ++t) {
+                const int kk = min(kbase + 32 * t, K - 32);
+                st.w[tt][t] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(wrow[tt] + (kk / 2 + 4 * kb)));
+            }
         }
 #pragma unroll
         for (int g = 0; g < GPS; ++g) {
-            const int gi = (kbase + g * (128 / GPS)) / G;
-            const bool ok = kbase + g * (128 / GPS) < K;
-            st.s[tt][g] = ok ? srow[tt][gi] : 0.0f;
-            st.z[tt][g] = SYM ? 8.0f : (ok ? (float)zrow[tt][gi] : 0.0f);
+            const int kg = kbase + g * (128 / GPS);
+            const bool ok = valid && kg < K;
+            const int gi = min(kg, K - 1) / G;
+            const float sv = srow[tt][gi];
+            st.s[tt][g] = ok ? sv : 0.0f;
+            st.z[tt][g] = SYM ? 8.0f : (float)zrow[tt][gi];
         }
     }
 #pragma unroll
     for (int mt = 0; mt < MTILES; ++mt)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int k = WIDE ? kbase + 32 * kb + 8 * t : kbase + 32 * t + 8 * kb;
-            st.x[mt][t] = (k < K) ? *reinterpret_cast<const uint4 *>(xrow[mt] + k) : make_uint4(0, 0, 0, 0);
+            const int k = min(WIDE ? kbase + 32 * kb + 8 * t : kbase + 32 * t + 8 * kb, K - 8);
+            st.x[mt][t] = *reinterpret_cast<const uint4 *>(xrow[mt] + k);
         }
 }
 
+// The MFMAs of one group run k-block outermost, so the MTILES * (TT + 1) accumulation chains interleave
+// instead of each waiting on its own previous result.
 template <int MTILES, int TT, int G>
 __device__ __forceinline__ void mstage_compute(const MStage<MTILES, TT, G> &st, f32x4_t acc[TT][MTILES], uint32_t mask,
                                                uint32_t magic)
@@ -363,39 +386,51 @@ __device__ __forceinline__ void mstage_compute(const MStage<MTILES, TT, G> &st, 
 #pragma unroll
     for (int g = 0; g < GPS; ++g) {
         f32x4_t xs[MTILES];
+        f32x4_t d[TT][MTILES];
 #pragma unroll
         for (int mt = 0; mt < MTILES; ++mt) {
             xs[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int t = g * TPG; t < (g + 1) * TPG; ++t)
+            for (int tt = 0; tt < TT; ++tt)
+                d[tt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int t = g * TPG; t < (g + 1) * TPG; ++t) {
+#pragma unroll
+            for (int mt = 0; mt < MTILES; ++mt)
                 xs[mt] = mfma_bf16(a[mt][t], ones, xs[mt]);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int mt = 0; mt < MTILES; ++mt)
+                    d[tt][mt] = mfma_bf16(a[mt][t], b[tt][t], d[tt][mt]);
         }
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             const float cf = -(16.0f + st.z[tt][g]);
             const float sc = st.s[tt][g];
 #pragma unroll
-            for (int mt = 0; mt < MTILES; ++mt) {
-                f32x4_t d = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int t = g * TPG; t < (g + 1) * TPG; ++t)
-                    d = mfma_bf16(a[mt][t], b[tt][t], d);
+            for (int mt = 0; mt < MTILES; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[tt][mt][r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[mt][r], d[r]), acc[tt][mt][r]);
-            }
+                    acc[tt][mt][r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[mt][r], d[tt][mt][r]), acc[tt][mt][r]);
         }
     }
 }
 
+// Waves per block at most: 8, or 4 for the widest token tile (its registers only fit at four waves).
+template <int MTILES>
+constexpr int mfma_max_waves() { return MTILES >= 4 ? 4 : kMfmaMaxWaves; }
+
 template <int MTILES, int TT, int G, bool SYM, bool OUT_BF16>
-__global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__ x, int64_t M, int64_t N, int64_t K,
-                                                    const uint8_t *__restrict__ w, const float *__restrict__ scales,
-                                                    const uint8_t *__restrict__ zeros, void *__restrict__ y)
+__global__ __launch_bounds__(64 * mfma_max_waves<MTILES>()) void k_w4a16_mfma(const uint16_t *__restrict__ x, int64_t M, int64_t N,
+                                                                   int64_t K, const uint8_t *__restrict__ w,
+                                                                   const float *__restrict__ scales,
+                                                                   const uint8_t *__restrict__ zeros, void *__restrict__ y)
 {
     __shared__ float red[kMfmaMaxWaves - 1][TT * MTILES * 4][kWave];
     const int lane = threadIdx.x % kWave;
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar loop bounds
     const int S = blockDim.x / kWave;
     const int nl = lane % 16, kb = lane / 16;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * TT;
@@ -426,20 +461,24 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__
         for (int mt = 0; mt < MTILES; ++mt)
             acc[tt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    MStage<MTILES, TT, G> sa, sb;
-    int ks = ks_begin;
-    if (ks < ks_end)
-        mstage_load<MTILES, TT, G, SYM>(sa, wrow, srow, zrow, xrow, ks * 128, (int)K, kb);
-    while (ks < ks_end) {
-        if (ks + 1 < ks_end)
-            mstage_load<MTILES, TT, G, SYM>(sb, wrow, srow, zrow, xrow, (ks + 1) * 128, (int)K, kb);
-        mstage_compute<MTILES, TT, G>(sa, acc, mask, magic);
-        if (ks + 1 >= ks_end)
-            break;
-        if (ks + 2 < ks_end)
-            mstage_load<MTILES, TT, G, SYM>(sa, wrow, srow, zrow, xrow, (ks + 2) * 128, (int)K, kb);
-        mstage_compute<MTILES, TT, G>(sb, acc, mask, magic);
-        ks += 2;
+    // uniform trip count, two register stages; k-steps past the slice load its last step and add nothing
+    const int n_ks = ks_end - ks_begin;
+    const int n_ks2 = (n_ks + 1) & ~1;
+    const int ks_last = max(ks_end - 1, ks_begin);
+    MStage<MTILES, TT, G> st[2];
+    mstage_load<MTILES, TT, G, SYM>(st[0], wrow, srow, zrow, xrow, ks_begin * 128, (int)K, kb, n_ks > 0);
+    for (int i = 0; i < n_ks2; i += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kn = i + h + 1;
+            mstage_load<MTILES, TT, G, SYM>(st[h ^ 1], wrow, srow, zrow, xrow, min(ks_begin + kn, ks_last) * 128,
+                                            (int)K, kb, kn < n_ks);
+            // keep the next stage's loads ahead of this stage's math: left alone, the scheduler sinks them
+            // towards their uses to shorten live ranges and the loop then waits on every load
+            __builtin_amdgcn_sched_barrier(0);
+            mstage_compute<MTILES, TT, G>(st[h], acc, mask, magic);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // combine the S K-slices in wave order, then store: lane holds rows n = n0 + 16 tt + nl at tokens
@@ -534,7 +573,7 @@ hipError_t mfma_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y
     const int64_t blocks = (a.N + 16 * TT - 1) / (16 * TT);
     const int64_t ksteps = (a.K + 127) / 128;
     int S = 1;
-    while (S < kMfmaMaxWaves && blocks * S < 4096 && ksteps / (2 * S) >= 4)
+    while (S < mfma_max_waves<MTILES>() && blocks * S < 4096 && ksteps / (2 * S) >= 2)
         S *= 2;
     const dim3 grid((unsigned)blocks), block(kWave * S);
     if (a.y_bf16)
