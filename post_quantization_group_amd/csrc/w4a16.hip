@@ -25,6 +25,9 @@
 //     once per 32 codes: sum x (u - off) = sum x (128 + u) - (128 + off) sum x, with off = 8 (symmetric)
 //     or z (asymmetric), then the group scale multiplies the 32-code partial sum.
 //   * No dequantized weight is ever written to memory.
+//
+// The matrix-core variant below keeps ordinary (allocating) weight loads: with non-temporal ones it ran
+// slower and left dirty lines in the last-level cache that slowed the kernels after it.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -307,7 +310,7 @@ __device__ __forceinline__ bf16x8_t pair_x(uint4 u)
                      __builtin_amdgcn_perm(u.w, u.y, 0x05040100u), __builtin_amdgcn_perm(u.w, u.y, 0x07060302u));
 }
 
-constexpr int kMfmaMaxWaves = 8;
+constexpr int kMfmaMaxWaves = 4;
 
 template <int MTILES, int TT, int G>
 struct MStage {
@@ -318,52 +321,45 @@ struct MStage {
     uint4 x[MTILES][4];
 };
 
-// Loads of one k-step. Every address is clamped into the tensor, so the loads are unconditional; parts of
-// a k-step past K (possible when g < 128) get a zero scale and add nothing.
 template <int MTILES, int TT, int G, bool SYM>
 __device__ __forceinline__ void mstage_load(MStage<MTILES, TT, G> &st, const uint8_t *const wrow[TT],
                                             const float *const srow[TT], const uint8_t *const zrow[TT],
-                                            const uint16_t *const xrow[MTILES], int kbase, int K, int kb, bool valid)
+                                            const uint16_t *const xrow[MTILES], int kbase, int K, int kb)
 {
     constexpr bool WIDE = (G == 128);
     constexpr int GPS = MStage<MTILES, TT, G>::GPS;
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
         if (WIDE) {
-            const u32x4_t v =
-                __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(wrow[tt] + (kbase / 2 + 16 * kb)));
+            const uint4 v = *reinterpret_cast<const uint4 *>(wrow[tt] + (kbase / 2 + 16 * kb));
             st.w[tt][0] = v.x;
             st.w[tt][1] = v.y;
             st.w[tt][2] = v.z;
             st.w[tt][3] = v.w;
         } else {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int kk = min(kbase + 32 * t, K - 32);
-                st.w[tt][t] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(wrow[tt] + (kk / 2 + 4 * kb)));
-            }
+            for (int t = 0; t < 4; ++t)
+                st.w[tt][t] = (kbase + 32 * t < K)
+                                  ? *reinterpret_cast<const uint32_t *>(wrow[tt] + (kbase / 2 + 16 * t + 4 * kb))
+                                  : 0u;
         }
 #pragma unroll
         for (int g = 0; g < GPS; ++g) {
-            const int kg = kbase + g * (128 / GPS);
-            const bool ok = valid && kg < K;
-            const int gi = min(kg, K - 1) / G;
-            const float sv = srow[tt][gi];
-            st.s[tt][g] = ok ? sv : 0.0f;
-            st.z[tt][g] = SYM ? 8.0f : (float)zrow[tt][gi];
+            const int gi = (kbase + g * (128 / GPS)) / G;
+            const bool ok = kbase + g * (128 / GPS) < K;
+            st.s[tt][g] = ok ? srow[tt][gi] : 0.0f;
+            st.z[tt][g] = SYM ? 8.0f : (ok ? (float)zrow[tt][gi] : 0.0f);
         }
     }
 #pragma unroll
     for (int mt = 0; mt < MTILES; ++mt)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int k = min(WIDE ? kbase + 32 * kb + 8 * t : kbase + 32 * t + 8 * kb, K - 8);
-            st.x[mt][t] = *reinterpret_cast<const uint4 *>(xrow[mt] + k);
+            const int k = WIDE ? kbase + 32 * kb + 8 * t : kbase + 32 * t + 8 * kb;
+            st.x[mt][t] = (k < K) ? *reinterpret_cast<const uint4 *>(xrow[mt] + k) : make_uint4(0, 0, 0, 0);
         }
 }
 
-// The MFMAs of one group run k-block outermost, so the MTILES * (TT + 1) accumulation chains interleave
-// instead of each waiting on its own previous result.
 template <int MTILES, int TT, int G>
 __device__ __forceinline__ void mstage_compute(const MStage<MTILES, TT, G> &st, f32x4_t acc[TT][MTILES], uint32_t mask,
                                                uint32_t magic)
@@ -386,51 +382,39 @@ __device__ __forceinline__ void mstage_compute(const MStage<MTILES, TT, G> &st, 
 #pragma unroll
     for (int g = 0; g < GPS; ++g) {
         f32x4_t xs[MTILES];
-        f32x4_t d[TT][MTILES];
 #pragma unroll
         for (int mt = 0; mt < MTILES; ++mt) {
             xs[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-                d[tt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-#pragma unroll
-        for (int t = g * TPG; t < (g + 1) * TPG; ++t) {
-#pragma unroll
-            for (int mt = 0; mt < MTILES; ++mt)
+            for (int t = g * TPG; t < (g + 1) * TPG; ++t)
                 xs[mt] = mfma_bf16(a[mt][t], ones, xs[mt]);
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-                for (int mt = 0; mt < MTILES; ++mt)
-                    d[tt][mt] = mfma_bf16(a[mt][t], b[tt][t], d[tt][mt]);
         }
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             const float cf = -(16.0f + st.z[tt][g]);
             const float sc = st.s[tt][g];
 #pragma unroll
-            for (int mt = 0; mt < MTILES; ++mt)
+            for (int mt = 0; mt < MTILES; ++mt) {
+                f32x4_t d = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = g * TPG; t < (g + 1) * TPG; ++t)
+                    d = mfma_bf16(a[mt][t], b[tt][t], d);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[tt][mt][r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[mt][r], d[tt][mt][r]), acc[tt][mt][r]);
+                    acc[tt][mt][r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[mt][r], d[r]), acc[tt][mt][r]);
+            }
         }
     }
 }
 
-// Waves per block at most: 8, or 4 for the widest token tile (its registers only fit at four waves).
-template <int MTILES>
-constexpr int mfma_max_waves() { return MTILES >= 4 ? 4 : kMfmaMaxWaves; }
-
 template <int MTILES, int TT, int G, bool SYM, bool OUT_BF16>
-__global__ __launch_bounds__(64 * mfma_max_waves<MTILES>()) void k_w4a16_mfma(const uint16_t *__restrict__ x, int64_t M, int64_t N,
-                                                                   int64_t K, const uint8_t *__restrict__ w,
-                                                                   const float *__restrict__ scales,
-                                                                   const uint8_t *__restrict__ zeros, void *__restrict__ y)
+__global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__ x, int64_t M, int64_t N, int64_t K,
+                                                    const uint8_t *__restrict__ w, const float *__restrict__ scales,
+                                                    const uint8_t *__restrict__ zeros, void *__restrict__ y)
 {
     __shared__ float red[kMfmaMaxWaves - 1][TT * MTILES * 4][kWave];
     const int lane = threadIdx.x % kWave;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar loop bounds
+    const int wv = threadIdx.x / kWave;
     const int S = blockDim.x / kWave;
     const int nl = lane % 16, kb = lane / 16;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * TT;
@@ -461,24 +445,20 @@ __global__ __launch_bounds__(64 * mfma_max_waves<MTILES>()) void k_w4a16_mfma(co
         for (int mt = 0; mt < MTILES; ++mt)
             acc[tt][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // uniform trip count, two register stages; k-steps past the slice load its last step and add nothing
-    const int n_ks = ks_end - ks_begin;
-    const int n_ks2 = (n_ks + 1) & ~1;
-    const int ks_last = max(ks_end - 1, ks_begin);
-    MStage<MTILES, TT, G> st[2];
-    mstage_load<MTILES, TT, G, SYM>(st[0], wrow, srow, zrow, xrow, ks_begin * 128, (int)K, kb, n_ks > 0);
-    for (int i = 0; i < n_ks2; i += 2) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int kn = i + h + 1;
-            mstage_load<MTILES, TT, G, SYM>(st[h ^ 1], wrow, srow, zrow, xrow, min(ks_begin + kn, ks_last) * 128,
-                                            (int)K, kb, kn < n_ks);
-            // keep the next stage's loads ahead of this stage's math: left alone, the scheduler sinks them
-            // towards their uses to shorten live ranges and the loop then waits on every load
-            __builtin_amdgcn_sched_barrier(0);
-            mstage_compute<MTILES, TT, G>(st[h], acc, mask, magic);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    MStage<MTILES, TT, G> sa, sb;
+    int ks = ks_begin;
+    if (ks < ks_end)
+        mstage_load<MTILES, TT, G, SYM>(sa, wrow, srow, zrow, xrow, ks * 128, (int)K, kb);
+    while (ks < ks_end) {
+        if (ks + 1 < ks_end)
+            mstage_load<MTILES, TT, G, SYM>(sb, wrow, srow, zrow, xrow, (ks + 1) * 128, (int)K, kb);
+        mstage_compute<MTILES, TT, G>(sa, acc, mask, magic);
+        if (ks + 1 >= ks_end)
+            break;
+        if (ks + 2 < ks_end)
+            mstage_load<MTILES, TT, G, SYM>(sa, wrow, srow, zrow, xrow, (ks + 2) * 128, (int)K, kb);
+        mstage_compute<MTILES, TT, G>(sb, acc, mask, magic);
+        ks += 2;
     }
 
     // combine the S K-slices in wave order, then store: lane holds rows n = n0 + 16 tt + nl at tokens
@@ -573,7 +553,7 @@ hipError_t mfma_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y
     const int64_t blocks = (a.N + 16 * TT - 1) / (16 * TT);
     const int64_t ksteps = (a.K + 127) / 128;
     int S = 1;
-    while (S < mfma_max_waves<MTILES>() && blocks * S < 4096 && ksteps / (2 * S) >= 2)
+    while (S < kMfmaMaxWaves && blocks * S < 4096 && ksteps / (2 * S) >= 4)
         S *= 2;
     const dim3 grid((unsigned)blocks), block(kWave * S);
     if (a.y_bf16)
