@@ -201,27 +201,30 @@ __global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__
             acc[r][m] = 0.0f;
 
     // two register stages: the loads of iteration it + 1 are in flight while iteration it is reduced
-    const int iters = (c_end - c_begin + kWave - 1) / kWave;
-    const int iters2 = (iters + 1) & ~1;
+    const int iters = (c_end - c_begin + kWave - 1) / kWave;  // uniform
     Stage<MT, R> st[2];
+    auto step = [&](int h, int it) {
+        const int cn = c_begin + lane + kWave * (it + 1);
+        stage_load<MT, R, G, SYM>(st[h ^ 1], bp, (uint32_t)(cn < c_last ? cn : c_last));
+        __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of this chunk's math
+        const bool ok = c_begin + lane + kWave * it < c_end;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            st[h].s[r] = ok ? st[h].s[r] : 0.0f;
+        stage_compute<MT, R>(st[h], acc, mask, magic);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     {
         const int c = c_begin + lane;
         stage_load<MT, R, G, SYM>(st[0], bp, (uint32_t)(c < c_last ? c : c_last));
     }
-    for (int it = 0; it < iters2; it += 2) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int cn = c_begin + lane + kWave * (it + h + 1);
-            stage_load<MT, R, G, SYM>(st[h ^ 1], bp, (uint32_t)(cn < c_last ? cn : c_last));
-            __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of this chunk's math
-            const bool ok = c_begin + lane + kWave * (it + h) < c_end;
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                st[h].s[r] = ok ? st[h].s[r] : 0.0f;
-            stage_compute<MT, R>(st[h], acc, mask, magic);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    int it = 0;
+    for (; it + 2 <= iters; it += 2) {
+        step(0, it);
+        step(1, it + 1);
     }
+    if (it < iters)  // odd trip count: one more chunk, in stage 0
+        step(0, it);
 
 #pragma unroll
     for (int r = 0; r < R; ++r)
