@@ -101,8 +101,12 @@ __global__ __launch_bounds__((BN / WN) * (BM / WM) * 64) void k_gemm_i8(
     constexpr int WP = BN * NP, XP = BM * NP;            // pieces per K step
     constexpr int WLOADS = (WP + NT - 1) / NT;            // per thread
     constexpr int XLOADS = (XP + NT - 1) / NT;
-    __shared__ __attribute__((aligned(16))) int8_t sW[2][BN * BK];
-    __shared__ __attribute__((aligned(16))) int8_t sX[2][BM * BK];
+    // operand stages; after the main loop the same memory stages the bf16 output tile
+    constexpr int kSmem = 2 * (BN + BM) * BK;
+    static_assert(kSmem >= BM * BN * 2, "the output tile must fit in the operand stages");
+    __shared__ __attribute__((aligned(16))) int8_t smem[kSmem];
+    int8_t(*sW)[BN * BK] = reinterpret_cast<int8_t(*)[BN * BK]>(smem);
+    int8_t(*sX)[BM * BK] = reinterpret_cast<int8_t(*)[BM * BK]>(smem + 2 * BN * BK);
 
     // XCD-aware tile order: XCD x = blockIdx % 8 takes tiles [x * per, (x + 1) * per)
     const int per = (tiles + kXcds - 1) / kXcds;
@@ -192,7 +196,48 @@ __global__ __launch_bounds__((BN / WN) * (BM / WM) * 64) void k_gemm_i8(
     }
 
     // epilogue: register group g (4 registers) of a 32x32 tile holds rows 8 g + 4 (lane / 32) + 0..3 at
-    // token column lane % 32
+    // token column lane % 32.
+    // bf16 output with 16-byte aligned rows: the scaled tile goes through LDS ([token][channel], 16-byte
+    // chunks xor-swizzled by the token's low four bits) and leaves as 16-byte stores, four full 256-byte
+    // rows per wave instruction. Written directly, each store would cover 16 bytes in each of 32 rows.
+    if (MODE == 1 && (N % 8) == 0 && (reinterpret_cast<uintptr_t>(c) % 16) == 0) {
+        constexpr int ROWB = BN * 2;  // bytes of one staged token row
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int ml = wm * WM + j * 32 + frow;
+            const int64_t m = m0 + ml;
+            const float sxm = m < M ? sa[m] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn * WN + i * 32 + 8 * g + 4 * fhalf;
+                    const int64_t nb = n0 + nl;
+                    float f[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float swn = (nb + r < N) ? sb[nb + r] : 0.0f;
+                        f[r] = (float)acc[i][j][4 * g + r] * (sxm * swn);
+                    }
+                    const int chunk = (nl * 2 / 16) ^ (ml & 15);
+                    *reinterpret_cast<uint2 *>(smem + ml * ROWB + chunk * 16 + (nl * 2) % 16) =
+                        make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+                }
+        }
+        __syncthreads();
+        constexpr int CHUNKS = BM * ROWB / 16;  // 16-byte chunks of the tile
+        uint16_t *y = static_cast<uint16_t *>(c);
+#pragma unroll
+        for (int q = tid; q < CHUNKS; q += NT) {
+            const int ml = q / (ROWB / 16), cl = q % (ROWB / 16);
+            const int64_t m = m0 + ml, nb = n0 + cl * 8;
+            if (m < M && nb < N) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(smem + ml * ROWB + ((cl ^ (ml & 15)) * 16));
+                *reinterpret_cast<uint4 *>(y + m * N + nb) = v;  // N % 8 == 0: a chunk never crosses N
+            }
+        }
+        return;
+    }
     const bool vec_ok = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(c) % (MODE == 1 ? 8 : 16)) == 0;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {

@@ -328,6 +328,24 @@ def test_w8a8_small_fp32_out(gpu_lib, mnk):
     assert torch.equal(y, y2)
 
 
+@pytest.mark.parametrize("mnk", [(130, 200, 512), (77, 196, 96), (256, 264, 128)])
+def test_w8a8_small_bf16_out(gpu_lib, mnk):
+    """bf16 epilogue on ragged tiles: N % 8 == 0 takes the LDS-staged store path, N % 8 != 0 the direct one."""
+    m, n, k = mnk
+    announce("w8a8 small bf16 %s" % (mnk,))
+    d = W.w8a8(m=m, n=n, k=k)
+    r = oracle.w8a8(d["x"], d["w"], 0.5)
+    xg, wg = to_gpu_bf16(d["x"]), to_gpu_bf16(d["w"])
+    s = gpu_lib.smooth(xg, wg, 0.5)
+    w_q, s_w, _ = gpu_lib.quantize(wg, 8, True, 1, 0, s, 2)
+    y, x_q, s_x = gpu_lib.qlinear_w8a8(xg, s, w_q, s_w, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(x_q.cpu().numpy(), r["q_x"])
+    assert np.array_equal(w_q.cpu().numpy(), r["q_w"])
+    err = normwise(to_f64(y), r["y"])
+    assert err <= TOL_BF16, err
+
+
 # --------------------------------------------------------------------------- determinism
 
 def test_reruns_are_bit_identical(gpu_lib):
