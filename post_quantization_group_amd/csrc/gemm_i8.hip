@@ -8,8 +8,10 @@
 // Instruction. v_mfma_i32_32x32x32_i8 (32x32 output, 32 deep) sustains about twice the int8 rate of the
 // 16x16x64 form on gfx950, so it is the building block. The weight tile is the MFMA "A" operand and the
 // activation tile "B": lane l holds output column m = l % 32 and, in accumulator register r, output row
-// n = 8 (r / 4) + 4 (l / 32) + r % 4, i.e. four consecutive output channels per group of four registers;
-// the epilogue writes them as one 16-byte (int32) or 8-byte (bf16) store.
+// n = 8 (r / 4) + 4 (l / 32) + r % 4, i.e. four consecutive output channels per group of four registers.
+// The bf16 epilogue (when output rows are 16-byte aligned) stages the scaled tile in LDS and writes it back
+// as 16-byte stores along output rows; otherwise each group of four registers is one 16-byte (int32 /
+// fp32) or 8-byte (bf16) store.
 // Tiling.
 //   block: BN (n) x BM (m) output tile, split into waves of WN x WM; K step of BK bytes (BK / 32 MFMA
 //          depths; 64 or 128).
