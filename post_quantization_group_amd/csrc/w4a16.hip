@@ -508,6 +508,220 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__
     }
 }
 
+// ------------------------------------------------------------------ matrix-core variant, g = 128, M <= 32
+//
+// v_mfma_f32_32x32x16_bf16 (32 tokens x 32 rows x 16 codes; twice the rate of the 16x16x32 form on
+// gfx950). Lane l holds A (activations) for token l % 32 and B (dequantized weights) for row l % 32, codes
+// 8 (l / 32) .. + 8 of the 16; D holds row l % 32 at tokens 8 (r / 4) + 4 (l / 32) + r % 4.
+//   * Loading operands straight into that layout makes every lane of a group of four read a different row
+//     (or token), i.e. four cache lines per quad; the L1 then saturates on tag lookups long before HBM
+//     does. So each wave stages a group (128 codes) through a private LDS region instead: its global loads
+//     read whole 64-byte row pieces (one line per quad), are written to LDS with an XOR swizzle (no bank
+//     conflicts), and read back in operand order. LDS operations of one wave execute in order, so no
+//     barrier is needed.
+//   * Lane h of MFMA t works on codes 64 h + 8 t .. + 8 of the group; the activations are re-paired as
+//     (x_j, x_{j+4}) once, when they are written to LDS, to match the nibble-pair dequantization.
+//   * One more MFMA per group against a B of ones gives sum_k x for the lane's tokens, and
+//     acc += s * (D - (128 + off) * xsum).
+//   * Scales (and zero points) of four groups come with one load; they go through a buffer resource, so the
+//     read past the last row's groups returns zero instead of touching memory.
+//   * The next group's global loads are issued right after the current group's LDS stores, so they are in
+//     flight during its MFMAs. S waves of a block split K and are combined through LDS (fixed order).
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma_bf16_32(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kStageMaxWaves = 8;
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format, no swizzle
+
+// XI activation load instructions of 4 tokens each: M <= 4 XI.
+template <int XI, bool SYM, bool OUT_BF16>
+__global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
+    const uint16_t *__restrict__ x, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ w,
+    const float *__restrict__ scales, const uint8_t *__restrict__ zeros, void *__restrict__ y)
+{
+    constexpr int kRegion = 2048 + XI * 1024;  // 32 rows x 64 B of codes, 4 XI tokens x 256 B
+    constexpr int kTokens = 4 * XI;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kStageMaxWaves * kRegion];
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int S = blockDim.x / kWave;
+    const int col = lane % 32, h = lane / 32;
+    const int64_t n0 = (int64_t)blockIdx.x * 32;
+    const int groups = (int)(K / 128);
+    const int g_begin = groups * wv / S, g_end = groups * (wv + 1) / S;
+    const int ng = g_end - g_begin;
+    const int g_last = g_end > g_begin ? g_end - 1 : g_begin;
+    const uint32_t mask = vreg_const(kNibbleMask);
+    const uint32_t magic = vreg_const(SYM ? (kMagic128 ^ kSignFlip128) : kMagic128);
+    const bf16x8_t ones = as_bf16x8(kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair);
+    uint8_t *const wl = lds + wv * kRegion;  // [32 rows][4 pieces of 16 B], piece ^= (row / 4) % 4
+    uint8_t *const xl = wl + 2048;           // [kTokens][16 pieces of 16 B], piece ^= token % 16
+
+    // global -> LDS: weight instruction I covers rows 16 I + lane / 4 (piece lane % 4), activation
+    // instruction I tokens 4 I + lane / 16 (piece lane % 16); tokens past M repeat token M - 1
+    const uint8_t *wsrc[2];
+    int wdst[2];
+#pragma unroll
+    for (int I = 0; I < 2; ++I) {
+        const int r = 16 * I + lane / 4, e = lane % 4;
+        wsrc[I] = w + std::min<int64_t>(n0 + r, N - 1) * (K / 2) + 16 * e;
+        wdst[I] = r * 64 + 16 * (e ^ ((r >> 2) & 3));
+    }
+    const uint16_t *xsrc[XI];
+    int xdst[XI];
+#pragma unroll
+    for (int I = 0; I < XI; ++I) {
+        const int t = 4 * I + lane / 16, p = lane % 16;
+        xsrc[I] = x + std::min<int64_t>(t, M - 1) * K + 8 * p;
+        xdst[I] = t * 256 + 16 * (p ^ (t & 15));
+    }
+    // LDS -> operands: B lane (j, h) reads pieces 2h, 2h+1 of row j; A lane (i, h) reads piece 8h + t of
+    // token i (tokens past the staged ones alias staged rows; their outputs are never stored)
+    int brd[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        brd[q] = col * 64 + 16 * ((2 * h + q) ^ ((col >> 2) & 3));
+    const int ti = col & (kTokens - 1);
+    const int64_t row = std::min<int64_t>(n0 + col, N - 1);
+    const __amdgpu_buffer_rsrc_t srs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)scales, (short)0, (int)(N * groups * 4), kRawBufferWord3);
+    const uint32_t soff = (uint32_t)(row * groups * 4);
+    const uint32_t ztotal = SYM ? 0u : (uint32_t)(N * groups);  // zero-point bytes (>= 4 when asymmetric)
+    const __amdgpu_buffer_rsrc_t zrs =  // unused (null, empty) when symmetric
+        __builtin_amdgcn_make_buffer_rsrc((void *)zeros, (short)0, (int)ztotal, kRawBufferWord3);
+    const uint32_t zoff = (uint32_t)(row * groups);
+
+    u32x4_t wr[2], xr[XI];  // vector types, so that their LDS stores stay plain vector stores
+    auto gload = [&](int i) __attribute__((always_inline)) {
+        const int g = min(g_begin + i, g_last);
+#pragma unroll
+        for (int I = 0; I < 2; ++I)
+            wr[I] = *reinterpret_cast<const u32x4_t *>(wsrc[I] + g * 64);
+#pragma unroll
+        for (int I = 0; I < XI; ++I)
+            xr[I] = *reinterpret_cast<const u32x4_t *>(xsrc[I] + g * 128);
+    };
+    // metadata of groups g_begin + i .. + 3: scales, and zero points as four bytes of one word
+    struct Meta {
+        u32x4_t s;
+        uint32_t z;
+    };
+    auto mload = [&](Meta &md, int i) __attribute__((always_inline)) {
+        md.s = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(srs, soff + 4 * (g_begin + i), 0, 0));
+        if (!SYM) {
+            // a dword that crosses the end of the buffer reads as 0 as a whole, so the 4-byte window is
+            // clamped to end inside the array (it holds at least 4 bytes) and shifted down afterwards
+            const uint32_t zb = zoff + (uint32_t)(g_begin + i);
+            const uint32_t zc = min(zb, ztotal - 4u);
+            md.z = __builtin_amdgcn_raw_buffer_load_b32(zrs, zc, 0, 0) >> (8u * (zb - zc));
+        }
+    };
+
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        acc[r] = 0.0f;
+
+    auto step = [&](int i, const Meta &md, int sj) __attribute__((always_inline)) {
+#pragma unroll
+        for (int I = 0; I < 2; ++I)
+            *reinterpret_cast<u32x4_t *>(wl + wdst[I]) = wr[I];
+#pragma unroll
+        for (int I = 0; I < XI; ++I) {
+            const u32x4_t v = xr[I];
+            *reinterpret_cast<u32x4_t *>(xl + xdst[I]) =
+                u32x4_t{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                        __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+        }
+        gload(i + 1);  // the LDS stores above have read these registers
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 b[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            b[q] = *reinterpret_cast<const uint4 *>(wl + brd[q]);
+        f32x16_t xs, d;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            xs[r] = 0.0f;
+            d[r] = 0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                               xl + ti * 256 + 16 * ((8 * h + t) ^ (ti & 15))));
+            xs = mfma_bf16_32(a, ones, xs);
+            const uint4 wq = b[t / 4];
+            const uint32_t wd = (t % 4 == 0) ? wq.x : (t % 4 == 1) ? wq.y : (t % 4 == 2) ? wq.z : wq.w;
+            const bf16x8_t bw = as_bf16x8(pair_bits(wd, mask, magic), pair_bits(wd >> 4, mask, magic),
+                                          pair_bits(wd >> 8, mask, magic), pair_bits(wd >> 12, mask, magic));
+            d = mfma_bf16_32(a, bw, d);
+        }
+        // the element goes through a scalar first: a bit_cast of a vector-element expression reads element
+        // 0 with this compiler
+        const uint32_t sbits = md.s[sj];
+        const float sc = __uint_as_float(sbits);
+        const float off = SYM ? 8.0f : (float)((md.z >> (8 * sj)) & 0xFFu);
+        const float cf = -(128.0f + off);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[r], d[r]), acc[r]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    Meta cur, nxt;
+    gload(0);
+    mload(cur, 0);
+    int i = 0;
+    for (; i + 4 <= ng; i += 4) {
+        mload(nxt, i + 4);
+        step(i, cur, 0);
+        step(i + 1, cur, 1);
+        step(i + 2, cur, 2);
+        step(i + 3, cur, 3);
+        cur = nxt;
+    }
+    if (i < ng)
+        step(i, cur, 0);
+    if (i + 1 < ng)
+        step(i + 1, cur, 1);
+    if (i + 2 < ng)
+        step(i + 2, cur, 2);
+
+    // combine the S K-slices: halving tree over the staging area, fixed order
+    float *red = reinterpret_cast<float *>(lds);  // [S / 2][16][64]
+    for (int half = S / 2; half >= 1; half /= 2) {
+        __syncthreads();
+        if (wv >= half && wv < 2 * half)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                red[((wv - half) * 16 + r) * kWave + lane] = acc[r];
+        __syncthreads();
+        if (wv < half)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[r] += red[(wv * 16 + r) * kWave + lane];
+    }
+    if (wv > 0)
+        return;
+    const int64_t n = n0 + col;
+    if (n >= N)
+        return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t m = 8 * (r / 4) + 4 * h + r % 4;
+        if (m < M) {
+            if (OUT_BF16)
+                reinterpret_cast<uint16_t *>(y)[m * N + n] = (uint16_t)f32_to_bf16_bits(acc[r]);
+            else
+                reinterpret_cast<float *>(y)[m * N + n] = acc[r];
+        }
+    }
+}
+
 namespace {
 
 // Waves per block: split K until the grid holds about `target_waves` waves, keeping at least one full
@@ -566,6 +780,34 @@ hipError_t mfma_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y
     return hipGetLastError();
 }
 
+// Staged matrix-core launch (g = 128, M <= 4 XI): 32 rows per block, waves split K until the grid holds
+// about 2048 waves (wide layers keep 4 waves per block, narrow ones up to 8), at least two groups each.
+template <int XI, bool SYM>
+hipError_t lds_launch(const W4A16Args &a, void *y, hipStream_t st)
+{
+    const int64_t blocks = (a.N + 31) / 32;
+    const int64_t groups = a.K / 128;
+    int S = 1;
+    while (2 * S <= kStageMaxWaves && blocks * S < 2048 && groups / (2 * S) >= 2)
+        S *= 2;
+    const dim3 grid((unsigned)blocks), block(kWave * S);
+    if (a.y_bf16)
+        k_w4a16_mfma_lds<XI, SYM, true><<<grid, block, 0, st>>>(a.x, a.M, a.N, a.K, a.w, a.scales, a.zeros, y);
+    else
+        k_w4a16_mfma_lds<XI, SYM, false><<<grid, block, 0, st>>>(a.x, a.M, a.N, a.K, a.w, a.scales, a.zeros, y);
+    return hipGetLastError();
+}
+
+template <bool SYM>
+hipError_t lds_m(const W4A16Args &a, hipStream_t st)
+{
+    if (a.M <= 8)
+        return lds_launch<2, SYM>(a, a.y, st);
+    if (a.M <= 16)
+        return lds_launch<4, SYM>(a, a.y, st);
+    return lds_launch<8, SYM>(a, a.y, st);
+}
+
 template <int G, bool SYM>
 hipError_t mfma_m(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
 {
@@ -610,6 +852,11 @@ constexpr int64_t kMfmaMinTokens = 5;
 hipError_t launch_w4a16(const W4A16Args &a, hipStream_t st)
 {
     const size_t ysz = a.y_bf16 ? 2 : 4;
+    // the staged kernel addresses scales through 32-bit buffer offsets
+    // (and, with zero points, reads them four bytes at a time from an array of at least four)
+    const bool staged_fits = a.N * (a.K / 128) * 4 < ((int64_t)1 << 31) && (a.symmetric || a.N * (a.K / 128) >= 4);
+    if (a.M >= kMfmaMinTokens && a.M <= 32 && a.group_size == 128 && staged_fits)
+        return a.symmetric ? lds_m<true>(a, st) : lds_m<false>(a, st);
     if (a.M >= kMfmaMinTokens) {
         for (int64_t m0 = 0; m0 < a.M; m0 += 64) {
             const int64_t mc = std::min<int64_t>(64, a.M - m0);

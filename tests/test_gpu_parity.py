@@ -207,6 +207,25 @@ def test_w4a16_ragged_fp32(gpu_lib, shape, sym):
     assert err <= TOL_F32, err
 
 
+# g = 128 and 5 <= M <= 32 take the LDS-staged matrix-core kernel: ragged N (partial 32-row tile), group
+# counts that are not a multiple of 4 (partial scale load) nor of the K split, one group only, and M = 33
+# (the general matrix-core kernel)
+@pytest.mark.parametrize("shape", [(5, 130, 640, 128), (13, 33, 1152, 128), (20, 1, 384, 128),
+                                   (32, 257, 2688, 128), (9, 64, 128, 128), (32, 96, 8192, 128),
+                                   (33, 70, 512, 128)])
+@pytest.mark.parametrize("sym", [True, False])
+def test_w4a16_staged_ragged_fp32(gpu_lib, shape, sym):
+    m, n, k, gs = shape
+    announce("w4a16 staged %s sym=%s" % (shape, sym))
+    rng = np.random.default_rng(n * 11 + k + m)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = W.bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    y, y_ref, gq, oq = w4a16_case(gpu_lib, w, False, x, sym, gs, torch.float32)
+    assert_quant_equal(gq, oq, 4, sym)
+    err = normwise(y, y_ref)
+    assert err <= TOL_F32, err
+
+
 @pytest.mark.parametrize("proj", range(len(W.L70B_PROJ)))
 def test_w4a16_l70b_sampled(gpu_lib, proj):
     """Full-size 70B projection: GPU quantizes all of it and runs the GEMV at M=1, 8, 32; the oracle checks
