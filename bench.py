@@ -8,13 +8,14 @@ One step is one pass over every stage of the quantized linear layer on synthetic
   dequantize the packed layer back to bf16                                          (standalone dequantize)
   w4a16_m1   the seven projections at batch 1 (decode)       <- the headline weight-stream GB/s
   w4a16_m32  the seven projections at batch 32
+  w4a16_m8   the seven projections at batch 8
   smooth     SmoothQuant factor, alpha = 0.5, X 2048x4096 (41 channels x50), W 11008x4096
   wquant     W' = W diag(s) -> INT8 per output channel
   w8a8       dynamic per-token INT8 activations + INT8 GEMM + s_x*s_w epilogue, 2048x11008x4096
                                                              <- the INT8 GEMM TOPS
 The packed layer exists twice. A step re-quantizes into one copy, runs the dequantize and the W8A8 layer,
-then the batch-32 pass over the other copy (a clean 455 MB read that also drains the dirty lines the
-1.7 GB dequantize left in the 256 MB last-level cache), and last the batch-1 decode pass over the copy
+then the batch-32 and batch-8 passes over the other copy (clean 455 MB reads that also drain the dirty lines
+the 1.7 GB dequantize left in the 256 MB last-level cache), and last the batch-1 decode pass over the copy
 quantized at the start of the step: cold weights streamed from HBM behind a clean cache, as in a decode
 loop where each layer's weight stream follows the previous one.
 
@@ -110,6 +111,7 @@ def main():
             pqg.quantize(w, 4, True, pqg.GROUP, 128, out=(packed[c], scales[c], None))
         projs.append(dict(name=name, n=n, k=k, w=w, x=x, packed=packed, scales=scales,
                           y1=torch.empty((1, n), dtype=torch.bfloat16, device=dev),
+                          y8=torch.empty((8, n), dtype=torch.bfloat16, device=dev),
                           y32=torch.empty((32, n), dtype=torch.bfloat16, device=dev)))
     deq = torch.empty(max(p["n"] * p["k"] for p in projs), dtype=torch.bfloat16, device=dev)
     d8 = W.w8a8()
@@ -128,12 +130,13 @@ def main():
     gemv_bytes_total = gemv_bytes + sum(p["k"] * 2 + p["n"] * 2 for p in projs)  # + x and y
     w8a8_ops = 2.0 * M8 * N8 * K8
 
-    parts = ["quantize", "dequantize", "smooth", "wquant", "w8a8_actquant", "w8a8_gemm", "w4a16_m32", "w4a16_m1"]
+    parts = ["quantize", "dequantize", "smooth", "wquant", "w8a8_actquant", "w8a8_gemm", "w4a16_m32", "w4a16_m8",
+             "w4a16_m1"]
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def run_step(i, rec):
         # Offline stages and the W8A8 layer first; this step re-quantizes the layer into copy c. Then the
-        # batch-32 pass streams copy o (455 MB of clean reads, which also drains the dirty lines the
+        # batch-32 and batch-8 passes stream copy o (clean reads, which also drain the dirty lines the
         # dequantize left in the last-level cache), and the batch-1 decode pass streams copy c, last touched
         # more than 2 GB of traffic earlier: cold weights and a clean cache, as in a decode loop.
         c, o = i % 2, 1 - i % 2
@@ -174,6 +177,11 @@ def main():
         if rec:
             marks["w4a16_m32"] = ev()
             marks["w4a16_m32"].record(stream)
+        for p in projs:  # S7: batch 8, same copy
+            pqg.qlinear_w4a16(p["x"][:8], p["packed"][o], p["scales"][o], None, 128, True, out=p["y8"])
+        if rec:
+            marks["w4a16_m8"] = ev()
+            marks["w4a16_m8"].record(stream)
         # Per-launch events sit between the seven launches only on odd steps: they break back-to-back
         # dispatch, so the sequence time (value) comes from the even steps and the per-kernel durations
         # (roofline) from the odd ones.
@@ -270,6 +278,9 @@ def main():
         },
         "per_projection_event_us": {p["name"]: round(float(t) * 1e3, 2) for p, t in zip(projs, launch_ms)},
         "stage_ms": {k: round(v, 4) for k, v in part_ms.items()},
+        # the batched passes over the same weight stream (packed codes + scales), as weight GB/s
+        "w4a16_batched_weight_gbs": {m: round(gemv_bytes / (part_ms["w4a16_m%d" % m] * 1e-3) / 1e9, 1)
+                                     for m in (8, 32)},
         "setup_s": round(setup_s, 1),
     }
     if args.copy_calibration:
