@@ -8,8 +8,8 @@
 // consecutive columns (8 per thread, one 16-byte load per row) and a slice of kRowsPerSlice rows; it writes
 // the slice maxima to ws[slice][K]. Eight rows are loaded before they are reduced, so each lane keeps
 // eight 16-byte loads in flight.
-// k_smooth_factor: a block of four waves owns 64 columns; wave q reduces slices q, q + 4, ... of both
-// tensors, the four partial maxima meet in LDS, and the first wave evaluates the factor.
+// k_smooth_factor: a block of 256 threads owns 16 columns; thread group q reduces slices q, q + 16, ... of
+// both tensors, the sixteen partial maxima meet in LDS, and the first group evaluates the factor.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -74,36 +74,44 @@ __global__ __launch_bounds__(64) void k_colabsmax(const XT *__restrict__ x, int6
     }
 }
 
+// Maximum over slices q, q + Q, q + 2Q, ... of column j (four loads in flight).
+template <int Q>
 __device__ __forceinline__ float slices_max(const float *__restrict__ ws, int64_t slices, int64_t cols, int64_t j,
                                             int q)
 {
     float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     int64_t p = q;
-    for (; p + 12 < slices; p += 16) {
+    for (; p + 3 * Q < slices; p += 4 * Q) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            a[u] = __builtin_fmaxf(a[u], ws[(p + 4 * u) * cols + j]);
+            a[u] = __builtin_fmaxf(a[u], ws[(p + Q * u) * cols + j]);
     }
-    for (; p < slices; p += 4)
+    for (; p < slices; p += Q)
         a[0] = __builtin_fmaxf(a[0], ws[p * cols + j]);
     return __builtin_fmaxf(__builtin_fmaxf(a[0], a[1]), __builtin_fmaxf(a[2], a[3]));
 }
+
+constexpr int kFactorCols = 16;                  // columns per block
+constexpr int kFactorSplit = 256 / kFactorCols;  // slice groups per column
 
 __global__ __launch_bounds__(256) void k_smooth_factor(const float *__restrict__ wsx, int64_t px,
                                                        const float *__restrict__ wsw, int64_t pw, int64_t cols,
                                                        double alpha, float *__restrict__ s)
 {
-    __shared__ float part[2][4][64];
-    const int c = threadIdx.x % 64, q = threadIdx.x / 64;
-    const int64_t j = (int64_t)blockIdx.x * 64 + c;
+    __shared__ float part[2][kFactorSplit][kFactorCols];
+    const int c = threadIdx.x % kFactorCols, q = threadIdx.x / kFactorCols;
+    const int64_t j = (int64_t)blockIdx.x * kFactorCols + c;
     const int64_t jj = j < cols ? j : cols - 1;
-    part[0][q][c] = slices_max(wsx, px, cols, jj, q);
-    part[1][q][c] = slices_max(wsw, pw, cols, jj, q);
+    part[0][q][c] = slices_max<kFactorSplit>(wsx, px, cols, jj, q);
+    part[1][q][c] = slices_max<kFactorSplit>(wsw, pw, cols, jj, q);
     __syncthreads();
     if (q != 0 || j >= cols)
         return;
-    const float ax = __builtin_fmaxf(__builtin_fmaxf(part[0][0][c], part[0][1][c]), __builtin_fmaxf(part[0][2][c], part[0][3][c]));
-    const float aw = __builtin_fmaxf(__builtin_fmaxf(part[1][0][c], part[1][1][c]), __builtin_fmaxf(part[1][2][c], part[1][3][c]));
+    float ax = part[0][0][c], aw = part[1][0][c];
+    for (int i = 1; i < kFactorSplit; ++i) {
+        ax = __builtin_fmaxf(ax, part[0][i][c]);
+        aw = __builtin_fmaxf(aw, part[1][i][c]);
+    }
     float r;
     if (ax == 0.0f || aw == 0.0f)
         r = 1.0f;  // undefined factor: leave the channel unscaled
@@ -145,8 +153,8 @@ hipError_t launch_smooth(const SmoothArgs &a, hipStream_t st)
         k_colabsmax<float, float><<<grid, 64, 0, st>>>(static_cast<const float *>(a.x), a.tokens,
                                                        static_cast<const float *>(a.w), a.out_features,
                                                        a.in_features, wsx, wsw);
-    k_smooth_factor<<<(unsigned)((a.in_features + 63) / 64), 256, 0, st>>>(wsx, px, wsw, pw, a.in_features, a.alpha,
-                                                                         a.s);
+    k_smooth_factor<<<(unsigned)((a.in_features + kFactorCols - 1) / kFactorCols), 256, 0, st>>>(
+        wsx, px, wsw, pw, a.in_features, a.alpha, a.s);
     return hipGetLastError();
 }
 
