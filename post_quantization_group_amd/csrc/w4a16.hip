@@ -269,7 +269,8 @@ __global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__
     }
 }
 
-// ------------------------------------------------------------------ matrix-core variant (any M <= 64)
+// ------------------------------------------------------------------ matrix-core variant (M >= 5 not taken by the
+// staged kernel below: g = 32 / 64, or M > 32; up to 64 tokens per launch)
 //
 // v_mfma_f32_16x16x32_bf16 computes D[i][j] += sum_k A[i][k] B[k][j] on 16x32 / 32x16 bf16 tiles. Here
 // A is the activation tile (i = token m) and B the dequantized weight tile (j = output row n), so lane
