@@ -12,6 +12,9 @@
 // The bf16 epilogue (when output rows are 16-byte aligned) stages the scaled tile in LDS and writes it back
 // as 16-byte stores along output rows; otherwise each group of four registers is one 16-byte (int32 /
 // fp32) or 8-byte (bf16) store.
+// Two kernels share this layout. The ring kernel further down (256 x 128 tiles, operands loaded straight into
+// a three-stage LDS ring) takes K % 64 == 0 and M >= 256; the register-staged 128 x 128 kernel described
+// next takes every other shape.
 // Tiling.
 //   block: BN (n) x BM (m) output tile, split into waves of WN x WM; K step of BK bytes (BK / 32 MFMA
 //          depths; 64 or 128).
@@ -272,6 +275,216 @@ hipError_t gemm_launch(const GemmI8Args &g, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_i8(const GemmI8Args &g, hipStream_t st) { return gemm_launch<128, 128, 32, 64, 64>(g, st); }
+// ------------------------------------------------------------------ ring kernel (K % 64 == 0, M >= 256)
+//
+// 256 (m) x 128 (n) block tile, four waves of 128 (m) x 64 (n), 64-byte K steps. Operands go global -> LDS
+// with direct loads (global_load_lds_dwordx4: no registers, no LDS store instructions) into a ring of three
+// stages. At step k the block issues the loads of step k + 2, multiplies stage k, and then waits only for
+// the loads of step k + 1 (issued one step earlier) before the barrier, so a barrier never drains the loads
+// of the step after next. The three stages are separate LDS arrays, which lets the compiler see that the
+// direct loads into one stage cannot alias the fragment reads of another (it would otherwise wait for
+// every outstanding direct load before each read).
+//   * A direct load writes lane l's 16 bytes to LDS at (base + 16 l): each instruction fills 64 consecutive
+//     16-byte slots. The xor swizzle of the LDS layout is applied on the source side: slot (row, physical
+//     piece p) is filled from logical piece p ^ swizzle(row) of that row.
+//   * The larger tile halves the LDS bytes read per MFMA against 128 x 128 tiles with 32 x 64 wave tiles,
+//     and 2048 x 11008 gives 688 tiles (2.7 rounds on 256 CUs). Two blocks fit per CU (72 KB of LDS each).
+//   * bf16 output goes through the idle stages like the 128 x 128 kernel's epilogue.
+constexpr int kRingBM = 256, kRingBN = 128, kRingWM = 128, kRingWN = 64, kRingBK = 64;
+constexpr int kRingWaves = (kRingBM / kRingWM) * (kRingBN / kRingWN);
+constexpr int kRingThreads = kRingWaves * kWave;
+constexpr int kRingStage = (kRingBM + kRingBN) * kRingBK;    // bytes: [BM][64] activations, [BN][64] weights
+constexpr int kRingLoads = kRingStage / 16 / kRingThreads;    // direct loads per thread per step
+static_assert(kRingStage % (16 * kRingThreads) == 0, "each thread issues whole loads");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+// s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4] (7 = no wait), lgkmcnt
+// [11:8] (15 = no wait)
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+template <int MODE>
+__global__ __launch_bounds__(kRingThreads, 2) void k_gemm_i8_ring(const int8_t *__restrict__ a,
+                                                                 const int8_t *__restrict__ b, int64_t M,
+                                                                 int64_t N, int64_t K, const float *__restrict__ sa,
+                                                                 const float *__restrict__ sb, void *__restrict__ c,
+                                                                 int tiles)
+{
+    constexpr int BM = kRingBM, BN = kRingBN, BK = kRingBK, WM = kRingWM, WN = kRingWN;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int XBYTES = BM * BK;
+    __shared__ __attribute__((aligned(16))) int8_t s0[kRingStage];
+    __shared__ __attribute__((aligned(16))) int8_t s1[kRingStage];
+    __shared__ __attribute__((aligned(16))) int8_t s2[kRingStage];
+
+    const int per = (tiles + kXcds - 1) / kXcds;  // XCD x takes tiles [x per, (x + 1) per)
+    const int t = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+    if (t >= tiles)
+        return;
+    const int m_tiles = (int)((M + BM - 1) / BM);
+    const int64_t n0 = (int64_t)(t / m_tiles) * BN;
+    const int64_t m0 = (int64_t)(t % m_tiles) * BM;
+
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = w % (BM / WM), wn = w / (BM / WM);
+    const int fr = lane % 32, fh = lane / 32;
+
+    // direct-load sources: instruction i of wave w fills slots (i * waves + w) * 64 + lane of a stage; slot
+    // P holds row P / 4 (activation rows first, then weight rows), physical piece P % 4
+    const int8_t *src[kRingLoads];
+    int lofs[kRingLoads];
+#pragma unroll
+    for (int i = 0; i < kRingLoads; ++i) {
+        const int S0 = (i * kRingWaves + w) * kWave;
+        const int P = S0 + lane;
+        const bool isx = P < BM * 4;
+        const int q = isx ? P : P - BM * 4;
+        const int r = q >> 2;
+        const int logical = (q & 3) ^ (((r >> 2) & 1) | ((r >> 3) & 2));  // inverse of lds_off<64>'s swizzle
+        if (isx)
+            src[i] = a + std::min<int64_t>(m0 + r, M - 1) * K + 16 * logical;
+        else
+            src[i] = b + std::min<int64_t>(n0 + r, N - 1) * K + 16 * logical;
+        lofs[i] = S0 * 16;
+    }
+    const int nsteps = (int)(K / BK);
+    auto issue = [&](int8_t *stage, int k) {
+        const int64_t kk = (int64_t)(k < nsteps ? k : nsteps - 1) * BK;  // past the end: reload the last step
+#pragma unroll
+        for (int i = 0; i < kRingLoads; ++i)
+            __builtin_amdgcn_global_load_lds((global_void_t *)(src[i] + kk), (lds_void_t *)(stage + lofs[i]), 16, 0, 0);
+    };
+
+    v16i acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0;
+
+    auto multiply = [&](const int8_t *xs) {
+        const int8_t *ws = xs + XBYTES;
+#pragma unroll
+        for (int s = 0; s < BK / 32; ++s) {
+            v4i fx[TM], fw[TN];
+#pragma unroll
+            for (int j = 0; j < TM; ++j)
+                fx[j] = *reinterpret_cast<const v4i *>(xs + lds_off<64>(wm * WM + j * 32 + fr, 2 * s + fh));
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+                fw[i] = *reinterpret_cast<const v4i *>(ws + lds_off<64>(wn * WN + i * 32 + fr, 2 * s + fh));
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int j = 0; j < TM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[i], fx[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    auto step = [&](int8_t *cur, int8_t *after_next, int k) {
+        issue(after_next, k + 2);
+        multiply(cur);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kRingLoads, 0));  // step k + 1 landed, fragment reads done
+        __builtin_amdgcn_s_barrier();
+    };
+
+    issue(s0, 0);
+    issue(s1, 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kRingLoads, 15));
+    __builtin_amdgcn_s_barrier();
+    int k = 0;
+    for (; k + 3 <= nsteps; k += 3) {
+        step(s0, s2, k);
+        step(s1, s0, k + 1);
+        step(s2, s1, k + 2);
+    }
+    if (k < nsteps)
+        step(s0, s2, k);
+    if (k + 1 < nsteps)
+        step(s1, s0, k + 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no direct load may land in the stages reused below
+
+    if (MODE == 1 && (N % 8) == 0 && (reinterpret_cast<uintptr_t>(c) % 16) == 0) {
+        // bf16 tile staged as [token][channel] rows of 256 bytes over the three stages (96 rows each)
+        constexpr int ROWB = BN * 2, RPS = kRingStage / ROWB;
+        static_assert(3 * RPS >= BM, "the output tile fits in the stages");
+        auto rowp = [&](int ml) -> int8_t * {
+            return ml < RPS ? s0 + ml * ROWB : ml < 2 * RPS ? s1 + (ml - RPS) * ROWB : s2 + (ml - 2 * RPS) * ROWB;
+        };
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int ml = wm * WM + j * 32 + fr;
+            const int64_t m = m0 + ml;
+            const float sxm = m < M ? sa[m] : 0.0f;
+            int8_t *rp = rowp(ml);
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn * WN + i * 32 + 8 * g + 4 * fh;
+                    const int64_t nb = n0 + nl;
+                    float f[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float swn = (nb + r < N) ? sb[nb + r] : 0.0f;
+                        f[r] = (float)acc[i][j][4 * g + r] * (sxm * swn);
+                    }
+                    const int chunk = (nl * 2 / 16) ^ (ml & 15);
+                    *reinterpret_cast<uint2 *>(rp + chunk * 16 + (nl * 2) % 16) =
+                        make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+                }
+        }
+        __syncthreads();
+        constexpr int CPR = ROWB / 16;
+        uint16_t *y = static_cast<uint16_t *>(c);
+        for (int q = tid; q < BM * CPR; q += kRingThreads) {
+            const int ml = q / CPR, cl = q % CPR;
+            const int64_t m = m0 + ml, nb = n0 + cl * 8;
+            if (m < M && nb < N)  // N % 8 == 0: a chunk never crosses N
+                *reinterpret_cast<uint4 *>(y + m * N + nb) =
+                    *reinterpret_cast<const uint4 *>(rowp(ml) + ((cl ^ (ml & 15)) * 16));
+        }
+        return;
+    }
+    const bool vec_ok = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(c) % (MODE == 1 ? 8 : 16)) == 0;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+        const int64_t m = m0 + wm * WM + j * 32 + fr;
+        const float sxm = (MODE == 0 || m >= M) ? 0.0f : sa[m];
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                store4<MODE>(v, m, n0 + wn * WN + i * 32 + 8 * g + 4 * fh, M, N, sxm, sb, c, vec_ok);
+            }
+    }
+}
+
+hipError_t ring_launch(const GemmI8Args &g, hipStream_t st)
+{
+    const int64_t tiles = ((g.N + kRingBN - 1) / kRingBN) * ((g.M + kRingBM - 1) / kRingBM);
+    const int64_t per = (tiles + kXcds - 1) / kXcds;
+    const dim3 grid((unsigned)(per * kXcds)), block(kRingThreads);
+    if (g.sa == nullptr)
+        k_gemm_i8_ring<0><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, nullptr, nullptr, g.c, (int)tiles);
+    else if (g.c_bf16)
+        k_gemm_i8_ring<1><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, g.sa, g.sb, g.c, (int)tiles);
+    else
+        k_gemm_i8_ring<2><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, g.sa, g.sb, g.c, (int)tiles);
+    return hipGetLastError();
+}
+
+// The ring kernel needs whole 64-byte K steps and pays off once there are full 256-token tiles.
+hipError_t launch_gemm_i8(const GemmI8Args &g, hipStream_t st)
+{
+    if (g.K % kRingBK == 0 && g.M >= kRingBM)
+        return ring_launch(g, st);
+    return gemm_launch<128, 128, 32, 64, 64>(g, st);
+}
 
 }  // namespace pqg

@@ -284,8 +284,11 @@ def test_smooth_zero_channel(gpu_lib):
     assert np.array_equal(s.view(np.uint32), oracle.smooth(x, d["w"], 0.5).view(np.uint32))
 
 
+# M >= 256 with K % 64 == 0 takes the three-stage ring kernel (256 x 128 tiles): ragged M and N, one K step,
+# K = 65 steps; (255, 64, 64) is just below it
 @pytest.mark.parametrize("mnk", [(1, 1, 16), (3, 5, 32), (128, 128, 64), (129, 257, 80), (200, 1000, 4096),
-                                 (64, 11008, 4096), (2048, 130, 4096)])
+                                 (64, 11008, 4096), (2048, 130, 4096), (256, 128, 64), (257, 136, 4160),
+                                 (513, 385, 1024), (700, 1000, 192), (255, 64, 64)])
 def test_gemm_s8_bitexact(gpu_lib, mnk):
     m, n, k = mnk
     announce("gemm s8 %s" % (mnk,))
@@ -328,7 +331,7 @@ def test_w8a8_full_layer(gpu_lib):
     assert err <= TOL_BF16, err
 
 
-@pytest.mark.parametrize("mnk", [(5, 77, 96), (130, 200, 512)])
+@pytest.mark.parametrize("mnk", [(5, 77, 96), (130, 200, 512), (300, 264, 128), (513, 385, 192)])
 def test_w8a8_small_fp32_out(gpu_lib, mnk):
     m, n, k = mnk
     announce("w8a8 small %s" % (mnk,))
@@ -349,9 +352,11 @@ def test_w8a8_small_fp32_out(gpu_lib, mnk):
     assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("mnk", [(130, 200, 512), (77, 196, 96), (256, 264, 128)])
+@pytest.mark.parametrize("mnk", [(130, 200, 512), (77, 196, 96), (256, 264, 128), (513, 384, 1024),
+                                 (300, 385, 128)])
 def test_w8a8_small_bf16_out(gpu_lib, mnk):
-    """bf16 epilogue on ragged tiles: N % 8 == 0 takes the LDS-staged store path, N % 8 != 0 the direct one."""
+    """bf16 epilogue on ragged tiles: N % 8 == 0 takes the LDS-staged store path, N % 8 != 0 the direct one
+    (M >= 256: in the ring kernel)."""
     m, n, k = mnk
     announce("w8a8 small bf16 %s" % (mnk,))
     d = W.w8a8(m=m, n=n, k=k)
