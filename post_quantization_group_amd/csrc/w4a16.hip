@@ -618,7 +618,8 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
             // clamped to end inside the array (it holds at least 4 bytes) and shifted down afterwards
             const uint32_t zb = zoff + (uint32_t)(g_begin + i);
             const uint32_t zc = min(zb, ztotal - 4u);
-            md.z = __builtin_amdgcn_raw_buffer_load_b32(zrs, zc, 0, 0) >> (8u * (zb - zc));
+            // (zb - zc <= 3 for every group a step uses; the prefetch past the slice may go further)
+            md.z = __builtin_amdgcn_raw_buffer_load_b32(zrs, zc, 0, 0) >> (8u * min(zb - zc, 3u));
         }
     };
 
