@@ -509,24 +509,28 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__
     }
 }
 
-// ------------------------------------------------------------------ matrix-core variant, g = 128, M <= 32
+// ------------------------------------------------------------------ matrix-core variant, M <= 32 per launch
 //
 // v_mfma_f32_32x32x16_bf16 (32 tokens x 32 rows x 16 codes; twice the rate of the 16x16x32 form on
 // gfx950). Lane l holds A (activations) for token l % 32 and B (dequantized weights) for row l % 32, codes
 // 8 (l / 32) .. + 8 of the 16; D holds row l % 32 at tokens 8 (r / 4) + 4 (l / 32) + r % 4.
 //   * Loading operands straight into that layout makes every lane of a group of four read a different row
 //     (or token), i.e. four cache lines per quad; the L1 then saturates on tag lookups long before HBM
-//     does. So each wave stages a group (128 codes) through a private LDS region instead: its global loads
-//     read whole 64-byte row pieces (one line per quad), are written to LDS with an XOR swizzle (no bank
-//     conflicts), and read back in operand order. LDS operations of one wave execute in order, so no
-//     barrier is needed.
-//   * Lane h of MFMA t works on codes 64 h + 8 t .. + 8 of the group; the activations are re-paired as
-//     (x_j, x_{j+4}) once, when they are written to LDS, to match the nibble-pair dequantization.
-//   * One more MFMA per group against a B of ones gives sum_k x for the lane's tokens, and
-//     acc += s * (D - (128 + off) * xsum).
+//     does. So each wave stages 128 codes of its 32 rows (and the activations) at a time through a private
+//     LDS region: its global loads read whole 64-byte row pieces (one line per quad), are written to LDS
+//     with an XOR swizzle (no bank conflicts), and read back in operand order. LDS operations of one wave
+//     execute in order, so no barrier is needed.
+//   * g = 128: lane h of MFMA t works on codes 64 h + 8 t .. + 8 of the step. g = 32 / 64: every MFMA must
+//     stay inside one group, so lane h of MFMA t takes codes 16 t + 8 h .. + 8; the even and odd 4-byte
+//     words of each row go to separate halves of its LDS row, which lets each lane read its words with the
+//     same two 16-byte reads.
+//   * The activations are re-paired as (x_j, x_{j+4}) once, when they are written to LDS, to match the
+//     nibble-pair dequantization.
+//   * One more MFMA against a B of ones gives sum_k x over each group for the lane's tokens, and
+//     acc += s * (D - (128 + off) * xsum) per group.
 //   * Scales (and zero points) of four groups come with one load; they go through a buffer resource, so the
 //     read past the last row's groups returns zero instead of touching memory.
-//   * The next group's global loads are issued right after the current group's LDS stores, so they are in
+//   * The next step's global loads are issued right after the current step's LDS stores, so they are in
 //     flight during its MFMAs. S waves of a block split K and are combined through LDS (fixed order).
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -538,12 +542,15 @@ __device__ __forceinline__ f32x16_t mfma_bf16_32(bf16x8_t a, bf16x8_t b, f32x16_
 constexpr int kStageMaxWaves = 8;
 constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format, no swizzle
 
-// XI activation load instructions of 4 tokens each: M <= 4 XI.
-template <int XI, bool SYM, bool OUT_BF16>
+// XI activation load instructions of 4 tokens each: M <= 4 XI; group size G in {32, 64, 128}; K % 128 == 0.
+template <int XI, int G, bool SYM, bool OUT_BF16>
 __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
     const uint16_t *__restrict__ x, int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ w,
     const float *__restrict__ scales, const uint8_t *__restrict__ zeros, void *__restrict__ y)
 {
+    constexpr int GPS = 128 / G;   // groups per 128-code step
+    constexpr int TPG = 8 / GPS;   // MFMAs per group
+    constexpr int SPM = 4 / GPS;   // steps per metadata load (four groups)
     constexpr int kRegion = 2048 + XI * 1024;  // 32 rows x 64 B of codes, 4 XI tokens x 256 B
     constexpr int kTokens = 4 * XI;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStageMaxWaves * kRegion];
@@ -552,25 +559,34 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
     const int S = blockDim.x / kWave;
     const int col = lane % 32, h = lane / 32;
     const int64_t n0 = (int64_t)blockIdx.x * 32;
-    const int groups = (int)(K / 128);
-    const int g_begin = groups * wv / S, g_end = groups * (wv + 1) / S;
-    const int ng = g_end - g_begin;
-    const int g_last = g_end > g_begin ? g_end - 1 : g_begin;
+    const int steps = (int)(K / 128);
+    const int groups = (int)(K / G);
+    const int s_begin = steps * wv / S, s_end = steps * (wv + 1) / S;
+    const int ns = s_end - s_begin;
+    const int s_last = s_end > s_begin ? s_end - 1 : s_begin;
     const uint32_t mask = vreg_const(kNibbleMask);
     const uint32_t magic = vreg_const(SYM ? (kMagic128 ^ kSignFlip128) : kMagic128);
     const bf16x8_t ones = as_bf16x8(kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair);
-    uint8_t *const wl = lds + wv * kRegion;  // [32 rows][4 pieces of 16 B], piece ^= (row / 4) % 4
+    uint8_t *const wl = lds + wv * kRegion;  // [32 rows][4 chunks of 16 B], chunk ^= (row / 4) % 4
     uint8_t *const xl = wl + 2048;           // [kTokens][16 pieces of 16 B], piece ^= token % 16
 
     // global -> LDS: weight instruction I covers rows 16 I + lane / 4 (piece lane % 4), activation
-    // instruction I tokens 4 I + lane / 16 (piece lane % 16); tokens past M repeat token M - 1
+    // instruction I tokens 4 I + lane / 16 (piece lane % 16); tokens past M repeat token M - 1.
+    // g = 128: piece e goes to chunk e. g < 128: its even words (2 of 4) to the row's first half, chunk
+    // e / 2 + byte 8 (e % 2), its odd words to the same place in the second half.
     const uint8_t *wsrc[2];
-    int wdst[2];
+    int wdst[2][2];
 #pragma unroll
     for (int I = 0; I < 2; ++I) {
-        const int r = 16 * I + lane / 4, e = lane % 4;
+        const int r = 16 * I + lane / 4, e = lane % 4, swz = (r >> 2) & 3;
         wsrc[I] = w + std::min<int64_t>(n0 + r, N - 1) * (K / 2) + 16 * e;
-        wdst[I] = r * 64 + 16 * (e ^ ((r >> 2) & 3));
+        if (G == 128) {
+            wdst[I][0] = r * 64 + 16 * (e ^ swz);
+            wdst[I][1] = 0;
+        } else {
+            wdst[I][0] = r * 64 + 16 * ((e >> 1) ^ swz) + 8 * (e & 1);
+            wdst[I][1] = r * 64 + 16 * ((2 + (e >> 1)) ^ swz) + 8 * (e & 1);
+        }
     }
     const uint16_t *xsrc[XI];
     int xdst[XI];
@@ -580,8 +596,9 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
         xsrc[I] = x + std::min<int64_t>(t, M - 1) * K + 8 * p;
         xdst[I] = t * 256 + 16 * (p ^ (t & 15));
     }
-    // LDS -> operands: B lane (j, h) reads pieces 2h, 2h+1 of row j; A lane (i, h) reads piece 8h + t of
-    // token i (tokens past the staged ones alias staged rows; their outputs are never stored)
+    // LDS -> operands: B lane (j, h) reads chunks 2h, 2h+1 of row j; A lane (i, h) of MFMA t reads piece
+    // 8h + t (g = 128) or 2t + h (g < 128) of token i (tokens past the staged ones alias staged rows; their
+    // outputs are never stored)
     int brd[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
@@ -598,25 +615,27 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
 
     u32x4_t wr[2], xr[XI];  // vector types, so that their LDS stores stay plain vector stores
     auto gload = [&](int i) __attribute__((always_inline)) {
-        const int g = min(g_begin + i, g_last);
+        const int st = min(s_begin + i, s_last);
 #pragma unroll
         for (int I = 0; I < 2; ++I)
-            wr[I] = *reinterpret_cast<const u32x4_t *>(wsrc[I] + g * 64);
+            wr[I] = *reinterpret_cast<const u32x4_t *>(wsrc[I] + st * 64);
 #pragma unroll
         for (int I = 0; I < XI; ++I)
-            xr[I] = *reinterpret_cast<const u32x4_t *>(xsrc[I] + g * 128);
+            xr[I] = *reinterpret_cast<const u32x4_t *>(xsrc[I] + st * 128);
     };
-    // metadata of groups g_begin + i .. + 3: scales, and zero points as four bytes of one word
+    // metadata of the four groups that start with step s_begin + i: scales, and zero points as the four
+    // bytes of one word
     struct Meta {
         u32x4_t s;
         uint32_t z;
     };
     auto mload = [&](Meta &md, int i) __attribute__((always_inline)) {
-        md.s = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(srs, soff + 4 * (g_begin + i), 0, 0));
+        const uint32_t g0 = (uint32_t)((s_begin + i) * GPS);
+        md.s = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(srs, soff + 4 * g0, 0, 0));
         if (!SYM) {
             // a dword that crosses the end of the buffer reads as 0 as a whole, so the 4-byte window is
             // clamped to end inside the array (it holds at least 4 bytes) and shifted down afterwards
-            const uint32_t zb = zoff + (uint32_t)(g_begin + i);
+            const uint32_t zb = zoff + g0;
             const uint32_t zc = min(zb, ztotal - 4u);
             // (zb - zc <= 3 for every group a step uses; the prefetch past the slice may go further)
             md.z = __builtin_amdgcn_raw_buffer_load_b32(zrs, zc, 0, 0) >> (8u * min(zb - zc, 3u));
@@ -630,8 +649,14 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
 
     auto step = [&](int i, const Meta &md, int sj) __attribute__((always_inline)) {
 #pragma unroll
-        for (int I = 0; I < 2; ++I)
-            *reinterpret_cast<u32x4_t *>(wl + wdst[I]) = wr[I];
+        for (int I = 0; I < 2; ++I) {
+            if (G == 128) {
+                *reinterpret_cast<u32x4_t *>(wl + wdst[I][0]) = wr[I];
+            } else {
+                *reinterpret_cast<uint2 *>(wl + wdst[I][0]) = make_uint2(wr[I].x, wr[I].z);
+                *reinterpret_cast<uint2 *>(wl + wdst[I][1]) = make_uint2(wr[I].y, wr[I].w);
+            }
+        }
 #pragma unroll
         for (int I = 0; I < XI; ++I) {
             const u32x4_t v = xr[I];
@@ -645,32 +670,37 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
 #pragma unroll
         for (int q = 0; q < 2; ++q)
             b[q] = *reinterpret_cast<const uint4 *>(wl + brd[q]);
-        f32x16_t xs, d;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            xs[r] = 0.0f;
-            d[r] = 0.0f;
+        for (int gq = 0; gq < GPS; ++gq) {
+            f32x16_t xs, d;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                xs[r] = 0.0f;
+                d[r] = 0.0f;
+            }
+#pragma unroll
+            for (int t = gq * TPG; t < (gq + 1) * TPG; ++t) {
+                const int piece = (G == 128) ? 8 * h + t : 2 * t + h;
+                const bf16x8_t a = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const uint4 *>(xl + ti * 256 + 16 * (piece ^ (ti & 15))));
+                xs = mfma_bf16_32(a, ones, xs);
+                const uint4 wq = b[t / 4];
+                const uint32_t wd = (t % 4 == 0) ? wq.x : (t % 4 == 1) ? wq.y : (t % 4 == 2) ? wq.z : wq.w;
+                const bf16x8_t bw = as_bf16x8(pair_bits(wd, mask, magic), pair_bits(wd >> 4, mask, magic),
+                                              pair_bits(wd >> 8, mask, magic), pair_bits(wd >> 12, mask, magic));
+                d = mfma_bf16_32(a, bw, d);
+            }
+            // the element goes through a scalar first: a bit_cast of a vector-element expression reads
+            // element 0 with this compiler
+            const int mi = sj * GPS + gq;  // group within the metadata word
+            const uint32_t sbits = md.s[mi];
+            const float sc = __uint_as_float(sbits);
+            const float off = SYM ? 8.0f : (float)((md.z >> (8 * mi)) & 0xFFu);
+            const float cf = -(128.0f + off);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[r], d[r]), acc[r]);
         }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                               xl + ti * 256 + 16 * ((8 * h + t) ^ (ti & 15))));
-            xs = mfma_bf16_32(a, ones, xs);
-            const uint4 wq = b[t / 4];
-            const uint32_t wd = (t % 4 == 0) ? wq.x : (t % 4 == 1) ? wq.y : (t % 4 == 2) ? wq.z : wq.w;
-            const bf16x8_t bw = as_bf16x8(pair_bits(wd, mask, magic), pair_bits(wd >> 4, mask, magic),
-                                          pair_bits(wd >> 8, mask, magic), pair_bits(wd >> 12, mask, magic));
-            d = mfma_bf16_32(a, bw, d);
-        }
-        // the element goes through a scalar first: a bit_cast of a vector-element expression reads element
-        // 0 with this compiler
-        const uint32_t sbits = md.s[sj];
-        const float sc = __uint_as_float(sbits);
-        const float off = SYM ? 8.0f : (float)((md.z >> (8 * sj)) & 0xFFu);
-        const float cf = -(128.0f + off);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            acc[r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[r], d[r]), acc[r]);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -678,20 +708,17 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
     gload(0);
     mload(cur, 0);
     int i = 0;
-    for (; i + 4 <= ng; i += 4) {
-        mload(nxt, i + 4);
-        step(i, cur, 0);
-        step(i + 1, cur, 1);
-        step(i + 2, cur, 2);
-        step(i + 3, cur, 3);
+    for (; i + SPM <= ns; i += SPM) {
+        mload(nxt, i + SPM);
+#pragma unroll
+        for (int sj = 0; sj < SPM; ++sj)
+            step(i + sj, cur, sj);
         cur = nxt;
     }
-    if (i < ng)
-        step(i, cur, 0);
-    if (i + 1 < ng)
-        step(i + 1, cur, 1);
-    if (i + 2 < ng)
-        step(i + 2, cur, 2);
+#pragma unroll
+    for (int sj = 0; sj + 1 < SPM; ++sj)
+        if (i + sj < ns)
+            step(i + sj, cur, sj);
 
     // combine the S K-slices: halving tree over the staging area, fixed order
     float *red = reinterpret_cast<float *>(lds);  // [S / 2][16][64]
@@ -782,32 +809,47 @@ hipError_t mfma_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y
     return hipGetLastError();
 }
 
-// Staged matrix-core launch (g = 128, M <= 4 XI): 32 rows per block, waves split K until the grid holds
-// about 2048 waves (wide layers keep 4 waves per block, narrow ones up to 8), at least two groups each.
-template <int XI, bool SYM>
-hipError_t lds_launch(const W4A16Args &a, void *y, hipStream_t st)
+// Staged matrix-core launch (M <= 4 XI tokens at x, output rows at y): 32 rows per block, waves split K
+// until the grid holds about 2048 waves (wide layers keep 4 waves per block, narrow ones up to 8), at least
+// two 128-code steps each.
+template <int XI, int G, bool SYM>
+hipError_t lds_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
 {
     const int64_t blocks = (a.N + 31) / 32;
-    const int64_t groups = a.K / 128;
+    const int64_t steps = a.K / 128;
     int S = 1;
-    while (2 * S <= kStageMaxWaves && blocks * S < 2048 && groups / (2 * S) >= 2)
+    while (2 * S <= kStageMaxWaves && blocks * S < 2048 && steps / (2 * S) >= 2)
         S *= 2;
     const dim3 grid((unsigned)blocks), block(kWave * S);
     if (a.y_bf16)
-        k_w4a16_mfma_lds<XI, SYM, true><<<grid, block, 0, st>>>(a.x, a.M, a.N, a.K, a.w, a.scales, a.zeros, y);
+        k_w4a16_mfma_lds<XI, G, SYM, true><<<grid, block, 0, st>>>(x, M, a.N, a.K, a.w, a.scales, a.zeros, y);
     else
-        k_w4a16_mfma_lds<XI, SYM, false><<<grid, block, 0, st>>>(a.x, a.M, a.N, a.K, a.w, a.scales, a.zeros, y);
+        k_w4a16_mfma_lds<XI, G, SYM, false><<<grid, block, 0, st>>>(x, M, a.N, a.K, a.w, a.scales, a.zeros, y);
     return hipGetLastError();
 }
 
-template <bool SYM>
-hipError_t lds_m(const W4A16Args &a, hipStream_t st)
+template <int G, bool SYM>
+hipError_t lds_mg(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
 {
-    if (a.M <= 8)
-        return lds_launch<2, SYM>(a, a.y, st);
-    if (a.M <= 16)
-        return lds_launch<4, SYM>(a, a.y, st);
-    return lds_launch<8, SYM>(a, a.y, st);
+    if (M <= 8)
+        return lds_launch<2, G, SYM>(a, x, M, y, st);
+    if (M <= 16)
+        return lds_launch<4, G, SYM>(a, x, M, y, st);
+    return lds_launch<8, G, SYM>(a, x, M, y, st);
+}
+
+// Up to 32 tokens per launch.
+template <bool SYM>
+hipError_t lds_m(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
+{
+    switch (a.group_size) {
+    case 32:
+        return lds_mg<32, SYM>(a, x, M, y, st);
+    case 64:
+        return lds_mg<64, SYM>(a, x, M, y, st);
+    default:
+        return lds_mg<128, SYM>(a, x, M, y, st);
+    }
 }
 
 template <int G, bool SYM>
@@ -848,17 +890,30 @@ hipError_t gemv_g(const W4A16Args &a, int mt, const uint16_t *x, void *y, hipStr
 
 }  // namespace
 
-// Tokens at or above which the matrix-core kernel replaces the vector kernel.
+// Tokens at or above which the matrix-core kernels replace the vector kernel.
 constexpr int64_t kMfmaMinTokens = 5;
+// Up to this many tokens the staged kernel runs (in launches of 32 tokens, each re-reading the weights).
+constexpr int64_t kStagedMaxTokens = 64;
 
 hipError_t launch_w4a16(const W4A16Args &a, hipStream_t st)
 {
     const size_t ysz = a.y_bf16 ? 2 : 4;
-    // the staged kernel addresses scales through 32-bit buffer offsets
-    // (and, with zero points, reads them four bytes at a time from an array of at least four)
-    const bool staged_fits = a.N * (a.K / 128) * 4 < ((int64_t)1 << 31) && (a.symmetric || a.N * (a.K / 128) >= 4);
-    if (a.M >= kMfmaMinTokens && a.M <= 32 && a.group_size == 128 && staged_fits)
-        return a.symmetric ? lds_m<true>(a, st) : lds_m<false>(a, st);
+    // the staged kernel works in 128-code steps and addresses scales through 32-bit buffer offsets (and,
+    // with zero points, reads them four bytes at a time from an array of at least four)
+    const int64_t groups = a.K / a.group_size;
+    const bool staged_fits = a.K % 128 == 0 && a.N * groups * 4 < ((int64_t)1 << 31) &&
+                             (a.symmetric || a.N * groups >= 4);
+    if (a.M >= kMfmaMinTokens && a.M <= kStagedMaxTokens && staged_fits) {
+        for (int64_t m0 = 0; m0 < a.M; m0 += 32) {
+            const int64_t mc = std::min<int64_t>(32, a.M - m0);
+            const uint16_t *x = a.x + m0 * a.K;
+            void *y = static_cast<char *>(a.y) + (size_t)m0 * (size_t)a.N * ysz;
+            hipError_t e = a.symmetric ? lds_m<true>(a, x, mc, y, st) : lds_m<false>(a, x, mc, y, st);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
     if (a.M >= kMfmaMinTokens) {
         for (int64_t m0 = 0; m0 < a.M; m0 += 64) {
             const int64_t mc = std::min<int64_t>(64, a.M - m0);

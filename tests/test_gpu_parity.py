@@ -207,17 +207,19 @@ def test_w4a16_ragged_fp32(gpu_lib, shape, sym):
     assert err <= TOL_F32, err
 
 
-# g = 128 and 5 <= M <= 32 take the LDS-staged matrix-core kernel: ragged N (partial 32-row tile), group
-# counts that are not a multiple of 4 (partial scale load) nor of the K split, one group only, and M = 33
-# (the general matrix-core kernel)
-@pytest.mark.parametrize("shape", [(5, 130, 640, 128), (13, 33, 1152, 128), (20, 1, 384, 128),
-                                   (32, 257, 2688, 128), (9, 64, 128, 128), (32, 96, 8192, 128),
-                                   (33, 70, 512, 128)])
+# 5 <= M <= 64 with K % 128 == 0 takes the LDS-staged matrix-core kernel (32 tokens per launch): ragged N
+# (partial 32-row tile), group counts that are not a multiple of the four-group metadata load nor of the K
+# split, one 128-code step, M = 33 and 64 (two launches); K % 128 != 0 and M > 64 take the general one
+@pytest.mark.parametrize("shape", [(5, 130, 640), (13, 33, 1152), (20, 1, 384), (32, 257, 2688), (9, 64, 128),
+                                   (32, 96, 8192), (33, 70, 512), (64, 130, 1024), (8, 40, 160), (70, 65, 256)])
+@pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("sym", [True, False])
-def test_w4a16_staged_ragged_fp32(gpu_lib, shape, sym):
-    m, n, k, gs = shape
-    announce("w4a16 staged %s sym=%s" % (shape, sym))
-    rng = np.random.default_rng(n * 11 + k + m)
+def test_w4a16_staged_ragged_fp32(gpu_lib, shape, gs, sym):
+    m, n, k = shape
+    if k % gs:
+        pytest.skip("K not a multiple of g")
+    announce("w4a16 staged %s g=%d sym=%s" % (shape, gs, sym))
+    rng = np.random.default_rng(n * 11 + k + m + gs)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     x = W.bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
     y, y_ref, gq, oq = w4a16_case(gpu_lib, w, False, x, sym, gs, torch.float32)
