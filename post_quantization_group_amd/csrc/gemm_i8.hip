@@ -479,9 +479,233 @@ hipError_t ring_launch(const GemmI8Args &g, hipStream_t st)
     return hipGetLastError();
 }
 
-// The ring kernel needs whole 64-byte K steps and pays off once there are full 256-token tiles.
+// ------------------------------------------------------------------ wide kernel (one round of 256 x 384 tiles)
+//
+// Measured on the ring kernel: with its 256 x 128 tile a CU must bring in 384 bytes per K byte for 32K
+// multiply-adds, about 47 B/clk at the int8 matrix-core rate, and it gets 20-27 B/clk from L2 under full
+// load; the same ring with all blocks reading one L2-resident tile was hardly faster, so the limit is the
+// per-CU path (direct loads into LDS plus the fragment reads out of it), not DRAM or L2 misses.
+//   * A 256 (m) x 384 (n) tile loads 640 bytes per K byte for 96K multiply-adds (about 27 B/clk at full
+//     rate), and 2048 x 11008 becomes 8 x 29 = 232 tiles: one round on 256 CUs instead of the ring
+//     kernel's 688 tiles on 512 block slots.
+//   * One block of eight waves per CU, each wave 128 (m) x 96 (n) = 4 x 3 MFMA tiles (192 accumulator
+//     registers; four waves of 128 x 192 would need 384 and the compiler spills them).
+//   * 64-byte K steps in a three-stage direct-to-LDS ring (3 x 40 KB), loads two steps ahead, as in the
+//     ring kernel. Stages are separate LDS blocks so that the compiler can tell a direct load into one
+//     stage from the fragment reads of another.
+//   * bf16 output is staged through the stages in two halves of 128 tokens (96 KB each) and written as
+//     16-byte stores along output rows; int32 and fp32 output, and bf16 with N % 8 != 0, use store4.
+// Taken when its tiles fill between three quarters and all of the CUs in a single round; otherwise the
+// ring kernel (more, smaller tiles) balances better.
+constexpr int kWideBM = 256, kWideBN = 384, kWideWM = 128, kWideWN = 96, kWideBK = 64;
+constexpr int kWideWaves = (kWideBM / kWideWM) * (kWideBN / kWideWN);
+constexpr int kWideThreads = kWideWaves * kWave;
+constexpr int kWideStage = (kWideBM + kWideBN) * kWideBK;         // 40960 bytes
+constexpr int kWideLoads = kWideStage / 16 / kWideThreads;         // 5 direct loads per thread per step
+constexpr int kWideALoads = kWideBM * kWideBK / 16 / kWideThreads;  // the first 2 fill activation rows
+static_assert(kWideStage % (16 * kWideThreads) == 0 && (kWideBM * kWideBK) % (16 * kWideThreads) == 0,
+              "each load instruction fills whole rows of one operand");
+
+// One LDS block per (size, id): distinct objects, so the compiler keeps them apart in alias analysis.
+template <int BYTES, int ID>
+__device__ __forceinline__ int8_t *lds_block()
+{
+    __shared__ __attribute__((aligned(16))) int8_t buf[BYTES];
+    return buf;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kWideThreads, 1) void k_gemm_i8_wide(const int8_t *__restrict__ a,
+                                                                 const int8_t *__restrict__ b, int64_t M,
+                                                                 int64_t N, int64_t K, const float *__restrict__ sa,
+                                                                 const float *__restrict__ sb, void *__restrict__ c,
+                                                                 int tiles)
+{
+    constexpr int BM = kWideBM, BN = kWideBN, WM = kWideWM, WN = kWideWN, BK = kWideBK;
+    constexpr int TM = WM / 32, TN = WN / 32, PPR = BK / 16;
+    int8_t *const s0 = lds_block<kWideStage, 0>();
+    int8_t *const s1 = lds_block<kWideStage, 1>();
+    int8_t *const s2 = lds_block<kWideStage, 2>();
+
+    const int per = (tiles + kXcds - 1) / kXcds;  // XCD x takes tiles [x per, (x + 1) per)
+    const int t = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+    if (t >= tiles)
+        return;
+    const int m_tiles = (int)((M + BM - 1) / BM);
+    const int64_t n0 = (int64_t)(t / m_tiles) * BN;
+    const int64_t m0 = (int64_t)(t % m_tiles) * BM;
+
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = w % (BM / WM), wn = w / (BM / WM);
+    const int fr = lane % 32, fh = lane / 32;
+
+    // direct-load sources as 32-bit offsets from the tile's first rows: instruction i of wave w fills slots
+    // (i * waves + w) * 64 + lane; slot P holds row P / 4 (activation rows first), physical piece P % 4
+    const int8_t *abase = a + m0 * K;
+    const int8_t *bbase = b + n0 * K;
+    uint32_t off[kWideLoads];
+#pragma unroll
+    for (int i = 0; i < kWideLoads; ++i) {
+        const int P = (i * kWideWaves + w) * kWave + lane;
+        const bool isx = i < kWideALoads;
+        const int q = isx ? P : P - BM * PPR;
+        const int r = q / PPR;
+        const int logical = (q % PPR) ^ (((r >> 2) & 1) | ((r >> 3) & 2));  // inverse of lds_off<64>'s swizzle
+        const int64_t rr = isx ? std::min<int64_t>(r, M - 1 - m0) : std::min<int64_t>(r, N - 1 - n0);
+        off[i] = (uint32_t)(rr * K + 16 * logical);
+    }
+    const int nsteps = (int)(K / BK);
+    auto issue = [&](int8_t *stage, int k) __attribute__((always_inline)) {
+        const uint32_t kk = (uint32_t)(k < nsteps ? k : nsteps - 1) * BK;  // past the end: reload the last step
+#pragma unroll
+        for (int i = 0; i < kWideLoads; ++i)
+            __builtin_amdgcn_global_load_lds((global_void_t *)((i < kWideALoads ? abase : bbase) + (off[i] + kk)),
+                                             (lds_void_t *)(stage + (i * kWideWaves + w) * kWave * 16), 16, 0, 0);
+    };
+
+    v16i acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0;
+
+    auto multiply = [&](const int8_t *xs) __attribute__((always_inline)) {
+        const int8_t *ws = xs + BM * BK;
+#pragma unroll
+        for (int s = 0; s < BK / 32; ++s) {
+            v4i fx[TM];
+#pragma unroll
+            for (int j = 0; j < TM; ++j)
+                fx[j] = *reinterpret_cast<const v4i *>(xs + lds_off<64>(wm * WM + j * 32 + fr, 2 * s + fh));
+#pragma unroll
+            for (int i = 0; i < TN; ++i) {
+                const v4i fw = *reinterpret_cast<const v4i *>(ws + lds_off<64>(wn * WN + i * 32 + fr, 2 * s + fh));
+#pragma unroll
+                for (int j = 0; j < TM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw, fx[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+    auto step = [&](int8_t *cur, int8_t *after_next, int k) __attribute__((always_inline)) {
+        issue(after_next, k + 2);
+        multiply(cur);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWideLoads, 0));  // step k + 1 landed, fragment reads done
+        __builtin_amdgcn_s_barrier();
+    };
+
+    issue(s0, 0);
+    issue(s1, 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWideLoads, 15));
+    __builtin_amdgcn_s_barrier();
+    int k = 0;
+    for (; k + 3 <= nsteps; k += 3) {
+        step(s0, s2, k);
+        step(s1, s0, k + 1);
+        step(s2, s1, k + 2);
+    }
+    if (k < nsteps)
+        step(s0, s2, k);
+    if (k + 1 < nsteps)
+        step(s1, s0, k + 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no direct load may land in the stages reused below
+
+    if (MODE == 1 && (N % 8) == 0 && (reinterpret_cast<uintptr_t>(c) % 16) == 0) {
+        // two halves of 128 tokens, each staged as [token][channel] bf16 rows of 768 bytes over the stages
+        constexpr int ROWB = BN * 2, RPS = kWideStage / ROWB, CPR = ROWB / 16;
+        static_assert(3 * RPS >= BM / 2, "half an output tile fits in the stages");
+        auto rowp = [&](int ml) __attribute__((always_inline)) -> int8_t * {
+            return ml < RPS ? s0 + ml * ROWB : ml < 2 * RPS ? s1 + (ml - RPS) * ROWB : s2 + (ml - 2 * RPS) * ROWB;
+        };
+        uint16_t *y = static_cast<uint16_t *>(c);
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (wm == h) {
+#pragma unroll
+                for (int j = 0; j < TM; ++j) {
+                    const int ml = j * 32 + fr;
+                    const int64_t m = m0 + h * WM + ml;
+                    const float sxm = m < M ? sa[m] : 0.0f;
+                    int8_t *rp = rowp(ml);
+#pragma unroll
+                    for (int i = 0; i < TN; ++i)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int nl = wn * WN + i * 32 + 8 * g + 4 * fh;
+                            const int64_t nb = n0 + nl;
+                            float f[4];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float swn = (nb + r < N) ? sb[nb + r] : 0.0f;
+                                f[r] = (float)acc[i][j][4 * g + r] * (sxm * swn);
+                            }
+                            const int chunk = (nl * 2 / 16) ^ (ml & 15);  // 48 chunks per row: stays in range
+                            *reinterpret_cast<uint2 *>(rp + chunk * 16 + (nl * 2) % 16) =
+                                make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+                        }
+                }
+            }
+            __syncthreads();
+            for (int q = tid; q < WM * CPR; q += kWideThreads) {
+                const int ml = q / CPR, cl = q % CPR;
+                const int64_t m = m0 + h * WM + ml, nb = n0 + cl * 8;
+                if (m < M && nb < N)  // N % 8 == 0: a chunk never crosses N
+                    *reinterpret_cast<uint4 *>(y + m * N + nb) =
+                        *reinterpret_cast<const uint4 *>(rowp(ml) + ((cl ^ (ml & 15)) * 16));
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    const bool vec_ok = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(c) % (MODE == 1 ? 8 : 16)) == 0;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+        const int64_t m = m0 + wm * WM + j * 32 + fr;
+        const float sxm = (MODE == 0 || m >= M) ? 0.0f : sa[m];
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                store4<MODE>(v, m, n0 + wn * WN + i * 32 + 8 * g + 4 * fh, M, N, sxm, sb, c, vec_ok);
+            }
+    }
+}
+
+inline int64_t wide_tiles(const GemmI8Args &g)
+{
+    return ((g.N + kWideBN - 1) / kWideBN) * ((g.M + kWideBM - 1) / kWideBM);
+}
+
+hipError_t wide_launch(const GemmI8Args &g, hipStream_t st)
+{
+    const int64_t tiles = wide_tiles(g);
+    const int64_t per = (tiles + kXcds - 1) / kXcds;
+    const dim3 grid((unsigned)(per * kXcds)), block(kWideThreads);
+    if (g.sa == nullptr)
+        k_gemm_i8_wide<0><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, nullptr, nullptr, g.c, (int)tiles);
+    else if (g.c_bf16)
+        k_gemm_i8_wide<1><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, g.sa, g.sb, g.c, (int)tiles);
+    else
+        k_gemm_i8_wide<2><<<grid, block, 0, st>>>(g.a, g.b, g.M, g.N, g.K, g.sa, g.sb, g.c, (int)tiles);
+    return hipGetLastError();
+}
+
+// Both direct-load kernels need whole 64-byte K steps. The wide kernel is taken when its 256 x 384 tiles
+// fill at least three quarters of the CUs in one round; the ring kernel once there are full 256-token tiles.
+constexpr int kCus = 256;
+
 hipError_t launch_gemm_i8(const GemmI8Args &g, hipStream_t st)
 {
+    if (g.K % kWideBK == 0) {
+        const int64_t wt = wide_tiles(g);
+        if (wt >= kCus * 3 / 4 && wt <= kCus)
+            return wide_launch(g, st);
+    }
     if (g.K % kRingBK == 0 && g.M >= kRingBM)
         return ring_launch(g, st);
     return gemm_launch<128, 128, 32, 64, 64>(g, st);

@@ -305,6 +305,24 @@ def test_gemm_s8_bitexact(gpu_lib, mnk):
     assert np.array_equal(c.cpu().numpy().astype(np.int64), ref)
 
 
+# 256 x 384 tiles that fill 192..256 CUs in one round take the wide kernel: ragged M and N (partial last
+# tiles), one K step, three (one pass of the three-stage loop) and five (loop plus a two-step tail)
+@pytest.mark.parametrize("mnk", [(2000, 11000, 64), (1800, 10500, 192), (1537, 12288, 320), (2048, 9000, 128),
+                                 (2048, 10997, 64)])
+def test_gemm_s8_wide_bitexact(gpu_lib, mnk):
+    m, n, k = mnk
+    announce("gemm s8 wide %s" % (mnk,))
+    rng = np.random.default_rng(m + n * 7 + k)
+    a = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    b = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    a[m - 1, :] = -127
+    b[n - 1, :] = -127  # extreme accumulators in the last (partial) tiles
+    c = gpu_lib.gemm_s8s8s32(to_gpu(a), to_gpu(b))
+    torch.cuda.synchronize()
+    ref = oracle.gemm_s8(a, b)
+    assert np.array_equal(c.cpu().numpy().astype(np.int64), ref)
+
+
 def test_w8a8_full_layer(gpu_lib):
     """The whole W8A8 path at 2048x11008x4096: smoothing factor, weight codes/scales, activation codes/scales
     bit-exact; int32 accumulators bit-exact and bf16 outputs within tolerance on 96 sampled tokens."""
@@ -333,7 +351,8 @@ def test_w8a8_full_layer(gpu_lib):
     assert err <= TOL_BF16, err
 
 
-@pytest.mark.parametrize("mnk", [(5, 77, 96), (130, 200, 512), (300, 264, 128), (513, 385, 192)])
+@pytest.mark.parametrize("mnk", [(5, 77, 96), (130, 200, 512), (300, 264, 128), (513, 385, 192),
+                                 (1800, 10500, 64)])
 def test_w8a8_small_fp32_out(gpu_lib, mnk):
     m, n, k = mnk
     announce("w8a8 small %s" % (mnk,))
@@ -355,10 +374,10 @@ def test_w8a8_small_fp32_out(gpu_lib, mnk):
 
 
 @pytest.mark.parametrize("mnk", [(130, 200, 512), (77, 196, 96), (256, 264, 128), (513, 384, 1024),
-                                 (300, 385, 128)])
+                                 (300, 385, 128), (2000, 11000, 128), (1800, 10501, 64)])
 def test_w8a8_small_bf16_out(gpu_lib, mnk):
     """bf16 epilogue on ragged tiles: N % 8 == 0 takes the LDS-staged store path, N % 8 != 0 the direct one
-    (M >= 256: in the ring kernel)."""
+    (M >= 256: in the ring kernel; 2000 x 11000 and 1800 x 10501: in the wide kernel)."""
     m, n, k = mnk
     announce("w8a8 small bf16 %s" % (mnk,))
     d = W.w8a8(m=m, n=n, k=k)
