@@ -188,9 +188,12 @@ def test_w4a16_ffn7b_asym(gpu_lib, gs, m):
 
 
 # (1, 64, 6144, 128) and (3, 33, 10240, 32) give the vector kernel an odd chunk-iteration count per wave
-# (the second with a partly filled last iteration)
+# (the second with a partly filled last iteration). (1, 2053, 16384, 64), (1, 4099, 16512, 128) and
+# (1, 2051, 2080, 32) have a partial last row block at M = 1 with 8, 4 and 1 waves per row (the second also
+# a partial last iteration).
 @pytest.mark.parametrize("shape", [(1, 257, 96, 32), (3, 7, 4096, 64), (5, 130, 2080, 32), (2, 1, 32, 32),
-                                   (4, 513, 640, 128), (1, 64, 6144, 128), (3, 33, 10240, 32)])
+                                   (4, 513, 640, 128), (1, 64, 6144, 128), (3, 33, 10240, 32),
+                                   (1, 2053, 16384, 64), (1, 4099, 16512, 128), (1, 2051, 2080, 32)])
 @pytest.mark.parametrize("sym", [True, False])
 def test_w4a16_ragged_fp32(gpu_lib, shape, sym):
     """Ragged N (not a multiple of the row block), K with a partial last iteration, all M in 1..5."""
