@@ -7,6 +7,8 @@ One step is one pass over every stage of the quantized linear layer on synthetic
              INT4, g = 128, packed                                                  (range, scale, codes, pack)
   dequantize the packed layer back to bf16                                          (standalone dequantize)
   w4a16_m1   the seven projections at batch 1 (decode)       <- the headline weight-stream GB/s
+             (every third step instead: the same weights as four launches, q|k|v and gate|up stored as
+             concatenated matrices sharing their input, as serving engines store them; reported apart)
   w4a16_m32  the seven projections at batch 32
   w4a16_m8   the seven projections at batch 8
   smooth     SmoothQuant factor, alpha = 0.5, X 2048x4096 (41 channels x50), W 11008x4096
@@ -101,18 +103,34 @@ def main():
 
     t_setup = time.time()
     # ---------------------------------------------------------------- inputs (resident in HBM)
+    # Each copy of the packed layer holds q|k|v and gate|up as concatenated matrices (rows of one group are
+    # independent, so the per-projection tensors are row views of them and quantize into them unchanged).
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+    fused = []
+    for g in groups:
+        n_sum, k = sum(W.L70B_PROJ[i][1] for i in g), W.L70B_PROJ[g[0]][2]
+        fused.append(dict(members=g, n=n_sum, k=k,
+                          packed=[torch.empty((n_sum, k // 2), dtype=torch.uint8, device=dev) for _ in range(2)],
+                          scales=[torch.empty(n_sum * k // 128, dtype=torch.float32, device=dev) for _ in range(2)],
+                          y1=torch.empty((1, n_sum), dtype=torch.bfloat16, device=dev)))
     projs = []
-    for i, (name, n, k) in enumerate(W.L70B_PROJ):
-        w = bf16(W.l70b_weight(i))
-        x = bf16(W.l70b_x(i, 32))
-        packed = [torch.empty((n, k // 2), dtype=torch.uint8, device=dev) for _ in range(2)]
-        scales = [torch.empty(n * k // 128, dtype=torch.float32, device=dev) for _ in range(2)]
-        for c in range(2):
-            pqg.quantize(w, 4, True, pqg.GROUP, 128, out=(packed[c], scales[c], None))
-        projs.append(dict(name=name, n=n, k=k, w=w, x=x, packed=packed, scales=scales,
-                          y1=torch.empty((1, n), dtype=torch.bfloat16, device=dev),
-                          y8=torch.empty((8, n), dtype=torch.bfloat16, device=dev),
-                          y32=torch.empty((32, n), dtype=torch.bfloat16, device=dev)))
+    for f in fused:
+        r0 = 0
+        for i in f["members"]:
+            name, n, k = W.L70B_PROJ[i]
+            w = bf16(W.l70b_weight(i))
+            x = bf16(W.l70b_x(i, 32))
+            packed = [f["packed"][c][r0:r0 + n] for c in range(2)]
+            scales = [f["scales"][c][r0 * (k // 128):(r0 + n) * (k // 128)] for c in range(2)]
+            r0 += n
+            for c in range(2):
+                pqg.quantize(w, 4, True, pqg.GROUP, 128, out=(packed[c], scales[c], None))
+            projs.append(dict(name=name, n=n, k=k, w=w, x=x, packed=packed, scales=scales,
+                              y1=torch.empty((1, n), dtype=torch.bfloat16, device=dev),
+                              y8=torch.empty((8, n), dtype=torch.bfloat16, device=dev),
+                              y32=torch.empty((32, n), dtype=torch.bfloat16, device=dev)))
+    for f in fused:
+        f["x"] = projs[f["members"][0]]["x"]  # the group's shared input
     deq = torch.empty(max(p["n"] * p["k"] for p in projs), dtype=torch.bfloat16, device=dev)
     d8 = W.w8a8()
     X8, W8 = bf16(d8["x"]), bf16(d8["w"])
@@ -182,24 +200,28 @@ def main():
         if rec:
             marks["w4a16_m8"] = ev()
             marks["w4a16_m8"].record(stream)
-        # Per-launch events sit between the seven launches only on odd steps: they break back-to-back
-        # dispatch, so the sequence time (value) comes from the even steps and the per-kernel durations
-        # (roofline) from the odd ones.
-        per_launch = rec and (i % 2 == 1)
+        # The decode pass takes one of three forms by step: the seven launches back to back (mode 0: the
+        # sequence time, value), the same with events between the launches (mode 1: per-kernel durations;
+        # the events break back-to-back dispatch), or the four launches of the concatenated layout (mode 2).
+        mode = i % 3
         gemv_ev = []
-        for p in projs:  # S6: decode GEMV, batch 1
-            if per_launch:
-                e0 = ev()
-                e0.record(stream)
-            pqg.qlinear_w4a16(p["x"][:1], p["packed"][c], p["scales"][c], None, 128, True, out=p["y1"])
-            if per_launch:
-                e1 = ev()
-                e1.record(stream)
-                gemv_ev.append((e0, e1))
+        if mode == 2:
+            for f in fused:  # S6 over the concatenated layout
+                pqg.qlinear_w4a16(f["x"][:1], f["packed"][c], f["scales"][c], None, 128, True, out=f["y1"])
+        else:
+            for p in projs:  # S6: decode GEMV, batch 1
+                if rec and mode == 1:
+                    e0 = ev()
+                    e0.record(stream)
+                pqg.qlinear_w4a16(p["x"][:1], p["packed"][c], p["scales"][c], None, 128, True, out=p["y1"])
+                if rec and mode == 1:
+                    e1 = ev()
+                    e1.record(stream)
+                    gemv_ev.append((e0, e1))
         if rec:
             marks["w4a16_m1"] = ev()
             marks["w4a16_m1"].record(stream)
-        return marks, gemv_ev
+        return marks, gemv_ev, mode
 
     for i in range(args.warmup):
         run_step(i, False)
@@ -216,15 +238,19 @@ def main():
     per_part = {k: [] for k in parts}
     gemv_launch_ms = []
     gemv_seq_ms = []
-    for marks, gemv_ev in records:
+    fused_seq_ms = []
+    for marks, gemv_ev, mode in records:
         prev = marks["start"]
         for k in parts:
-            per_part[k].append(prev.elapsed_time(marks[k]))
+            t = prev.elapsed_time(marks[k])
             prev = marks[k]
-        if gemv_ev:  # odd step: per-launch kernel durations
+            if k != "w4a16_m1" or mode == 0:
+                per_part[k].append(t)
+            elif mode == 2:
+                fused_seq_ms.append(t)
+        if mode == 1:  # per-launch kernel durations
             gemv_launch_ms.append([a.elapsed_time(b) for a, b in gemv_ev])
-        else:  # even step: the seven launches back to back, between the two surrounding marks
-            gemv_seq_ms.append(per_part["w4a16_m1"][-1])
+    gemv_seq_ms = per_part["w4a16_m1"]  # mode 0: the seven launches back to back, between the surrounding marks
     med = lambda v: float(np.median(v))  # noqa: E731
     part_ms = {k: med(v) for k, v in per_part.items()}
     launch_ms = np.median(np.array(gemv_launch_ms), axis=0)  # per projection
@@ -281,6 +307,13 @@ def main():
         # the batched passes over the same weight stream (packed codes + scales), as weight GB/s
         "w4a16_batched_weight_gbs": {m: round(gemv_bytes / (part_ms["w4a16_m%d" % m] * 1e-3) / 1e9, 1)
                                      for m in (8, 32)},
+        # the same decode weight stream as four launches (q|k|v, o, gate|up, down), each group stored as one
+        # concatenated matrix and sharing its input
+        "w4a16_m1_fused_layout": {"launches": ["+".join(W.L70B_PROJ[i][0] for i in g) for g in groups],
+                                  "value": round(gemv_bytes / (med(fused_seq_ms) * 1e-3) / 1e9, 1),
+                                  "unit": "GB/s",
+                                  "hbm_frac": round(gemv_bytes / (med(fused_seq_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "ms": round(med(fused_seq_ms), 4)},
         "setup_s": round(setup_s, 1),
     }
     if args.copy_calibration:
