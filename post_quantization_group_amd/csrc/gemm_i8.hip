@@ -12,9 +12,10 @@
 // The bf16 epilogue (when output rows are 16-byte aligned) stages the scaled tile in LDS and writes it back
 // as 16-byte stores along output rows; otherwise each group of four registers is one 16-byte (int32 /
 // fp32) or 8-byte (bf16) store.
-// Two kernels share this layout. The ring kernel further down (256 x 128 tiles, operands loaded straight into
-// a three-stage LDS ring) takes K % 64 == 0 and M >= 256; the register-staged 128 x 128 kernel described
-// next takes every other shape.
+// Three kernels share this layout. With K % 64 == 0, the wide kernel at the end (256 x 384 tiles, one block
+// of eight waves per CU) takes shapes whose tiles fill three quarters to all of the CUs in one round, and the
+// ring kernel (256 x 128 tiles) other shapes with M >= 256; both load their operands straight into a
+// three-stage LDS ring. The register-staged 128 x 128 kernel described next takes every other shape.
 // Tiling.
 //   block: BN (n) x BM (m) output tile, split into waves of WN x WM; K step of BK bytes (BK / 32 MFMA
 //          depths; 64 or 128).
