@@ -103,6 +103,29 @@ int32_t pqg_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols,
                      size_t workspace_bytes, void *stream);
 
 /*
+ * Static per-tensor quantization with calibrated parameters [P3 §11.4.5 step 5 (per-tensor INT8
+ * activations); P3 §11.1.4 (static scales fixed offline from calibration data, against dynamic ones
+ * computed at run time)]: q = clamp(round(x / scale) + zero, qmin, qmax) for every element, with (scale,
+ * zero) given by the caller, e.g. from pqg_quantize with PQG_TENSOR over calibration activations. Values
+ * beyond the calibrated range clip to qmin / qmax.
+ *   x            : [rows, cols] of x_dtype (PQG_F32 or PQG_BF16), e.g. the smoothed activations X diag(s)^-1
+ *                  as a LayerNorm with the factor folded into its gain produces them [P3 §11.4.4].
+ *   bits         : 4 or 8; symmetric: 1 -> codes in [-qmax, qmax] and zero must be 0; 0 -> codes in
+ *                  [0, 2^bits - 1] and zero in that range.
+ *   scale        : finite and > 0.
+ *   codes (out)  : as pqg_quantize (bits == 8: int8 / uint8 [rows, cols]; bits == 4: packed uint8
+ *                  [rows, cols / 2]).
+ *   row_scales (out, optional): fp32 [rows], every entry set to `scale`: the per-token scale vector that
+ *                  pqg_qlinear_w8a8 takes with x == NULL, so that the static path reuses its GEMM and
+ *                  epilogue; NULL to skip.
+ * Rounding as in pqg_quantize (round-half-to-even of the correctly rounded fp32 quotient); bit-identical to a
+ * strict-IEEE CPU evaluation. Requires cols % 32 == 0.
+ */
+int32_t pqg_quantize_static(const void *x, int32_t x_dtype, int64_t rows, int64_t cols, int32_t bits,
+                            int32_t symmetric, float scale, int32_t zero, void *codes, float *row_scales,
+                            void *stream);
+
+/*
  * Dequantization  x_hat = s * (q - z)  [P1 core formula; P2 §3; P3 §11.1.1]: one fp32 multiply per element,
  * rounded to nearest-even when out_dtype is PQG_BF16.
  *   codes / scales / zeros / bits / symmetric / granularity / group_size: as produced by pqg_quantize

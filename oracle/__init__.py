@@ -57,6 +57,10 @@ def _load():
         lib.or_quantize.argtypes = [P, I32, I64, I64, P, I32, I32, I32, I32, I32, P, P, P]
         lib.or_quantize.restype = I32
         lib.or_dequantize.argtypes = [P, P, P, I64, I64, I32, I32, P, P]
+        lib.or_quantize_static.argtypes = [P, I32, I64, I64, I32, I32, ctypes.c_float, I32, P]
+        lib.or_quantize_static.restype = I32
+        lib.or_fold_smoothing_bf16.argtypes = [P, I64, I64, P, P]
+        lib.or_fold_smoothing_bf16.restype = None
         lib.or_dequantize.restype = I32
         lib.or_pack_int4.argtypes = [P, I64, I64, P]
         lib.or_pack_int4.restype = I32
@@ -238,3 +242,43 @@ def w8a8(x_bf16, w_bf16, alpha: float = 0.5):
     y = w8a8_epilogue(acc, s_x, s_w)
     return {"s": s, "q_w": q_w.astype(np.int8), "s_w": s_w, "q_x": q_x.astype(np.int8), "s_x": s_x,
             "acc": acc, "y": y}
+
+
+def quantize_static(x, bits: int, symmetric: bool, scale: float, zero: int = 0):
+    """Static per-tensor quantization with a given (scale, zero) [P3 §11.1.4; §11.4.5 step 5]: int32 codes
+    (unpacked) of a float32 array or of bf16 bit patterns (uint16)."""
+    xa, dt = _float_input(x)
+    rows, cols = xa.shape
+    q = np.empty((rows, cols), np.int32)
+    if _load().or_quantize_static(_ptr(xa), dt, rows, cols, bits, int(symmetric), float(np.float32(scale)), int(zero),
+                                  _ptr(q)) != 0:
+        raise ValueError("bad static quantization parameters")
+    return q
+
+
+def fold_smoothing_bf16(x_bf16, s):
+    """X diag(s)^-1 rounded to bf16, as a LayerNorm with s folded into its gain emits it [P3 §11.4.4]."""
+    xa = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = xa.shape
+    out = np.empty((rows, cols), np.uint16)
+    _load().or_fold_smoothing_bf16(_ptr(xa), rows, cols, _ptr(np.ascontiguousarray(s, np.float32)), _ptr(out))
+    return out
+
+
+def w8a8_static(x_cal_bf16, x_bf16, w_bf16, alpha: float = 0.5):
+    """The pages' own SmoothQuant pipeline [P3 §11.4.5], in their order: per-channel maxima of the calibration
+    activations and of the weights give s (steps 1-2); diag(s) W to INT8 per output channel (steps 3a, 4); s
+    folded into the previous LayerNorm, so activations arrive as bf16 X diag(s)^-1 (step 3b, §11.4.4); one
+    per-tensor activation scale fixed from the calibration activations (step 5, static); at inference the
+    static codes, the exact integer GEMM and the s_x * s_w epilogue (step 6). Returns a dict of every stage."""
+    s = smooth(x_cal_bf16, w_bf16, alpha)
+    q_w, s_w, _ = quantize(w_bf16, 8, True, ROW, smooth=s, smooth_mode=SMOOTH_MUL)
+    xc_prime = fold_smoothing_bf16(x_cal_bf16, s)
+    _, s_cal, _ = quantize(xc_prime, 8, True, TENSOR)
+    s_x = np.float32(s_cal[0])
+    x_prime = fold_smoothing_bf16(x_bf16, s)
+    q_x = quantize_static(x_prime, 8, True, s_x)
+    acc = gemm_s8(q_x.astype(np.int8), q_w.astype(np.int8))
+    y = w8a8_epilogue(acc, np.full(x_prime.shape[0], s_x, np.float32), s_w)
+    return {"s": s, "q_w": q_w.astype(np.int8), "s_w": s_w, "x_prime": x_prime, "s_x": s_x,
+            "q_x": q_x.astype(np.int8), "acc": acc, "y": y}

@@ -211,6 +211,59 @@ int or_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, const fl
     return 0;
 }
 
+/*
+ * Static per-tensor quantization [P3 §11.1.4 static quantization: parameters fixed beforehand from
+ * calibration data; §11.4.5 step 5: per-tensor INT8 activations]: every element takes the same given
+ * (s, z), q = clamp(round(x / s) + z, qmin, qmax). Inputs beyond the calibrated range clip. The sum and the
+ * clamp are done in binary32 before the conversion to int, so a quotient far outside the code range cannot
+ * overflow an int.
+ * Returns 0, or -1 on bad arguments (bits, a non-positive scale, a zero point outside the code range).
+ */
+int or_quantize_static(const void *x, int x_dtype, int64_t rows, int64_t cols, int bits, int symmetric,
+                       float scale, int zero, int32_t *q)
+{
+    if (bits != 4 && bits != 8)
+        return -1;
+    if (!(scale > 0.0f))
+        return -1;
+    int qmin, qmax;
+    if (symmetric) {
+        qmax = (1 << (bits - 1)) - 1;
+        qmin = -qmax;
+        if (zero != 0)
+            return -1;
+    } else {
+        qmin = 0;
+        qmax = (1 << bits) - 1;
+        if (zero < qmin || zero > qmax)
+            return -1;
+    }
+    int64_t n = rows * cols;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float t = nearbyintf(load_elem(x, x_dtype, i) / scale) + (float)zero;
+        if (t < (float)qmin)
+            t = (float)qmin;
+        if (t > (float)qmax)
+            t = (float)qmax;
+        q[i] = (int32_t)t;
+    }
+    return 0;
+}
+
+/*
+ * The smoothed activations as a LayerNorm with the SmoothQuant factor folded into its gain would emit them
+ * [P3 §11.4.4: LayerNorm(X) diag(s)^-1 = LayerNorm'(X), gamma' = gamma / s]: x'[t, j] = bf16(x[t, j] / s[j]),
+ * one correctly rounded binary32 division, then round to nearest even bf16. (Reading: the folded LayerNorm
+ * output is the unfolded one divided by s_j and rounded once to the activation type.)
+ */
+void or_fold_smoothing_bf16(const uint16_t *x, int64_t rows, int64_t cols, const float *s, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows * cols; ++i)
+        out[i] = or_f32_to_bf16(bf16_to_f32(x[i]) / s[i % cols]);
+}
+
 /* Segment index of flat element i, for the three granularities. */
 static int64_t segment_of(int64_t i, int64_t cols, int granularity, int group_size)
 {

@@ -27,7 +27,8 @@ SMOOTH_NONE, SMOOTH_DIV, SMOOTH_MUL = 0, 1, 2
 ABI_VERSION = 1
 
 EXPORTS = [
-    "pqg_abi_version", "pqg_last_error", "pqg_quantize_workspace_bytes", "pqg_quantize", "pqg_dequantize",
+    "pqg_abi_version", "pqg_last_error", "pqg_quantize_workspace_bytes", "pqg_quantize", "pqg_quantize_static",
+    "pqg_dequantize",
     "pqg_smooth_workspace_bytes", "pqg_smooth", "pqg_qlinear_w4a16", "pqg_qlinear_w8a8", "pqg_gemm_s8s8s32",
 ]
 
@@ -58,6 +59,8 @@ def load(path: str = LIB_PATH):
     lib.pqg_quantize_workspace_bytes.argtypes = [I64, I64, I32]
     lib.pqg_quantize.restype = I32
     lib.pqg_quantize.argtypes = [P, I32, I64, I64, P, I32, I32, I32, I32, I32, P, P, P, P, SZ, P]
+    lib.pqg_quantize_static.restype = I32
+    lib.pqg_quantize_static.argtypes = [P, I32, I64, I64, I32, I32, ctypes.c_float, I32, P, P, P]
     lib.pqg_dequantize.restype = I32
     lib.pqg_dequantize.argtypes = [P, P, P, I64, I64, I32, I32, I32, I32, P, I32, P]
     lib.pqg_smooth_workspace_bytes.restype = SZ
@@ -139,6 +142,30 @@ def quantize(x: torch.Tensor, bits: int, symmetric: bool, granularity: int, grou
                             granularity, group_size, _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(ws), ws_bytes,
                             _stream(dev)))
     return codes, scales, zeros
+
+
+def quantize_static(x: torch.Tensor, bits: int, symmetric: bool, scale: float, zero: int = 0, out=None,
+                    row_scales: bool | torch.Tensor = False):
+    """pqg_quantize_static: codes of x with a fixed, calibrated per-tensor (scale, zero). Returns (codes,
+    row_scales-or-None); row_scales=True allocates the [rows] per-token copy of the scale that qlinear_w8a8
+    takes with x=None (or pass a preallocated fp32 tensor)."""
+    lib = load()
+    dev = _dev(x)
+    rows, cols = x.shape
+    if out is None:
+        if bits == 4:
+            codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        else:
+            codes = torch.empty((rows, cols), dtype=torch.int8 if symmetric else torch.uint8, device=dev)
+    else:
+        codes = out
+    if row_scales is True:
+        row_scales = torch.empty(rows, dtype=torch.float32, device=dev)
+    elif row_scales is False:
+        row_scales = None
+    _check(lib.pqg_quantize_static(_ptr(x), _float_dtype(x), rows, cols, bits, int(symmetric), float(scale), int(zero),
+                                   _ptr(codes), _ptr(row_scales), _stream(dev)))
+    return codes, row_scales
 
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, zeros, rows: int, cols: int, bits: int, symmetric: bool,

@@ -110,6 +110,35 @@ int32_t pqg_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols,
     return hip_status(pqg::launch_quantize(a, as_stream(stream)), "pqg_quantize launch");
 }
 
+int32_t pqg_quantize_static(const void *x, int32_t x_dtype, int64_t rows, int64_t cols, int32_t bits,
+                            int32_t symmetric, float scale, int32_t zero, void *codes, float *row_scales,
+                            void *stream)
+{
+    g_err[0] = 0;
+    if (rows < 0 || cols < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (!valid_float_dtype(x_dtype))
+        return fail(PQG_EINVAL, "unknown x_dtype %d", x_dtype);
+    if (bits != 4 && bits != 8)
+        return fail(PQG_EINVAL, "bits must be 4 or 8 (got %d)", bits);
+    if (!(scale > 0.0f) || !(scale <= 3.4028234663852886e38f))
+        return fail(PQG_EINVAL, "scale must be finite and > 0");
+    if (symmetric && zero != 0)
+        return fail(PQG_EINVAL, "zero must be 0 for symmetric quantization (got %d)", zero);
+    if (!symmetric && (zero < 0 || zero > (1 << bits) - 1))
+        return fail(PQG_EINVAL, "zero %d outside the %d-bit code range", zero, bits);
+    if (cols % 32 != 0)
+        return fail(PQG_EINVAL, "cols (%lld) must be a multiple of 32", (long long)cols);
+    if (rows == 0 || cols == 0)
+        return PQG_OK;
+    if (!x || !codes)
+        return fail(PQG_EINVAL, "x and codes are required");
+    if (!aligned(x, 16) || !aligned(codes, 16) || (row_scales && !aligned(row_scales, 4)))
+        return fail(PQG_EINVAL, "misaligned pointer (x, codes: 16 bytes; row_scales: 4 bytes)");
+    pqg::StaticQuantArgs a{x, x_dtype == PQG_BF16, rows, cols, bits, symmetric != 0, scale, zero, codes, row_scales};
+    return hip_status(pqg::launch_quantize_static(a, as_stream(stream)), "pqg_quantize_static launch");
+}
+
 int32_t pqg_dequantize(const void *codes, const float *scales, const uint8_t *zeros, int64_t rows, int64_t cols,
                        int32_t bits, int32_t symmetric, int32_t granularity, int32_t group_size, void *out,
                        int32_t out_dtype, void *stream)

@@ -28,6 +28,19 @@ struct QuantArgs {
     void *workspace;
 };
 
+// Static per-tensor quantization: fixed, caller-given (scale, zero); row_scales (optional) filled with scale.
+struct StaticQuantArgs {
+    const void *x;
+    bool x_bf16;
+    int64_t rows, cols;
+    int bits;
+    bool symmetric;
+    float scale;
+    int zero;
+    void *codes;
+    float *row_scales;
+};
+
 struct DequantArgs {
     const void *codes;
     const float *scales;
@@ -78,6 +91,7 @@ struct GemmI8Args {
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
 size_t quantize_workspace_bytes(int32_t granularity);
+hipError_t launch_quantize_static(const StaticQuantArgs &a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st);
 
 size_t smooth_workspace_bytes(int64_t tokens, int64_t out_features, int64_t in_features);

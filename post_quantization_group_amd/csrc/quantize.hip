@@ -228,6 +228,33 @@ __global__ __launch_bounds__(256) void k_tensor_quant(const XT *__restrict__ x, 
     }
 }
 
+// ------------------------------------------------------------------ static per-tensor
+
+// Fixed (scale, zero) from calibration ("第11章 模型量化与压缩" §11.1.4 static quantization; §11.4.5 step 5):
+// the same code step as above with the segment parameters given instead of measured. Grid-stride over
+// chunks of 8; the first `rows` threads also write the per-token copy of the scale.
+template <typename XT, int BITS, bool SYM>
+__global__ __launch_bounds__(256) void k_quant_static(const XT *__restrict__ x, int64_t n_chunks, float scale,
+                                                      float zero, void *__restrict__ codes,
+                                                      float *__restrict__ row_scales, int64_t rows)
+{
+    SegParams p;
+    p.s = scale;
+    p.r = 1.0f / scale;
+    p.z = zero;
+    p.qmax = SYM ? (float)((1 << (BITS - 1)) - 1) : (float)((1 << BITS) - 1);
+    p.qmin = SYM ? -p.qmax : 0.0f;
+    const int64_t t0 = (int64_t)blockIdx.x * 256 + threadIdx.x, stride = (int64_t)gridDim.x * 256;
+    if (row_scales)
+        for (int64_t r = t0; r < rows; r += stride)
+            row_scales[r] = scale;
+    for (int64_t c = t0; c < n_chunks; c += stride) {
+        float v[8];
+        load8<XT>(x + c * 8, v);
+        store_codes8<BITS>(v, p, codes, c * 8);
+    }
+}
+
 // ------------------------------------------------------------------ dequantize
 
 template <int BITS, bool SYM, int GRAN, bool OUT_BF16>
@@ -384,6 +411,30 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t st)
 size_t quantize_workspace_bytes(int32_t granularity)
 {
     return granularity == QG_TENSOR ? (size_t)kTensorBlocks * 3 * sizeof(float) : 0;
+}
+
+template <typename XT, int BITS, bool SYM>
+hipError_t static_launch(const StaticQuantArgs &a, hipStream_t st)
+{
+    const int64_t n_chunks = a.rows * a.cols / 8;
+    const int64_t want = std::max<int64_t>((n_chunks + 255) / 256, (a.rows + 255) / 256);
+    const int64_t blocks = std::min<int64_t>(want, 4096);  // grid-stride beyond 16 blocks per CU
+    k_quant_static<XT, BITS, SYM><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
+        static_cast<const XT *>(a.x), n_chunks, a.scale, (float)a.zero, a.codes, a.row_scales, a.rows);
+    return hipGetLastError();
+}
+
+template <typename XT>
+hipError_t static_type(const StaticQuantArgs &a, hipStream_t st)
+{
+    if (a.bits == 4)
+        return a.symmetric ? static_launch<XT, 4, true>(a, st) : static_launch<XT, 4, false>(a, st);
+    return a.symmetric ? static_launch<XT, 8, true>(a, st) : static_launch<XT, 8, false>(a, st);
+}
+
+hipError_t launch_quantize_static(const StaticQuantArgs &a, hipStream_t st)
+{
+    return a.x_bf16 ? static_type<uint16_t>(a, st) : static_type<float>(a, st);
 }
 
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st)

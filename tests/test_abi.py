@@ -73,6 +73,25 @@ def test_workspace_sizes(lib):
     assert lib.pqg_smooth_workspace_bytes(2048, 11008, 4096) >= 2 * 4096 * 4
 
 
+@pytest.mark.parametrize("kw,needle", [
+    (dict(bits=6), "bits"), (dict(scale=0.0), "scale"), (dict(scale=float("inf")), "scale"),
+    (dict(scale=float("nan")), "scale"), (dict(zero=3), "zero must be 0"), (dict(symmetric=0, bits=4, zero=16), "outside"),
+    (dict(symmetric=0, zero=-1), "outside"), (dict(cols=200), "multiple of 32"), (dict(x_dtype=5), "x_dtype"),
+    (dict(x=None), "required"), (dict(codes=MISALIGNED), "misaligned"), (dict(rows=-2), "negative"),
+])
+def test_quantize_static_rejects(lib, kw, needle):
+    a = dict(x=FAKE, x_dtype=1, rows=4, cols=256, bits=8, symmetric=1, scale=0.5, zero=0, codes=FAKE, row_scales=None)
+    a.update(kw)
+    rc = lib.pqg_quantize_static(a["x"], a["x_dtype"], a["rows"], a["cols"], a["bits"], a["symmetric"], a["scale"],
+                                 a["zero"], a["codes"], a["row_scales"], None)
+    assert rc == pqg.EINVAL
+    assert needle in lib.pqg_last_error().decode()
+
+
+def test_quantize_static_empty_is_ok(lib):
+    assert lib.pqg_quantize_static(None, 1, 0, 256, 8, 1, 0.5, 0, None, None, None) == pqg.OK
+
+
 def test_dequantize_rejects(lib):
     rc = lib.pqg_dequantize(FAKE, FAKE, None, 4, 256, 4, 0, 2, 128, FAKE, 0, None)
     assert rc == pqg.EINVAL and "zeros" in lib.pqg_last_error().decode()

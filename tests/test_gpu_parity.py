@@ -396,6 +396,100 @@ def test_w8a8_small_bf16_out(gpu_lib, mnk):
     assert err <= TOL_BF16, err
 
 
+# --------------------------------------------------------------------------- static per-tensor path
+
+# The scale is 0.7 x the calibration batch's own per-tensor scale, so that about the top 30 % of the range
+# clips; ragged row counts, one 32-column chunk, fp32 and bf16 inputs, the per-token scale fill.
+@pytest.mark.parametrize("shape", [(1, 32), (7, 96), (130, 4096), (2048, 4096)])
+@pytest.mark.parametrize("bits,sym", [(8, True), (8, False), (4, True), (4, False)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_static_bitexact(gpu_lib, shape, bits, sym, dtype):
+    rows, cols = shape
+    announce("quantize static %s bits=%d sym=%s %s" % (shape, bits, sym, dtype))
+    x = W.w8a8_calibration(m=rows, k=cols)
+    xc = W.w8a8(m=max(rows, 8), n=8, k=cols)["x"]
+    _, sc, zc = oracle.quantize(xc, bits, sym, oracle.TENSOR)
+    scale = np.float32(sc[0] * np.float32(0.7))
+    zero = 0 if sym else int(zc[0])
+    xin = x if dtype == "bf16" else W.bf16_to_f32(x)
+    xg = to_gpu_bf16(x) if dtype == "bf16" else to_gpu(W.bf16_to_f32(x))
+    codes, rs = gpu_lib.quantize_static(xg, bits, sym, float(scale), zero, row_scales=True)
+    torch.cuda.synchronize()
+    q = oracle.quantize_static(xin, bits, sym, scale, zero)
+    want = oracle_codes_bytes(q, bits, sym)
+    got = codes.cpu().numpy()
+    assert got.shape == want.shape
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+    assert np.array_equal(rs.cpu().numpy().view(np.uint32), np.full(rows, scale, np.float32).view(np.uint32))
+    qmax = (1 << (bits - 1)) - 1 if sym else (1 << bits) - 1
+    assert (q == qmax).any()  # the 0.7 x scale did make values clip
+
+
+def w8a8_static_gpu(gpu_lib, xc_prime, x_prime, xcal, w, out_dtype):
+    """The static pipeline through the library: smoothing factor from the calibration batch, weight codes of
+    diag(s) W, the per-tensor scale of the calibration X' (dynamic per-tensor quantize = calibration), static
+    codes of X', then the GEMM + epilogue with the per-token copy of that scale."""
+    wg = to_gpu_bf16(w)
+    s = gpu_lib.smooth(to_gpu_bf16(xcal), wg, 0.5)
+    w_q, s_w, _ = gpu_lib.quantize(wg, 8, True, 1, 0, s, 2)
+    _, s_cal, _ = gpu_lib.quantize(to_gpu_bf16(xc_prime), 8, True, 0)
+    s_x = float(s_cal.cpu().numpy()[0])
+    x_q, x_scales = gpu_lib.quantize_static(to_gpu_bf16(x_prime), 8, True, s_x, row_scales=True)
+    y, _, _ = gpu_lib.qlinear_w8a8(None, None, w_q, s_w, out_dtype=out_dtype, x_q=x_q, x_scales=x_scales)
+    torch.cuda.synchronize()
+    return s, w_q, s_w, np.float32(s_x), x_q, y
+
+
+@pytest.mark.parametrize("mnk", [(64, 264, 256), (300, 385, 192), (5, 77, 96)])
+def test_w8a8_static_pipeline_small(gpu_lib, mnk):
+    """The pages' SmoothQuant pipeline with static per-tensor activations ("第11章 模型量化与压缩" §11.4.5):
+    every integer and scale bit-exact, fp32 output within 1e-5 normwise."""
+    m, n, k = mnk
+    announce("w8a8 static small %s" % (mnk,))
+    d = W.w8a8(m=m, n=n, k=k)
+    xcal = W.w8a8_calibration(m=128, k=k)
+    r = oracle.w8a8_static(xcal, d["x"], d["w"], 0.5)
+    xc_prime = oracle.fold_smoothing_bf16(xcal, r["s"])
+    s, w_q, s_w, s_x, x_q, y = w8a8_static_gpu(gpu_lib, xc_prime, r["x_prime"], xcal, d["w"], torch.float32)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), r["s"].view(np.uint32))
+    assert np.array_equal(w_q.cpu().numpy(), r["q_w"])
+    assert np.array_equal(s_w.cpu().numpy().view(np.uint32), r["s_w"].view(np.uint32))
+    assert s_x.view(np.uint32) == np.float32(r["s_x"]).view(np.uint32)
+    assert np.array_equal(x_q.cpu().numpy(), r["q_x"])
+    err = normwise(to_f64(y), r["y"])
+    assert err <= TOL_F32, err
+
+
+def test_w8a8_static_full_layer(gpu_lib):
+    """2048 x 11008 x 4096 with a 512-token calibration batch: the smoothing factor, weight codes and scales,
+    the calibrated scale and all activation codes bit-exact; int32 accumulators bit-exact and bf16 outputs
+    within tolerance on 96 sampled tokens."""
+    announce("w8a8 static full layer")
+    d = W.w8a8()
+    xcal = W.w8a8_calibration()
+    so = oracle.smooth(xcal, d["w"], 0.5)
+    xc_prime = oracle.fold_smoothing_bf16(xcal, so)
+    x_prime = oracle.fold_smoothing_bf16(d["x"], so)
+    s, w_q, s_w, s_x, x_q, y = w8a8_static_gpu(gpu_lib, xc_prime, x_prime, xcal, d["w"], torch.bfloat16)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    qw, sw, _ = oracle.quantize(d["w"], 8, True, oracle.ROW, 0, so, oracle.SMOOTH_MUL)
+    assert np.array_equal(w_q.cpu().numpy(), qw.astype(np.int8))
+    assert np.array_equal(s_w.cpu().numpy().view(np.uint32), sw.view(np.uint32))
+    _, sc, _ = oracle.quantize(xc_prime, 8, True, oracle.TENSOR)
+    assert s_x.view(np.uint32) == sc[0].view(np.uint32)
+    qx = oracle.quantize_static(x_prime, 8, True, sc[0])
+    assert np.array_equal(x_q.cpu().numpy(), qx.astype(np.int8))
+    rng = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([rng.choice(2048, size=94, replace=False), [0, 2047]]))
+    acc_ref = oracle.gemm_s8(qx[toks].astype(np.int8), qw.astype(np.int8))
+    acc = gpu_lib.gemm_s8s8s32(x_q[torch.from_numpy(toks).cuda()].contiguous(), w_q)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
+    y_ref = oracle.w8a8_epilogue(acc_ref, np.full(toks.size, sc[0], np.float32), sw)
+    err = normwise(to_f64(y)[toks], y_ref)
+    assert err <= TOL_BF16, err
+
+
 # --------------------------------------------------------------------------- determinism
 
 def test_reruns_are_bit_identical(gpu_lib):

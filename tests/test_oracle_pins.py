@@ -430,3 +430,92 @@ def test_w8a8_epilogue_and_pipeline():
     y_true = xf @ wf.T
     assert np.linalg.norm(r["y"] - y_true) / np.linalg.norm(y_true) < 0.05
     assert np.abs(r["q_x"]).max() <= 127 and np.abs(r["q_w"]).max() <= 127
+
+
+# --------------------------------------------------------------------------- static per-tensor path
+
+def test_static_worked_example():
+    """Static per-tensor INT8 with the worked example's own scale 2.1 / 127 ("大模型压缩：从研究到生产的完整
+    攻略（1）", symmetric example; "第11章 模型量化与压缩" §11.1.4 static parameters): the printed codes of elements
+    0, 2, 3, 4 and the recorded reading for element 1."""
+    g = gold("worked_example_symmetric_int8.json")
+    x = f32([g["x"]])
+    s = np.float32(2.1) / np.float32(127)
+    q = oracle.quantize_static(x, 8, True, s)
+    for i in (0, 2, 3, 4):
+        assert q[0, i] == g["printed_codes"][i]
+    assert q[0].tolist() == g["expected_codes"]
+
+
+def test_static_clips_outside_calibrated_range():
+    """Values beyond the calibrated range clip to the ends of the code range (§11.1.4: static parameters
+    are fixed, so out-of-distribution inputs saturate): INT8 symmetric at scale 1/127 maps [-1, 1] onto
+    [-127, 127]; 1.5, 1e30 and -3 saturate, 0.5 is 63.5 -> 64 (tie to even), -0.25 is -31.75 -> -32."""
+    x = f32([[1.5, 1e30, -3.0, 0.5, -0.25, 1.0, -1.0, 0.0]])
+    q = oracle.quantize_static(x, 8, True, np.float32(1.0) / np.float32(127))
+    assert q[0].tolist() == [127, 127, -127, 64, -32, 127, -127, 0]
+    # INT4 asymmetric, zero 8, scale 0.5: [-4, 3.5] -> [0, 15]
+    x4 = f32([[-4.0, -4.5, 3.5, 100.0, 0.0, 0.25, 0.75, -1.0]])
+    q4 = oracle.quantize_static(x4, 4, False, np.float32(0.5), zero=8)
+    assert q4[0].tolist() == [0, 0, 15, 15, 8, 8, 10, 6]
+
+
+def test_static_asymmetric_exact_rational():
+    """Brute force in exact rational arithmetic: q = clamp(rne(x / s) + z) for random x, s, z (ties in the
+    binary32 quotient are skipped: there the exact and the rounded quotient may legitimately differ)."""
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        bits = 4 if trial % 2 else 8
+        qmax = (1 << bits) - 1
+        z = int(rng.integers(0, qmax + 1))
+        s = np.float32(rng.uniform(0.01, 0.3))
+        x = (rng.standard_normal((1, 64)) * 5).astype(np.float32)
+        q = oracle.quantize_static(x, bits, False, s, zero=z)
+        for j in range(64):
+            t = Fraction(float(x[0, j])) / Fraction(float(s))
+            fl = t - (t.numerator // t.denominator)
+            if abs(fl - Fraction(1, 2)) < Fraction(1, 1 << 18):
+                continue
+            r = round(t)  # Python rounds Fractions half to even
+            assert q[0, j] == min(max(r + z, 0), qmax)
+
+
+def test_static_matches_dynamic_when_given_its_scale():
+    """With the scale the dynamic per-tensor path measures (pinned above), the static codes are the dynamic
+    ones: the two paths share the code step and differ only in where (s, z) come from."""
+    d = workloads.w8a8(m=32, n=16, k=256)
+    for bits, sym in ((8, True), (8, False), (4, True), (4, False)):
+        q, s, z = oracle.quantize(d["x"], bits, sym, oracle.TENSOR)
+        qs = oracle.quantize_static(d["x"], bits, sym, s[0], zero=0 if sym else int(z[0]))
+        assert np.array_equal(q, qs), (bits, sym)
+
+
+def test_fold_smoothing_exact_cases():
+    """X diag(s)^-1 in bf16 ("第11章 模型量化与压缩" §11.4.4, the factor folded into LayerNorm): s = 1 returns X
+    bit for bit, and powers of two only move the exponent (exact, no rounding, away from the subnormals)."""
+    d = workloads.w8a8(m=8, n=8, k=128)
+    x = d["x"]
+    assert np.array_equal(oracle.fold_smoothing_bf16(x, np.ones(128, np.float32)), x)
+    s = np.where(np.arange(128) % 2 == 0, 4.0, 0.125).astype(np.float32)
+    xp = workloads.bf16_to_f32(oracle.fold_smoothing_bf16(x, s)).astype(np.float64)
+    assert np.array_equal(xp, workloads.bf16_to_f32(x).astype(np.float64) / s.astype(np.float64))
+
+
+def test_w8a8_static_pipeline():
+    """The pages' pipeline (§11.4.5 steps 1-6) with a static per-tensor activation scale: the scale is the
+    calibration batch's max |X'| / 127; the epilogue is acc * s_x * s_w; the result approximates X W^T; and
+    when the inference batch is the calibration batch the codes equal the dynamic per-tensor ones."""
+    d = workloads.w8a8(m=64, n=24, k=256)
+    xc = workloads.w8a8_calibration(m=128, k=256)
+    r = oracle.w8a8_static(xc, d["x"], d["w"], 0.5)
+    xcp = workloads.bf16_to_f32(oracle.fold_smoothing_bf16(xc, r["s"]))
+    assert r["s_x"] == np.float32(np.abs(xcp).max()) / np.float32(127)
+    ref = r["acc"].astype(np.float64) * np.float64(r["s_x"]) * r["s_w"].astype(np.float64)[None, :]
+    assert np.array_equal(r["y"], ref)
+    xf = workloads.bf16_to_f32(d["x"]).astype(np.float64)
+    wf = workloads.bf16_to_f32(d["w"]).astype(np.float64)
+    y_true = xf @ wf.T
+    assert np.linalg.norm(r["y"] - y_true) / np.linalg.norm(y_true) < 0.05
+    same = oracle.w8a8_static(d["x"], d["x"], d["w"], 0.5)
+    qd, _, _ = oracle.quantize(same["x_prime"], 8, True, oracle.TENSOR)
+    assert np.array_equal(same["q_x"], qd.astype(np.int8))

@@ -101,6 +101,15 @@ def w8a8(m: int = 2048, n: int = 11008, k: int = 4096):
     return {"x": bf16_bits(x), "w": bf16_bits(w), "outlier_chans": chans}
 
 
+def w8a8_calibration(m: int = 512, k: int = 4096):
+    """Calibration activations for the W8A8 layer: a second batch from the same distribution (N(0, 1), the
+    same 1 % of channels x50), drawn from its own stream. bf16."""
+    x = normal(rng(W8A8, 3), (m, k), 1.0)
+    chans = np.sort(rng(W8A8, 1).choice(k, size=int(round(0.01 * k)), replace=False))
+    x[:, chans] *= np.float32(50.0)
+    return bf16_bits(x)
+
+
 ROW_BLOCK = 512  # rows per generator stream for the large layer weights
 
 
