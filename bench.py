@@ -15,6 +15,8 @@ One step is one pass over every stage of the quantized linear layer on synthetic
   wquant     W' = W diag(s) -> INT8 per output channel
   w8a8       dynamic per-token INT8 activations + INT8 GEMM + s_x*s_w epilogue, 2048x11008x4096
                                                              <- the INT8 GEMM TOPS
+  w8a8_static_actquant  the pages' static variant: X' = X diag(s)^-1 in bf16 (as a LayerNorm with s folded
+             into its gain emits it) to INT8 with one calibrated per-tensor scale (the GEMM is the same)
 The packed layer exists twice. A step re-quantizes into one copy, runs the dequantize and the W8A8 layer,
 then the batch-32 and batch-8 passes over the other copy (clean 455 MB reads that also drain the dirty lines
 the 1.7 GB dequantize left in the 256 MB last-level cache), and last the batch-1 decode pass over the copy
@@ -141,6 +143,13 @@ def main():
     y8 = torch.empty((M8, N8), dtype=torch.bfloat16, device=dev)
     xq8 = torch.empty((M8, K8), dtype=torch.int8, device=dev)
     sx8 = torch.empty(M8, dtype=torch.float32, device=dev)
+    # static variant: X' stands in for the output of the previous LayerNorm with s folded into its gain, and
+    # the per-tensor activation scale is calibrated once on a second batch
+    Xp8 = (X8.float() / s8).to(torch.bfloat16)
+    Xcal = (bf16(W.w8a8_calibration(512, K8)).float() / s8).to(torch.bfloat16)
+    s_static = float(pqg.quantize(Xcal, 8, True, pqg.TENSOR)[1].cpu()[0])
+    xq8s = torch.empty((M8, K8), dtype=torch.int8, device=dev)
+    sx8s = torch.empty(M8, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
@@ -148,8 +157,8 @@ def main():
     gemv_bytes_total = gemv_bytes + sum(p["k"] * 2 + p["n"] * 2 for p in projs)  # + x and y
     w8a8_ops = 2.0 * M8 * N8 * K8
 
-    parts = ["quantize", "dequantize", "smooth", "wquant", "w8a8_actquant", "w8a8_gemm", "w4a16_m32", "w4a16_m8",
-             "w4a16_m1"]
+    parts = ["quantize", "dequantize", "smooth", "wquant", "w8a8_actquant", "w8a8_gemm", "w8a8_static_actquant",
+             "w4a16_m32", "w4a16_m8", "w4a16_m1"]
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def run_step(i, rec):
@@ -190,6 +199,10 @@ def main():
         if rec:
             marks["w8a8_gemm"] = ev()
             marks["w8a8_gemm"].record(stream)
+        pqg.quantize_static(Xp8, 8, True, s_static, out=xq8s, row_scales=sx8s)  # static per-tensor activations
+        if rec:
+            marks["w8a8_static_actquant"] = ev()
+            marks["w8a8_static_actquant"].record(stream)
         for p in projs:  # S7: batch 32
             pqg.qlinear_w4a16(p["x"], p["packed"][o], p["scales"][o], None, 128, True, out=p["y32"])
         if rec:
@@ -307,6 +320,13 @@ def main():
         # the batched passes over the same weight stream (packed codes + scales), as weight GB/s
         "w4a16_batched_weight_gbs": {m: round(gemv_bytes / (part_ms["w4a16_m%d" % m] * 1e-3) / 1e9, 1)
                                      for m in (8, 32)},
+        # the static per-tensor activation quantize of the W8A8 layer (bf16 X' in, INT8 codes and the per-token
+        # copy of the scale out), and the static layer = it plus the same GEMM + epilogue launch
+        "w8a8_static": {"actquant_us": round(part_ms["w8a8_static_actquant"] * 1e3, 2),
+                        "actquant_gbs": round((M8 * K8 * 3 + M8 * 4) / (part_ms["w8a8_static_actquant"] * 1e-3) / 1e9,
+                                              1),
+                        "layer_us": round((part_ms["w8a8_static_actquant"] + gemm_ms) * 1e3, 2),
+                        "calibrated_scale": s_static},
         # the same decode weight stream as four launches (q|k|v, o, gate|up, down), each group stored as one
         # concatenated matrix and sharing its input
         "w4a16_m1_fused_layout": {"launches": ["+".join(W.L70B_PROJ[i][0] for i in g) for g in groups],

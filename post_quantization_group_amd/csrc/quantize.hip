@@ -232,7 +232,10 @@ __global__ __launch_bounds__(256) void k_tensor_quant(const XT *__restrict__ x, 
 
 // Fixed (scale, zero) from calibration ("第11章 模型量化与压缩" §11.1.4 static quantization; §11.4.5 step 5):
 // the same code step as above with the segment parameters given instead of measured. Grid-stride over
-// chunks of 8; the first `rows` threads also write the per-token copy of the scale.
+// chunks of 8, kStaticUnroll chunks per thread per pass with their loads issued together (one chunk per
+// thread left the stream latency-bound); the first `rows` threads also write the per-token copy of the scale.
+constexpr int kStaticUnroll = 4;
+
 template <typename XT, int BITS, bool SYM>
 __global__ __launch_bounds__(256) void k_quant_static(const XT *__restrict__ x, int64_t n_chunks, float scale,
                                                       float zero, void *__restrict__ codes,
@@ -248,10 +251,16 @@ __global__ __launch_bounds__(256) void k_quant_static(const XT *__restrict__ x, 
     if (row_scales)
         for (int64_t r = t0; r < rows; r += stride)
             row_scales[r] = scale;
-    for (int64_t c = t0; c < n_chunks; c += stride) {
-        float v[8];
-        load8<XT>(x + c * 8, v);
-        store_codes8<BITS>(v, p, codes, c * 8);
+    for (int64_t c0 = t0; c0 < n_chunks; c0 += stride * kStaticUnroll) {
+        float v[kStaticUnroll][8];
+#pragma unroll
+        for (int u = 0; u < kStaticUnroll; ++u)
+            if (c0 + u * stride < n_chunks)
+                load8<XT>(x + (c0 + u * stride) * 8, v[u]);
+#pragma unroll
+        for (int u = 0; u < kStaticUnroll; ++u)
+            if (c0 + u * stride < n_chunks)
+                store_codes8<BITS>(v[u], p, codes, (c0 + u * stride) * 8);
     }
 }
 
@@ -417,7 +426,8 @@ template <typename XT, int BITS, bool SYM>
 hipError_t static_launch(const StaticQuantArgs &a, hipStream_t st)
 {
     const int64_t n_chunks = a.rows * a.cols / 8;
-    const int64_t want = std::max<int64_t>((n_chunks + 255) / 256, (a.rows + 255) / 256);
+    const int64_t want = std::max<int64_t>((n_chunks + 256 * kStaticUnroll - 1) / (256 * kStaticUnroll),
+                                           (a.rows + 255) / 256);
     const int64_t blocks = std::min<int64_t>(want, 4096);  // grid-stride beyond 16 blocks per CU
     k_quant_static<XT, BITS, SYM><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(
         static_cast<const XT *>(a.x), n_chunks, a.scale, (float)a.zero, a.codes, a.row_scales, a.rows);
