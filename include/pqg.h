@@ -200,6 +200,25 @@ int32_t pqg_qlinear_w8a8(const void *x, const float *smooth, const int8_t *w_q, 
 int32_t pqg_gemm_s8s8s32(const int8_t *a, const int8_t *b, int64_t M, int64_t N, int64_t K, int32_t *c,
                          void *stream);
 
+/*
+ * W4A8 linear layer  y[m, n] = s_x[m] * sum_g s_w[n, g] * sum_{k in g} q_x[m, k] * (q_w[n, k] - z[n, g])
+ * [P3 §11.4.5 (SmoothQuant combined with group-wise INT4 weights gives W4A8); P3 §11.10.2 (weight and
+ * activation quantization are independent and stack: W4A8 is AWQ-style INT4 weights with SmoothQuant INT8
+ * activations); P3 §11.1.6 (INT4 groups); P2 §11 (one scale per token)].
+ * Each group's integer sum is exact (int32); the group scales weight them in fp32; the token scale is applied
+ * last, and the result is rounded to y_dtype.
+ *   x_q      : int8 [M, K] per-token symmetric activation codes and x_scales fp32 [M], e.g. pqg_quantize with
+ *              PQG_ROW, bits 8, symmetric, PQG_SMOOTH_DIV.
+ *   w_packed : uint8 [N, K / 2] INT4 codes as pqg_quantize writes them with PQG_GROUP, bits 4 (symmetric:
+ *              two's complement; asymmetric: unsigned with zero points), e.g. on diag(s) W (PQG_SMOOTH_MUL);
+ *              w_scales fp32 [N, K / group_size]; w_zeros uint8 [N, K / group_size], NULL iff symmetric.
+ *   group_size in {32, 64, 128}. Requires K % 128 == 0.
+ *   y (out)  : [M, N] of y_dtype (PQG_F32 or PQG_BF16).
+ */
+int32_t pqg_qlinear_w4a8(const int8_t *x_q, const float *x_scales, int64_t M, int64_t N, int64_t K,
+                         const uint8_t *w_packed, const float *w_scales, const uint8_t *w_zeros, int32_t group_size,
+                         int32_t symmetric, void *y, int32_t y_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,8 @@ def _load():
         lib.or_quantize_static.restype = I32
         lib.or_fold_smoothing_bf16.argtypes = [P, I64, I64, P, P]
         lib.or_fold_smoothing_bf16.restype = None
+        lib.or_w4a8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, P]
+        lib.or_w4a8.restype = I32
         lib.or_dequantize.restype = I32
         lib.or_pack_int4.argtypes = [P, I64, I64, P]
         lib.or_pack_int4.restype = I32
@@ -282,3 +284,28 @@ def w8a8_static(x_cal_bf16, x_bf16, w_bf16, alpha: float = 0.5):
     y = w8a8_epilogue(acc, np.full(x_prime.shape[0], s_x, np.float32), s_w)
     return {"s": s, "q_w": q_w.astype(np.int8), "s_w": s_w, "x_prime": x_prime, "s_x": s_x,
             "q_x": q_x.astype(np.int8), "acc": acc, "y": y}
+
+
+def w4a8(q_x, s_x, q_w, s_w, z_w, group_size: int):
+    """W4A8 product [P3 §11.4.5, §11.10.2]: q_x int8 [M, K] with per-token s_x [M]; q_w unpacked INT4 codes
+    [N, K] with per-group s_w [N * K / g] and z_w (None for symmetric codes) -> binary64 y [M, N]."""
+    xq = np.ascontiguousarray(q_x, dtype=np.int8)
+    qw = np.ascontiguousarray(q_w, dtype=np.int32)
+    M, K = xq.shape
+    N = qw.shape[0]
+    y = np.empty((M, N), np.float64)
+    z = None if z_w is None else np.ascontiguousarray(z_w, dtype=np.uint8)
+    if _load().or_w4a8(_ptr(xq), _ptr(np.ascontiguousarray(s_x, np.float32)), M, N, K, _ptr(qw),
+                       _ptr(np.ascontiguousarray(s_w, np.float32)), _ptr(z), group_size, _ptr(y)) != 0:
+        raise ValueError("group size must divide K")
+    return y
+
+
+def w4a8_pipeline(x_bf16, w_bf16, alpha: float, group_size: int, symmetric: bool):
+    """W4A8 with SmoothQuant activations [P3 §11.4.5, §11.10.2]: the smoothing factor; diag(s) W to INT4 per
+    group; X diag(s)^-1 to INT8 per token (dynamic); the W4A8 product. Returns a dict of every stage."""
+    s = smooth(x_bf16, w_bf16, alpha)
+    q_w, s_w, z_w = quantize(w_bf16, 4, symmetric, GROUP, group_size, smooth=s, smooth_mode=SMOOTH_MUL)
+    q_x, s_x, _ = quantize(x_bf16, 8, True, ROW, smooth=s, smooth_mode=SMOOTH_DIV)
+    y = w4a8(q_x.astype(np.int8), s_x, q_w, s_w, z_w, group_size)
+    return {"s": s, "q_w": q_w, "s_w": s_w, "z_w": z_w, "q_x": q_x.astype(np.int8), "s_x": s_x, "y": y}

@@ -438,6 +438,34 @@ int or_gemm_s8(const int8_t *a, const int8_t *b, int64_t M, int64_t N, int64_t K
 
 /* Dequantize the integer product with the per-token activation scale and the per-output-channel weight
  * scale [P3 §11.4.5 step 6; P2 §11 vector-wise scaling]: y[m, n] = acc[m, n] * s_x[m] * s_w[n] in binary64. */
+/*
+ * W4A8 [P3 §11.4.5, §11.10.2: INT4 group weights stacked on INT8 per-token activations, each with its own
+ * scales]: y[m, n] = s_x[m] * sum_g s_w[n, g] * sum_{k in g} q_x[m, k] * (q_w[n, k] - z[n, g]).
+ * The integer sum of each group is exact (int64); the scaling and the sum over groups are binary64.
+ * q_w are the unpacked codes [N, K]; z may be NULL (symmetric codes, z = 0); any g dividing K.
+ */
+int or_w4a8(const int8_t *xq, const float *sx, int64_t M, int64_t N, int64_t K, const int32_t *qw, const float *sw,
+            const uint8_t *zw, int64_t g, double *y)
+{
+    if (g <= 0 || K % g != 0)
+        return -1;
+    const int64_t groups = K / g;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double t = 0.0;
+            for (int64_t gi = 0; gi < groups; ++gi) {
+                const int64_t z = zw ? (int64_t)zw[n * groups + gi] : 0;
+                int64_t acc = 0;
+                for (int64_t k = gi * g; k < (gi + 1) * g; ++k)
+                    acc += (int64_t)xq[m * K + k] * ((int64_t)qw[n * K + k] - z);
+                t += (double)sw[n * groups + gi] * (double)acc;
+            }
+            y[m * N + n] = (double)sx[m] * t;
+        }
+    return 0;
+}
+
 void or_w8a8_epilogue(const int64_t *acc, const float *s_x, const float *s_w, int64_t M, int64_t N, double *y)
 {
     for (int64_t m = 0; m < M; ++m)

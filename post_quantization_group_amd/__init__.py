@@ -30,6 +30,7 @@ EXPORTS = [
     "pqg_abi_version", "pqg_last_error", "pqg_quantize_workspace_bytes", "pqg_quantize", "pqg_quantize_static",
     "pqg_dequantize",
     "pqg_smooth_workspace_bytes", "pqg_smooth", "pqg_qlinear_w4a16", "pqg_qlinear_w8a8", "pqg_gemm_s8s8s32",
+    "pqg_qlinear_w4a8",
 ]
 
 _lib = None
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH):
     lib.pqg_qlinear_w8a8.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, P, P]
     lib.pqg_gemm_s8s8s32.restype = I32
     lib.pqg_gemm_s8s8s32.argtypes = [P, P, I64, I64, I64, P, P]
+    lib.pqg_qlinear_w4a8.restype = I32
+    lib.pqg_qlinear_w4a8.argtypes = [P, P, I64, I64, I64, P, P, P, I32, I32, P, I32, P]
     if lib.pqg_abi_version() != ABI_VERSION:
         raise ImportError("libpqg.so ABI %d != binding ABI %d" % (lib.pqg_abi_version(), ABI_VERSION))
     _lib = lib
@@ -248,3 +251,21 @@ def gemm_s8s8s32(a: torch.Tensor, b: torch.Tensor, out=None):
     c = torch.empty((M, N), dtype=torch.int32, device=dev) if out is None else out
     _check(lib.pqg_gemm_s8s8s32(_ptr(a), _ptr(b), M, N, K, _ptr(c), _stream(dev)))
     return c
+
+
+def qlinear_w4a8(x_q: torch.Tensor, x_scales: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, w_zeros,
+                 group_size: int, symmetric: bool, out_dtype=torch.bfloat16, out=None):
+    """pqg_qlinear_w4a8: per-token INT8 activation codes x [M, K] (scales [M]) times packed INT4 group codes
+    [N, K/2] (scales / zero points [N * K / group_size]) -> y [M, N]."""
+    lib = load()
+    dev = _dev(x_q)
+    if x_q.dtype != torch.int8:
+        raise TypeError("x_q must be int8")
+    M, K = x_q.shape
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 2 != K:
+        raise ValueError("w_packed must be [N, K/2]")
+    y = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    _check(lib.pqg_qlinear_w4a8(_ptr(x_q), _ptr(x_scales), M, N, K, _ptr(w_packed), _ptr(w_scales), _ptr(w_zeros),
+                                group_size, int(symmetric), _ptr(y), _float_dtype(y), _stream(dev)))
+    return y

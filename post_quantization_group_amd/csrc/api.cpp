@@ -285,4 +285,33 @@ int32_t pqg_gemm_s8s8s32(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
     return hip_status(pqg::launch_gemm_i8(g, as_stream(stream)), "pqg_gemm_s8s8s32 launch");
 }
 
+int32_t pqg_qlinear_w4a8(const int8_t *x_q, const float *x_scales, int64_t M, int64_t N, int64_t K,
+                         const uint8_t *w_packed, const float *w_scales, const uint8_t *w_zeros, int32_t group_size,
+                         int32_t symmetric, void *y, int32_t y_dtype, void *stream)
+{
+    g_err[0] = 0;
+    if (M < 0 || N < 0 || K < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (!valid_float_dtype(y_dtype))
+        return fail(PQG_EINVAL, "unknown y_dtype %d", y_dtype);
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(PQG_EINVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+    if (K % 128 != 0)
+        return fail(PQG_EINVAL, "K (%lld) must be a multiple of 128", (long long)K);
+    if (M == 0 || N == 0)
+        return PQG_OK;
+    if (!x_q || !x_scales || !w_packed || !w_scales || !y)
+        return fail(PQG_EINVAL, "x_q, x_scales, w_packed, w_scales and y are required");
+    if (symmetric && w_zeros)
+        return fail(PQG_EINVAL, "w_zeros must be NULL for symmetric weight codes");
+    if (!symmetric && !w_zeros)
+        return fail(PQG_EINVAL, "w_zeros is required for asymmetric weight codes");
+    if (!aligned(x_q, 16) || !aligned(w_packed, 16) || !aligned(x_scales, 4) || !aligned(w_scales, 4) ||
+        !aligned(y, 4))
+        return fail(PQG_EINVAL, "misaligned pointer (x_q, w_packed: 16 bytes; scales, y: 4 bytes)");
+    pqg::W4A8Args a{x_q, x_scales, M, N, K, w_packed, w_scales, w_zeros, group_size, symmetric != 0, y,
+                    y_dtype == PQG_BF16};
+    return hip_status(pqg::launch_w4a8(a, as_stream(stream)), "pqg_qlinear_w4a8 launch");
+}
+
 }  // extern "C"

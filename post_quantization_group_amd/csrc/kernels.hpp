@@ -101,4 +101,20 @@ hipError_t launch_w4a16(const W4A16Args &a, hipStream_t st);
 
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st);
 
+// W4A8: INT8 per-token activation codes x INT4 per-group weight codes.
+struct W4A8Args {
+    const int8_t *x_q;       // [M, K]
+    const float *x_scales;   // [M]
+    int64_t M, N, K;
+    const uint8_t *w;        // packed INT4 [N, K/2]
+    const float *w_scales;   // [N, K/g]
+    const uint8_t *w_zeros;  // [N, K/g], NULL iff symmetric
+    int group_size;
+    bool symmetric;
+    void *y;                 // [M, N]
+    bool y_bf16;
+};
+
+hipError_t launch_w4a8(const W4A8Args &a, hipStream_t st);
+
 }  // namespace pqg

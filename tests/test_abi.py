@@ -129,3 +129,17 @@ def test_w8a8_and_gemm_reject(lib):
     assert rc == pqg.EINVAL and "multiple of 16" in lib.pqg_last_error().decode()
     rc = lib.pqg_gemm_s8s8s32(MISALIGNED, FAKE, 4, 4, 32, FAKE, None)
     assert rc == pqg.EINVAL and "misaligned" in lib.pqg_last_error().decode()
+
+
+def test_w4a8_rejects(lib):
+    def call(**kw):
+        a = dict(xq=FAKE, sx=FAKE, M=4, N=64, K=256, w=FAKE, sw=FAKE, zw=None, g=128, sym=1, y=FAKE, yd=1)
+        a.update(kw)
+        return lib.pqg_qlinear_w4a8(a["xq"], a["sx"], a["M"], a["N"], a["K"], a["w"], a["sw"], a["zw"], a["g"],
+                                    a["sym"], a["y"], a["yd"], None)
+    for kw, needle in [(dict(g=96), "group_size"), (dict(K=192), "multiple of 128"), (dict(sym=0), "w_zeros"),
+                       (dict(zw=FAKE), "must be NULL"), (dict(yd=4), "y_dtype"), (dict(xq=None), "required"),
+                       (dict(w=MISALIGNED), "misaligned"), (dict(M=-1), "negative")]:
+        assert call(**kw) == pqg.EINVAL, kw
+        assert needle in lib.pqg_last_error().decode(), kw
+    assert call(M=0, xq=None, sx=None, w=None, sw=None, y=None) == pqg.OK

@@ -490,6 +490,71 @@ def test_w8a8_static_full_layer(gpu_lib):
     assert err <= TOL_BF16, err
 
 
+# --------------------------------------------------------------------------- W4A8
+
+# Ragged M and N (partial 128-token and 64 / 128-channel tiles), one K step (K = 128), three, eight.
+@pytest.mark.parametrize("mnk", [(5, 77, 128), (130, 200, 384), (257, 129, 1024), (64, 264, 256), (300, 385, 512)])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("sym", [True, False])
+def test_w4a8_small_fp32(gpu_lib, mnk, gs, sym):
+    m, n, k = mnk
+    announce("w4a8 %s g=%d sym=%s" % (mnk, gs, sym))
+    rng = np.random.default_rng(m * 31 + n + k + gs)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    qx = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    sx = rng.uniform(0.001, 0.05, m).astype(np.float32)
+    codes, s_w, z_w = gpu_lib.quantize(to_gpu(w), 4, sym, 2, gs)
+    y = gpu_lib.qlinear_w4a8(to_gpu(qx), to_gpu(sx), codes, s_w, z_w, gs, sym, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    q, so, zo = oracle.quantize(w, 4, sym, oracle.GROUP, gs)
+    assert np.array_equal(codes.cpu().numpy(), oracle.pack_int4(q))
+    y_ref = oracle.w4a8(qx, sx, q, so, zo, gs)
+    err = normwise(to_f64(y), y_ref)
+    assert err <= TOL_F32, err
+
+
+@pytest.mark.parametrize("mnk,gs,sym", [((130, 200, 384), 128, True), ((257, 136, 256), 32, False),
+                                        ((64, 1000, 512), 64, True)])
+def test_w4a8_small_bf16(gpu_lib, mnk, gs, sym):
+    m, n, k = mnk
+    announce("w4a8 bf16 %s g=%d sym=%s" % (mnk, gs, sym))
+    rng = np.random.default_rng(m + n * 3 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    qx = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    sx = rng.uniform(0.001, 0.05, m).astype(np.float32)
+    codes, s_w, z_w = gpu_lib.quantize(to_gpu(w), 4, sym, 2, gs)
+    y = gpu_lib.qlinear_w4a8(to_gpu(qx), to_gpu(sx), codes, s_w, z_w, gs, sym, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    q, so, zo = oracle.quantize(w, 4, sym, oracle.GROUP, gs)
+    err = normwise(to_f64(y), oracle.w4a8(qx, sx, q, so, zo, gs))
+    assert err <= TOL_BF16, err
+
+
+def test_w4a8_full_layer(gpu_lib):
+    """The W8A8 layer's shapes with INT4 g = 128 weights (2048 x 11008 x 4096): smoothing factor, weight and
+    activation codes and scales bit-exact; bf16 outputs within tolerance on 96 sampled tokens."""
+    announce("w4a8 full layer")
+    d = W.w8a8()
+    xg, wg = to_gpu_bf16(d["x"]), to_gpu_bf16(d["w"])
+    s = gpu_lib.smooth(xg, wg, 0.5)
+    codes, s_w, _ = gpu_lib.quantize(wg, 4, True, 2, 128, s, 2)
+    x_q, s_x, _ = gpu_lib.quantize(xg, 8, True, 1, 0, s, 1)
+    y = gpu_lib.qlinear_w4a8(x_q, s_x, codes, s_w, None, 128, True, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    so = oracle.smooth(d["x"], d["w"], 0.5)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    q, sw, _ = oracle.quantize(d["w"], 4, True, oracle.GROUP, 128, so, oracle.SMOOTH_MUL)
+    assert np.array_equal(codes.cpu().numpy(), oracle.pack_int4(q))
+    assert np.array_equal(s_w.cpu().numpy().view(np.uint32), sw.view(np.uint32))
+    qx, sx, _ = oracle.quantize(d["x"], 8, True, oracle.ROW, 0, so, oracle.SMOOTH_DIV)
+    assert np.array_equal(x_q.cpu().numpy(), qx.astype(np.int8))
+    rng = np.random.default_rng(6)
+    toks = np.unique(np.concatenate([rng.choice(2048, size=94, replace=False), [0, 2047]]))
+    y_ref = oracle.w4a8(qx[toks].astype(np.int8), sx[toks], q, sw, None, 128)
+    err = normwise(to_f64(y)[toks], y_ref)
+    assert err <= TOL_BF16, err
+
+
 # --------------------------------------------------------------------------- determinism
 
 def test_reruns_are_bit_identical(gpu_lib):

@@ -519,3 +519,61 @@ def test_w8a8_static_pipeline():
     same = oracle.w8a8_static(d["x"], d["x"], d["w"], 0.5)
     qd, _, _ = oracle.quantize(same["x_prime"], 8, True, oracle.TENSOR)
     assert np.array_equal(same["q_x"], qd.astype(np.int8))
+
+
+# --------------------------------------------------------------------------- W4A8
+
+def test_w4a8_one_group_is_w8a8():
+    """With one group spanning K and no zero point, W4A8 is the W8A8 product with a per-channel weight scale
+    ("第11章 模型量化与压缩" §11.4.5): the pinned integer GEMM and epilogue."""
+    rng = np.random.default_rng(11)
+    qx = rng.integers(-127, 128, size=(9, 256)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(13, 256)).astype(np.int32)
+    sx = rng.uniform(0.001, 0.1, 9).astype(np.float32)
+    sw = rng.uniform(0.001, 0.1, 13).astype(np.float32)
+    y = oracle.w4a8(qx, sx, qw, sw, None, 256)
+    ref = oracle.w8a8_epilogue(oracle.gemm_s8(qx, qw.astype(np.int8)), sx, sw)
+    assert np.allclose(y, ref, rtol=1e-15, atol=0)
+
+
+def test_w4a8_unit_scales_is_integer_product():
+    """All scales 1: the result is the exact integer product of q_x and (q_w - z) with z per group."""
+    rng = np.random.default_rng(12)
+    for g in (32, 64, 128):
+        qx = rng.integers(-127, 128, size=(5, 384)).astype(np.int8)
+        qw = rng.integers(0, 16, size=(7, 384)).astype(np.int32)
+        z = rng.integers(0, 16, size=(7, 384 // g)).astype(np.uint8)
+        y = oracle.w4a8(qx, np.ones(5, np.float32), qw, np.ones(7 * 384 // g, np.float32), z.ravel(), g)
+        wz = qw.astype(np.int64) - np.repeat(z.astype(np.int64), g, axis=1)
+        assert np.array_equal(y, (qx.astype(np.int64) @ wz.T).astype(np.float64))
+
+
+def test_w4a8_brute_force_rational():
+    """Tiny inputs against exact rational arithmetic (the binary64 result within 1e-12 relative)."""
+    rng = np.random.default_rng(13)
+    qx = rng.integers(-127, 128, size=(3, 96)).astype(np.int8)
+    qw = rng.integers(0, 16, size=(4, 96)).astype(np.int32)
+    z = rng.integers(0, 16, size=(4, 3)).astype(np.uint8)
+    sx = rng.uniform(0.01, 1, 3).astype(np.float32)
+    sw = rng.uniform(0.01, 1, 12).astype(np.float32)
+    y = oracle.w4a8(qx, sx, qw, sw, z.ravel(), 32)
+    for m in range(3):
+        for n in range(4):
+            t = Fraction(0)
+            for gi in range(3):
+                acc = sum(int(qx[m, k]) * (int(qw[n, k]) - int(z[n, gi])) for k in range(32 * gi, 32 * gi + 32))
+                t += Fraction(float(sw[n * 3 + gi])) * acc
+            exact = Fraction(float(sx[m])) * t
+            assert abs(Fraction(y[m, n]) - exact) <= abs(exact) * Fraction(1, 10 ** 12)
+
+
+def test_w4a8_pipeline_approximates_float_product():
+    """INT4 group weights (g = 128) with SmoothQuant INT8 activations approximate X W^T (coarser than W8A8:
+    INT4 weights)."""
+    d = workloads.w8a8(m=32, n=48, k=512)
+    xf = workloads.bf16_to_f32(d["x"]).astype(np.float64)
+    wf = workloads.bf16_to_f32(d["w"]).astype(np.float64)
+    y_true = xf @ wf.T
+    for sym in (True, False):
+        r = oracle.w4a8_pipeline(d["x"], d["w"], 0.5, 128, sym)
+        assert np.linalg.norm(r["y"] - y_true) / np.linalg.norm(y_true) < 0.2
