@@ -17,6 +17,8 @@ One step is one pass over every stage of the quantized linear layer on synthetic
                                                              <- the INT8 GEMM TOPS
   w8a8_static_actquant  the pages' static variant: X' = X diag(s)^-1 in bf16 (as a LayerNorm with s folded
              into its gain emits it) to INT8 with one calibrated per-tensor scale (the GEMM is the same)
+  w4a8       the same layer with the smoothed weights as INT4, g = 128 (quantized once, offline), times the
+             step's per-token INT8 activation codes                                    <- the W4A8 TOPS
 The packed layer exists twice. A step re-quantizes into one copy, runs the dequantize and the W8A8 layer,
 then the batch-32 and batch-8 passes over the other copy (clean 455 MB reads that also drain the dirty lines
 the 1.7 GB dequantize left in the 256 MB last-level cache), and last the batch-1 decode pass over the copy
@@ -149,6 +151,8 @@ def main():
     Xcal = (bf16(W.w8a8_calibration(512, K8)).float() / s8).to(torch.bfloat16)
     s_static = float(pqg.quantize(Xcal, 8, True, pqg.TENSOR)[1].cpu()[0])
     xq8s = torch.empty((M8, K8), dtype=torch.int8, device=dev)
+    wq4, sw4, _ = pqg.quantize(W8, 4, True, pqg.GROUP, 128, s8, pqg.SMOOTH_MUL)
+    y4 = torch.empty((M8, N8), dtype=torch.bfloat16, device=dev)
     sx8s = torch.empty(M8, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
@@ -158,7 +162,7 @@ def main():
     w8a8_ops = 2.0 * M8 * N8 * K8
 
     parts = ["quantize", "dequantize", "smooth", "wquant", "w8a8_actquant", "w8a8_gemm", "w8a8_static_actquant",
-             "w4a16_m32", "w4a16_m8", "w4a16_m1"]
+             "w4a8_gemm", "w4a16_m32", "w4a16_m8", "w4a16_m1"]
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def run_step(i, rec):
@@ -203,6 +207,10 @@ def main():
         if rec:
             marks["w8a8_static_actquant"] = ev()
             marks["w8a8_static_actquant"].record(stream)
+        pqg.qlinear_w4a8(xq8, sx8, wq4, sw4, None, 128, True, out=y4)  # INT4 g = 128 weights x INT8 activations
+        if rec:
+            marks["w4a8_gemm"] = ev()
+            marks["w4a8_gemm"].record(stream)
         for p in projs:  # S7: batch 32
             pqg.qlinear_w4a16(p["x"], p["packed"][o], p["scales"][o], None, 128, True, out=p["y32"])
         if rec:
@@ -314,6 +322,16 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                          "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": gemm_traffic,
                          "ops_per_launch": w8a8_ops, "avg_launch_us": round(gemm_ms * 1e3, 2)},
+        },
+        # the W4A8 layer: one launch over the same activation codes; its weights take half the INT8 GEMM's
+        # bytes (4 bits against 8) plus one fp32 scale per 128 weights
+        "w4a8_gemm": {
+            "value": round(w8a8_ops / (part_ms["w4a8_gemm"] * 1e-3) / 1e12, 1),
+            "unit": "TOPS",
+            "frac": round(w8a8_ops / (part_ms["w4a8_gemm"] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "avg_launch_us": round(part_ms["w4a8_gemm"] * 1e3, 2),
+            "group_size": 128,
+            "weight_bytes": N8 * K8 // 2 + N8 * (K8 // 128) * 4,
         },
         "per_projection_event_us": {p["name"]: round(float(t) * 1e3, 2) for p, t in zip(projs, launch_ms)},
         "stage_ms": {k: round(v, 4) for k, v in part_ms.items()},

@@ -125,25 +125,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_w4a8(const int8_t *__restrict__
         const int p = tid + kThreads * i;
         woffs[i] = (uint32_t)(std::min<int64_t>(p / 4, N - 1 - n0) * (K / 2) + 16 * (p % 4));
     }
-    uint4 rx[kXLoads], rw[kWLoads];
+    // staging registers as clang vectors: arrays of HIP's uint4 struct stayed in scratch memory here
+    v4i rx[kXLoads], rw[kWLoads];
     auto load = [&](int step) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kXLoads; ++i)
-            rx[i] = *reinterpret_cast<const uint4 *>(xbase + (xoffs[i] + (uint32_t)step * kBK));
+            rx[i] = *reinterpret_cast<const v4i *>(xbase + (xoffs[i] + (uint32_t)step * kBK));
 #pragma unroll
         for (int i = 0; i < kWLoads; ++i)
-            rw[i] = *reinterpret_cast<const uint4 *>(wbase + (woffs[i] + (uint32_t)step * (kBK / 2)));
+            rw[i] = *reinterpret_cast<const v4i *>(wbase + (woffs[i] + (uint32_t)step * (kBK / 2)));
     };
     auto store = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kXLoads; ++i) {
             const int p = tid + kThreads * i;
-            *reinterpret_cast<uint4 *>(&sX[st][xoff(p / 8, p % 8)]) = rx[i];
+            *reinterpret_cast<v4i *>(&sX[st][xoff(p / 8, p % 8)]) = rx[i];
         }
 #pragma unroll
         for (int i = 0; i < kWLoads; ++i) {
             const int p = tid + kThreads * i;
-            *reinterpret_cast<uint4 *>(&sW[st][woff(p / 4, p % 4)]) = rw[i];
+            *reinterpret_cast<v4i *>(&sW[st][woff(p / 4, p % 4)]) = rw[i];
         }
     };
 
