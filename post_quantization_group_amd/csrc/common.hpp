@@ -8,6 +8,24 @@ namespace pqg {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
+// ------------------------------------------------------------------ direct global -> LDS loads
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+// s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4] (7 = no wait), lgkmcnt
+// [11:8] (15 = no wait)
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+// One LDS block per (size, id): distinct objects, so the compiler keeps them apart in alias analysis (it
+// would otherwise wait for every outstanding direct load into one block before reading another).
+template <int BYTES, int ID>
+__device__ __forceinline__ int8_t *lds_block()
+{
+    __shared__ __attribute__((aligned(16))) int8_t buf[BYTES];
+    return buf;
+}
+
 // ------------------------------------------------------------------ bf16
 
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }

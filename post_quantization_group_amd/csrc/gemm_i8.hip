@@ -298,12 +298,6 @@ constexpr int kRingStage = (kRingBM + kRingBN) * kRingBK;    // bytes: [BM][64] 
 constexpr int kRingLoads = kRingStage / 16 / kRingThreads;    // direct loads per thread per step
 static_assert(kRingStage % (16 * kRingThreads) == 0, "each thread issues whole loads");
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void global_void_t;
-
-// s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4] (7 = no wait), lgkmcnt
-// [11:8] (15 = no wait)
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
 template <int MODE>
 __global__ __launch_bounds__(kRingThreads, 2) void k_gemm_i8_ring(const int8_t *__restrict__ a,
@@ -507,13 +501,6 @@ constexpr int kWideALoads = kWideBM * kWideBK / 16 / kWideThreads;  // the first
 static_assert(kWideStage % (16 * kWideThreads) == 0 && (kWideBM * kWideBK) % (16 * kWideThreads) == 0,
               "each load instruction fills whole rows of one operand");
 
-// One LDS block per (size, id): distinct objects, so the compiler keeps them apart in alias analysis.
-template <int BYTES, int ID>
-__device__ __forceinline__ int8_t *lds_block()
-{
-    __shared__ __attribute__((aligned(16))) int8_t buf[BYTES];
-    return buf;
-}
 
 template <int MODE>
 __global__ __launch_bounds__(kWideThreads, 1) void k_gemm_i8_wide(const int8_t *__restrict__ a,

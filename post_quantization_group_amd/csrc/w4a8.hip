@@ -8,25 +8,33 @@
 //
 // Operands. v_mfma_i32_32x32x32_i8 with the activation tile as A (rows = tokens) and the weight tile as B
 // (columns = output channels): lane l holds output channel n = l % 32 and, in register r, token
-// m = 8 (r / 4) + 4 (l / 32) + r % 4. A lane therefore needs one weight scale and one zero point per group
-// and tile, whatever r.
-//   * Weight codes are staged packed (two per byte) and unpacked when read: 8 bytes (16 codes) of row n give
-//     one B operand. Per 4-byte word (8 codes): the low and the high nibbles are masked into bytes, biased by
-//     0x80 (and, for two's-complement codes, their sign bit flipped, which turns q into q + 8), put back in
-//     code order with v_perm, and the zero point (8 for symmetric codes) is subtracted from all four bytes
-//     at once: each byte is >= 0x80 > z, so no borrow crosses a byte. Removing the bias leaves the signed
-//     byte q - z in [-15, 15].
-//   * Which codes one MFMA sums is free as long as A and B agree; what matters is that every MFMA lies inside
-//     one group. A step's 128 codes are taken as two pairs of 64 codes, each pair as two MFMAs. For g = 64
-//     and 128 a pair lies inside one group, and lane half h takes the pair's codes 32 h .. 32 h + 31 (one
-//     16-byte read of packed codes, 16 codes per MFMA). For g = 32 each MFMA must be one group of 32
-//     consecutive codes, so lane half h takes its codes 16 h .. 16 h + 15 (an 8-byte read per MFMA). The
-//     int32 accumulator of a group is started from zero, and after the group's last MFMA it is added into
-//     fp32 accumulators with its scale s_w[n, g].
-// Tiling: 128 (m) x 128 (n) block tile, four waves of 64 x 64 (2 x 2 MFMA tiles; 128 x 64 and 64 x 32 for
-// g = 32 and 64), K steps of 128 codes
-// (activation rows 128 bytes, weight rows 64 bytes), two LDS stages filled from registers while the other
-// is multiplied, as in the register-staged INT8 kernel. XCD-aware tile order as there.
+// m = 8 (r / 4) + 4 (l / 32) + r % 4. A lane therefore needs one weight scale (and zero point) per group,
+// whatever r.
+//
+// What bounds it. Every group ends in a fold: each int32 accumulator is converted to fp32 and added with its
+// group scale, two VALU instructions per accumulator per group. At g = 128 that is as many VALU cycles as
+// the group's MFMA cycles (a wave64 VALU instruction takes 4 cycles, an int8 32x32x32 MFMA 32), so the
+// kernel is built to spend as little VALU as possible elsewhere:
+//   * Symmetric codes (two's complement nibbles) are unpacked by moving each nibble to the top of its byte:
+//     the byte then reads as 16 q, so the MFMA sums 16x the exact integer, and the factor 1/16 is applied
+//     with the token scale at the end (a power of two: the fp32 results are those of unscaled sums). Per
+//     4-byte word (8 codes): one shift, two v_perm, two masks.
+//   * Asymmetric codes: the nibbles are masked into bytes biased by 0x80, put in code order with v_perm, and
+//     the zero point is subtracted from all four bytes at once (each byte is >= 0x80 > z, so no borrow
+//     crosses a byte); removing the bias leaves the signed byte q - z in [-15, 15].
+//   * A wave computes 128 tokens x 32 channels (four MFMA tiles share each unpacked weight operand).
+// Which codes one MFMA sums is free as long as A and B agree; what matters is that every MFMA lies inside one
+// group. A step's 128 codes are two pairs of 64 codes, each pair two MFMAs. For g = 64 and 128 a pair lies
+// inside one group and lane half h takes the pair's codes 32 h .. 32 h + 31 (one 16-byte read of packed
+// codes, 16 codes per MFMA); for g = 32 each MFMA must be one group of 32 consecutive codes, so lane half h
+// takes its codes 16 h .. 16 h + 15 (an 8-byte read per MFMA). The int32 accumulators of a group start from
+// zero (the MFMA's C operand) and are folded after the group's last MFMA.
+// Tiling and feed: 128 (m) x 128 (n) block tile, four waves side by side along n, K steps of 128 codes.
+// Operands go global -> LDS with direct loads (no registers, no LDS store instructions) into a ring of three
+// stages, as in the INT8 GEMM's ring kernel: step k issues the loads of step k + 2, multiplies stage k and
+// waits only for the loads of step k + 1. The group scales of step k + 1 are loaded into registers just
+// before those direct loads, so waiting for all but the last six loads also covers them. The epilogue stages
+// the unscaled fp32 tile in the idle stages and writes 16-byte chunks of output rows with the token scale.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,49 +46,54 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kW8Xcds = 8;
-constexpr int kBM = 128, kWM = 64, kBK = 128;  // kBK in codes
-constexpr int kThreads = 256;
-constexpr int kXRow = kBK, kWRow = kBK / 2;    // bytes per staged row
-constexpr int kXLoads = kBM * kXRow / 16 / kThreads;  // 4
-static_assert(kXLoads * 16 * kThreads == kBM * kXRow, "whole loads");
-
-// Output channels per wave: 64 (two MFMA tiles) for g = 128, 32 for g = 32 and 64, whose per-step group
-// metadata and more frequent folds would otherwise not fit the 256 registers of two waves per SIMD.
-template <int G>
-struct W4A8Tile {
-    static constexpr int WN = G == 128 ? 64 : 32, BN = 2 * WN;
-    static constexpr int WLOADS = BN * kWRow / 16 / kThreads;
-    static_assert(WLOADS * 16 * kThreads == BN * kWRow, "whole loads");
-};
+constexpr int kBM = 128, kBN = 128, kBK = 128;  // tokens x channels per block, codes per K step
+constexpr int kWaves = 4, kThreads = kWaves * kWave;
+constexpr int kWN = kBN / kWaves;                // 32 channels per wave
+constexpr int kTM = kBM / 32;                    // 4 token tiles per wave
+constexpr int kXRow = kBK, kWRow = kBK / 2;      // bytes per staged row
+constexpr int kXBytes = kBM * kXRow;             // 16384
+constexpr int kStage = kXBytes + kBN * kWRow;    // 24576
+constexpr int kLoads = kStage / 16 / kThreads;   // 6 direct loads per thread per step
+constexpr int kXLoads = kXBytes / 16 / kThreads; // the first 4 fill activation rows
+static_assert(kLoads * 16 * kThreads == kStage && kXLoads * 16 * kThreads == kXBytes, "whole loads");
+static_assert(kWN == 32, "one MFMA tile of channels per wave");
 
 // LDS offset of 16-byte piece c of a staged row r: rows of 128 bytes (activations) and 64 bytes (packed
 // weights). The piece index is xor-ed with row bits so that the 16 rows read together by one half of a
-// wave fall into different bank quads.
-__device__ __forceinline__ int xoff(int r, int c) { return r * kXRow + 16 * (c ^ (((r >> 1) & 3) | ((r >> 2) & 4))); }
-__device__ __forceinline__ int woff(int r, int c) { return r * kWRow + 16 * (c ^ (((r >> 2) & 1) | ((r >> 3) & 2))); }
+// wave fall into different bank quads. Both swizzles are their own inverse.
+__device__ __forceinline__ int xsw(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
+__device__ __forceinline__ int wsw(int r) { return ((r >> 2) & 1) | ((r >> 3) & 2); }
+__device__ __forceinline__ int xoff(int r, int c) { return r * kXRow + 16 * (c ^ xsw(r)); }
+__device__ __forceinline__ int woff(int r, int c) { return r * kWRow + 16 * (c ^ wsw(r)); }
 
-// One B operand (16 signed codes q - z) from 8 bytes of packed codes, with the zero point z replicated in zz.
-__device__ __forceinline__ v4i unpack8(uint32_t w0, uint32_t w1, uint32_t mask, uint32_t bias, uint32_t zz)
+// One B operand from 8 bytes of symmetric packed codes: 16 bytes 16 q, in code order.
+__device__ __forceinline__ v4i unpack_sym(uint32_t w0, uint32_t w1)
 {
     const uint32_t w[2] = {w0, w1};
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const uint32_t ev = __builtin_amdgcn_bitop3_b32(w[i], mask, bias, 0x6A);       // codes 0,2,4,6: (a & b) ^ c
-        const uint32_t od = __builtin_amdgcn_bitop3_b32(w[i] >> 4, mask, bias, 0x6A);  // codes 1,3,5,7
-        // back in code order (bytes c0 c1 c2 c3 and c4 c5 c6 c7), then minus z in every byte, bias removed
-        o[2 * i] = (__builtin_amdgcn_perm(od, ev, 0x05010400u) - zz) ^ 0x80808080u;
-        o[2 * i + 1] = (__builtin_amdgcn_perm(od, ev, 0x07030602u) - zz) ^ 0x80808080u;
+        const uint32_t s = w[i] << 4;  // byte j: low nibble of byte j on top
+        // bytes (s0 w0 s1 w1) and (s2 w2 s3 w3): codes 0..3 and 4..7 on top of their bytes
+        o[2 * i] = __builtin_amdgcn_perm(w[i], s, 0x05010400u) & 0xF0F0F0F0u;
+        o[2 * i + 1] = __builtin_amdgcn_perm(w[i], s, 0x07030602u) & 0xF0F0F0F0u;
     }
     return v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
 }
 
-// A loop-invariant constant in a VGPR (v_bitop3_b32 takes no literal).
-__device__ __forceinline__ uint32_t vconst(uint32_t c)
+// One B operand from 8 bytes of asymmetric packed codes: 16 signed bytes q - z, with z replicated in zz.
+__device__ __forceinline__ v4i unpack_asym(uint32_t w0, uint32_t w1, uint32_t zz)
 {
-    uint32_t r;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
-    return r;
+    const uint32_t w[2] = {w0, w1};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t ev = (w[i] & 0x0F0F0F0Fu) | 0x80808080u;         // codes 0,2,4,6 + 0x80
+        const uint32_t od = ((w[i] >> 4) & 0x0F0F0F0Fu) | 0x80808080u;  // codes 1,3,5,7 + 0x80
+        o[2 * i] = (__builtin_amdgcn_perm(od, ev, 0x05010400u) - zz) ^ 0x80808080u;
+        o[2 * i + 1] = (__builtin_amdgcn_perm(od, ev, 0x07030602u) - zz) ^ 0x80808080u;
+    }
+    return v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
 }
 
 template <int G, bool SYM, bool OUT_BF16>
@@ -89,12 +102,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_w4a8(const int8_t *__restrict__
                                                      const float *__restrict__ sw, const uint8_t *__restrict__ zw,
                                                      void *__restrict__ y, int tiles)
 {
-    constexpr int kWN = W4A8Tile<G>::WN, kBN = W4A8Tile<G>::BN, kWLoads = W4A8Tile<G>::WLOADS;
-    constexpr int TM = kWM / 32, TN = kWN / 32;
     constexpr int DPG = G / 32;   // MFMA depths per group (1, 2 or 4: a divisor of the 4 depths of a step)
     constexpr int GPS = kBK / G;  // groups per step
-    __shared__ __attribute__((aligned(16))) int8_t sX[2][kBM * kXRow];
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][kBN * kWRow];
+    int8_t *const s0 = lds_block<kStage, 0>();
+    int8_t *const s1 = lds_block<kStage, 1>();
+    int8_t *const s2 = lds_block<kStage, 2>();
 
     const int per = (tiles + kW8Xcds - 1) / kW8Xcds;  // XCD x takes tiles [x per, (x + 1) per)
     const int t = (int)(blockIdx.x % kW8Xcds) * per + (int)(blockIdx.x / kW8Xcds);
@@ -106,184 +118,195 @@ __global__ __launch_bounds__(kThreads, 2) void k_w4a8(const int8_t *__restrict__
 
     const int tid = threadIdx.x, lane = tid % kWave;
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = w % (kBM / kWM), wn = w / (kBM / kWM);
     const int col = lane % 32, h = lane / 32;
     const int64_t groups = K / G;
+    const int nsteps = (int)(K / kBK);
 
-    // global -> register -> LDS: piece p = tid + 256 i -> staged row p / pieces-per-row, piece p % that.
-    // 32-bit offsets from the tile's first rows (a [128, K] activation slice and a [BN, K / 2] weight slice).
-    const int8_t *xbase = xq + m0 * K;
-    const uint8_t *wbase = wp + n0 * (K / 2);
-    uint32_t xoffs[kXLoads], woffs[kWLoads];
+    // Direct-load sources. Instruction i of wave w fills the 64 slots from S = (i * waves + w) * 64 of a stage:
+    // slots [0, 1024) are activation row P / 8, physical piece P % 8; the rest weight row (P - 1024) / 4,
+    // physical piece P % 4. A slot is filled from the logical piece that the swizzle puts there; rows past
+    // M or N repeat the last row (computed, never stored). 32-bit offsets from the tile's first rows.
+    const int8_t *const xbase = xq + m0 * K;
+    const uint8_t *const wbase = wp + n0 * (K / 2);
+    uint32_t offs[kLoads];
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i) {
-        const int p = tid + kThreads * i;
-        xoffs[i] = (uint32_t)(std::min<int64_t>(p / 8, M - 1 - m0) * K + 16 * (p % 8));
-    }
-#pragma unroll
-    for (int i = 0; i < kWLoads; ++i) {
-        const int p = tid + kThreads * i;
-        woffs[i] = (uint32_t)(std::min<int64_t>(p / 4, N - 1 - n0) * (K / 2) + 16 * (p % 4));
-    }
-    // staging registers as clang vectors: arrays of HIP's uint4 struct stayed in scratch memory here
-    v4i rx[kXLoads], rw[kWLoads];
-    auto load = [&](int step) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kXLoads; ++i)
-            rx[i] = *reinterpret_cast<const v4i *>(xbase + (xoffs[i] + (uint32_t)step * kBK));
-#pragma unroll
-        for (int i = 0; i < kWLoads; ++i)
-            rw[i] = *reinterpret_cast<const v4i *>(wbase + (woffs[i] + (uint32_t)step * (kBK / 2)));
-    };
-    auto store = [&](int st) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kXLoads; ++i) {
-            const int p = tid + kThreads * i;
-            *reinterpret_cast<v4i *>(&sX[st][xoff(p / 8, p % 8)]) = rx[i];
+    for (int i = 0; i < kLoads; ++i) {
+        const int P = (i * kWaves + w) * kWave + lane;
+        if (i < kXLoads) {
+            const int r = P >> 3;
+            offs[i] = (uint32_t)(std::min<int64_t>(r, M - 1 - m0) * K + 16 * ((P & 7) ^ xsw(r)));
+        } else {
+            const int q = P - kBM * 8, r = q >> 2;
+            offs[i] = (uint32_t)(std::min<int64_t>(r, N - 1 - n0) * (K / 2) + 16 * ((q & 3) ^ wsw(r)));
         }
+    }
+    auto issue = [&](int8_t *stage, int k) __attribute__((always_inline)) {
+        const int64_t kk = k < nsteps ? k : nsteps - 1;  // past the end: reload the last step
+        const int8_t *xb = xbase + kk * kBK;
+        const uint8_t *wb = wbase + kk * (kBK / 2);
 #pragma unroll
-        for (int i = 0; i < kWLoads; ++i) {
-            const int p = tid + kThreads * i;
-            *reinterpret_cast<v4i *>(&sW[st][woff(p / 4, p % 4)]) = rw[i];
+        for (int i = 0; i < kLoads; ++i) {
+            const void *src = i < kXLoads ? (const void *)(xb + offs[i]) : (const void *)(wb + offs[i]);
+            __builtin_amdgcn_global_load_lds((global_void_t *)src, (lds_void_t *)(stage + (i * kWaves + w) * kWave * 16),
+                                             16, 0, 0);
         }
     };
 
-    // per-lane weight rows of the TN tiles (clamped: rows past N are computed, never stored)
-    int64_t nrow[TN];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-        nrow[i] = std::min<int64_t>(n0 + wn * kWN + i * 32 + col, N - 1);
-    // scales and replicated zero points of the step's GPS groups, loaded one step ahead like the tiles
+    // the lane's channel (clamped: channels past N are computed, never stored) and its group metadata
+    const int64_t nrow = std::min<int64_t>(n0 + w * kWN + col, N - 1);
+    const float *const swr = sw + nrow * groups;
+    const uint8_t *const zwr = SYM ? nullptr : zw + nrow * groups;
     struct Meta {
-        float s[TN][GPS];
-        uint32_t zz[TN][GPS];
+        float s[GPS];
+        uint32_t zz[GPS];
     };
-    auto load_meta = [&](Meta &md, int step) __attribute__((always_inline)) {
+    auto load_meta = [&](Meta &md, int k) __attribute__((always_inline)) {
+        const int64_t kk = k < nsteps ? k : nsteps - 1;
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
-#pragma unroll
-            for (int gi = 0; gi < GPS; ++gi) {
-                const int64_t idx = nrow[i] * groups + (int64_t)step * GPS + gi;
-                md.s[i][gi] = sw[idx];
-                md.zz[i][gi] = (SYM ? 8u : (uint32_t)zw[idx]) * 0x01010101u;
-            }
+        for (int gi = 0; gi < GPS; ++gi) {
+            md.s[gi] = swr[kk * GPS + gi];
+            md.zz[gi] = SYM ? 0u : (uint32_t)zwr[kk * GPS + gi] * 0x01010101u;
+        }
     };
 
-    const uint32_t mask = vconst(0x0F0F0F0Fu);
-    const uint32_t bias = vconst(SYM ? 0x88888888u : 0x80808080u);
-    v16i acc[TN][TM];
-    float facc[TN][TM][16];
+    v16i acc[kTM];
+    float facc[kTM][16];
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+    for (int j = 0; j < kTM; ++j)
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
+        for (int e = 0; e < 16; ++e) {
+            acc[j][e] = 0;
+            facc[j][e] = 0.0f;
+        }
+    // add a finished group into the fp32 accumulators and restart the integer ones
+    auto fold = [&](float sc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kTM; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                acc[i][j][e] = 0;
-                facc[i][j][e] = 0.0f;
+                facc[j][e] = __builtin_fmaf(sc, (float)acc[j][e], facc[j][e]);
+                acc[j][e] = 0;
             }
-    // add a finished group (index gi within the step) into the fp32 accumulators, restart the integer ones
-    auto fold = [&](const Meta &md, int gi) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < TN; ++i) {
-            const float sc = md.s[i][gi];
-#pragma unroll
-            for (int j = 0; j < TM; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    facc[i][j][e] = __builtin_fmaf(sc, (float)acc[i][j][e], facc[i][j][e]);
-                    acc[i][j][e] = 0;
-                }
-        }
     };
 
-    const int nsteps = (int)(K / kBK);
-    Meta mcur, mnxt;
-    load(0);
-    load_meta(mcur, 0);
-    store(0);
-    __syncthreads();
-    for (int step = 0; step < nsteps; ++step) {
-        const int cur = step & 1;
-        if (step + 1 < nsteps) {
-            load(step + 1);
-            load_meta(mnxt, step + 1);
-        }
-        // two pairs of MFMA depths per step; pair q covers codes 64 q .. 64 q + 63 of the step
+    const int wrow = w * kWN + col;  // the lane's weight row in a stage
+    auto multiply = [&](const int8_t *st, const Meta &md) __attribute__((always_inline)) {
+        const int8_t *ws = st + kXBytes;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            v4i fb[TN][2];
+        for (int q = 0; q < 2; ++q) {  // pair q: codes 64 q .. 64 q + 63 of the step
+            v4i fb[2];
+            if constexpr (G == 32) {  // MFMA e is group 2 q + e: packed piece 2 q + e, its half h
 #pragma unroll
-            for (int i = 0; i < TN; ++i) {
-                const int row = wn * kWN + i * 32 + col;
-                if constexpr (G == 32) {
-                    // MFMA e is group 2 q + e: packed piece 2 q + e, its half h
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const uint2 pc = *reinterpret_cast<const uint2 *>(&sW[cur][woff(row, 2 * q + e) + 8 * h]);
-                        fb[i][e] = unpack8(pc.x, pc.y, mask, bias, mcur.zz[i][2 * q + e]);
-                    }
-                } else {
-                    // the pair is inside group (2 q) / DPG: packed piece 2 q + h, MFMA e its half e
-                    const uint4 pc = *reinterpret_cast<const uint4 *>(&sW[cur][woff(row, 2 * q + h)]);
-                    const uint32_t zz = mcur.zz[i][(2 * q) / DPG];
-                    fb[i][0] = unpack8(pc.x, pc.y, mask, bias, zz);
-                    fb[i][1] = unpack8(pc.z, pc.w, mask, bias, zz);
+                for (int e = 0; e < 2; ++e) {
+                    const uint2 pc = *reinterpret_cast<const uint2 *>(ws + woff(wrow, 2 * q + e) + 8 * h);
+                    fb[e] = SYM ? unpack_sym(pc.x, pc.y) : unpack_asym(pc.x, pc.y, md.zz[2 * q + e]);
                 }
+            } else {  // the pair lies in group (2 q) / DPG: packed piece 2 q + h, MFMA e its half e
+                const v4i pc = *reinterpret_cast<const v4i *>(ws + woff(wrow, 2 * q + h));
+                const uint32_t zz = md.zz[(2 * q) / DPG];
+                fb[0] = SYM ? unpack_sym(pc[0], pc[1]) : unpack_asym(pc[0], pc[1], zz);
+                fb[1] = SYM ? unpack_sym(pc[2], pc[3]) : unpack_asym(pc[2], pc[3], zz);
             }
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                // the activation piece holding the same 16 codes as fb[.][e]
-                const int xp = G == 32 ? 4 * q + 2 * e + h : 4 * q + 2 * h + e;
-                v4i fa[TM];
+                const int xp = G == 32 ? 4 * q + 2 * e + h : 4 * q + 2 * h + e;  // same 16 codes as fb[e]
+                v4i fa[kTM];
 #pragma unroll
-                for (int j = 0; j < TM; ++j)
-                    fa[j] = *reinterpret_cast<const v4i *>(&sX[cur][xoff(wm * kWM + j * 32 + col, xp)]);
+                for (int j = 0; j < kTM; ++j)
+                    fa[j] = *reinterpret_cast<const v4i *>(st + xoff(j * 32 + col, xp));
 #pragma unroll
-                for (int i = 0; i < TN; ++i)
-#pragma unroll
-                    for (int j = 0; j < TM; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[j], fb[i][e], acc[i][j], 0, 0, 0);
-                // depth 2 q + e of the step ends its group when (2 q + e + 1) % DPG == 0 (DPG divides 4)
-                if ((2 * q + e + 1) % DPG == 0)
-                    fold(mcur, (2 * q + e) / DPG);
+                for (int j = 0; j < kTM; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[j], fb[e], acc[j], 0, 0, 0);
+                if ((2 * q + e + 1) % DPG == 0)  // depth 2 q + e ends its group
+                    fold(md.s[(2 * q + e) / DPG]);
             }
         }
-        if (step + 1 < nsteps) {
-            store(cur ^ 1);
-            mcur = mnxt;
-        }
-        __syncthreads();
-    }
+    };
 
-    // epilogue: token scale and store; lane holds channel n, registers r the tokens 8 (r / 4) + 4 h + r % 4.
-    // For one r the 32 lanes of a half write 32 consecutive channels of one output row.
+    Meta mcur, mnxt;
+    auto step = [&](const int8_t *cur, int8_t *after_next, int k) __attribute__((always_inline)) {
+        load_meta(mnxt, k + 1);    // before the direct loads: the wait below covers it
+        issue(after_next, k + 2);
+        multiply(cur, mcur);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kLoads, 0));  // step k + 1 landed, fragment reads done
+        __builtin_amdgcn_s_barrier();
+        mcur = mnxt;
+    };
+
+    load_meta(mcur, 0);
+    issue(s0, 0);
+    issue(s1, 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kLoads, 15));
+    __builtin_amdgcn_s_barrier();
+    int k = 0;
+    for (; k + 3 <= nsteps; k += 3) {
+        step(s0, s2, k);
+        step(s1, s0, k + 1);
+        step(s2, s1, k + 2);
+    }
+    if (k < nsteps)
+        step(s0, s2, k);
+    if (k + 1 < nsteps)
+        step(s1, s0, k + 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no direct load may land in the stages reused below
+    __syncthreads();
+
+    // Epilogue: the unscaled fp32 tile as [token][channel] rows (512 bytes + 16 of padding, so the two lane
+    // halves, 4 rows apart, write different banks) over the three stages; then each thread takes 8-channel
+    // chunks of a row, applies the token scale (with 1/16 for symmetric codes), and stores them.
+    constexpr int ROWB = kBN * 4 + 16, RPS = kStage / ROWB;
+    static_assert(3 * RPS >= kBM, "the output tile fits in the stages");
+    auto rowp = [&](int ml) __attribute__((always_inline)) -> float * {
+        int8_t *p = ml < RPS ? s0 + ml * ROWB : ml < 2 * RPS ? s1 + (ml - RPS) * ROWB : s2 + (ml - 2 * RPS) * ROWB;
+        return reinterpret_cast<float *>(p);
+    };
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-        const int64_t n = n0 + wn * kWN + i * 32 + col;
-        if (n >= N)
+    for (int j = 0; j < kTM; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            rowp(j * 32 + 8 * (r / 4) + 4 * h + r % 4)[w * kWN + col] = facc[j][r];
+    __syncthreads();
+    constexpr float kUnit = SYM ? 0.0625f : 1.0f;
+    constexpr int CPR = kBN / 8;  // 8-channel chunks per row
+    const bool vec_ok = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(y) % 16) == 0;
+    for (int qi = tid; qi < kBM * CPR; qi += kThreads) {
+        const int ml = qi / CPR, cl = qi % CPR;
+        const int64_t m = m0 + ml, nb = n0 + cl * 8;
+        if (m >= M || nb >= N)
             continue;
-#pragma unroll
-        for (int j = 0; j < TM; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * kWM + j * 32 + 8 * (r / 4) + 4 * h + r % 4;
-                if (m < M) {
-                    const float v = facc[i][j][r] * sx[m];
-                    if (OUT_BF16)
-                        reinterpret_cast<uint16_t *>(y)[m * N + n] = (uint16_t)f32_to_bf16_bits(v);
-                    else
-                        reinterpret_cast<float *>(y)[m * N + n] = v;
-                }
+        const float *src = rowp(ml) + cl * 8;
+        const float4 a = reinterpret_cast<const float4 *>(src)[0], b = reinterpret_cast<const float4 *>(src)[1];
+        const float sm = sx[m] * kUnit;
+        const float v[8] = {a.x * sm, a.y * sm, a.z * sm, a.w * sm, b.x * sm, b.y * sm, b.z * sm, b.w * sm};
+        if (vec_ok) {  // N % 8 == 0: a chunk never crosses N
+            if (OUT_BF16)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(y) + m * N + nb) =
+                    make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                               pack_bf16x2(v[6], v[7]));
+            else {
+                float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(y) + m * N + nb);
+                o[0] = make_float4(v[0], v[1], v[2], v[3]);
+                o[1] = make_float4(v[4], v[5], v[6], v[7]);
             }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (nb + e < N) {
+                    if (OUT_BF16)
+                        static_cast<uint16_t *>(y)[m * N + nb + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                    else
+                        static_cast<float *>(y)[m * N + nb + e] = v[e];
+                }
+        }
     }
 }
 
 template <int G, bool SYM>
 hipError_t w4a8_go(const W4A8Args &a, hipStream_t st)
 {
-    constexpr int kBN = W4A8Tile<G>::BN;
     const int64_t tiles = ((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM);
+    if (tiles > (int64_t)0x7FFFFFF0)
+        return hipErrorInvalidValue;
     const int64_t per = (tiles + kW8Xcds - 1) / kW8Xcds;
     const dim3 grid((unsigned)(per * kW8Xcds)), block(kThreads);
     if (a.y_bf16)
