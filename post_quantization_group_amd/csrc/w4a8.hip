@@ -23,6 +23,8 @@
 //     the zero point is subtracted from all four bytes at once (each byte is >= 0x80 > z, so no borrow
 //     crosses a byte); removing the bias leaves the signed byte q - z in [-15, 15].
 //   * A wave computes 128 tokens x 32 channels (four MFMA tiles share each unpacked weight operand).
+//   * The folds are software-pipelined against the MFMAs (see multiply below), so that the VALU converts
+//     one tile while the matrix core multiplies another, instead of each fold waiting for its MFMAs.
 // Which codes one MFMA sums is free as long as A and B agree; what matters is that every MFMA lies inside one
 // group. A step's 128 codes are two pairs of 64 codes, each pair two MFMAs. For g = 64 and 128 a pair lies
 // inside one group and lane half h takes the pair's codes 32 h .. 32 h + 31 (one 16-byte read of packed
@@ -178,49 +180,78 @@ __global__ __launch_bounds__(kThreads, 2) void k_w4a8(const int8_t *__restrict__
             acc[j][e] = 0;
             facc[j][e] = 0.0f;
         }
-    // add a finished group into the fp32 accumulators and restart the integer ones
-    auto fold = [&](float sc) __attribute__((always_inline)) {
+    // Part p of np of the fold of tile j's finished group: its 16 / np accumulators converted and added to the
+    // fp32 ones with the group scale.
+    auto fold_part = [&](int j, float sc, int p, int np) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < kTM; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                facc[j][e] = __builtin_fmaf(sc, (float)acc[j][e], facc[j][e]);
-                acc[j][e] = 0;
-            }
+        for (int e = p * (16 / np); e < (p + 1) * (16 / np); ++e)
+            facc[j][e] = __builtin_fmaf(sc, (float)acc[j][e], facc[j][e]);
     };
 
+    // Depth d = 2 q + e of a step: pair q, MFMA e. Its activation piece holds the same 16 codes per lane half
+    // as its B operand.
+    auto xpiece = [&](int d) __attribute__((always_inline)) {
+        const int q = d / 2, e = d % 2;
+        return G == 32 ? 4 * q + 2 * e + h : 4 * q + 2 * h + e;
+    };
     const int wrow = w * kWN + col;  // the lane's weight row in a stage
+    // Work unit u = (group gi, token tile j) of a step: the group's DPG MFMAs on tile j. The fold of unit u - L
+    // is split over them, one part after each MFMA, so the VALU converts while the matrix core multiplies.
+    // The lag L keeps the folded accumulators a whole unit away from the MFMA that wrote them (a fold right
+    // behind its MFMA waits for it); L < 4 still folds a tile before the unit that reuses it. The last L
+    // units of a step are folded by the first L units of the next step (all in the step's last group).
+    constexpr int kUnits = GPS * kTM;
+    constexpr int L = DPG == 1 ? 3 : 2;
+    static_assert(L < kTM && L <= kTM, "pending units lie in one group");
+    float pend_s = 0.0f;  // group scale of the pending folds; 0 before the first step (accumulators are 0)
     auto multiply = [&](const int8_t *st, const Meta &md) __attribute__((always_inline)) {
         const int8_t *ws = st + kXBytes;
+        v4i fb[4];  // the step's four B operands
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {  // pair q: codes 64 q .. 64 q + 63 of the step
-            v4i fb[2];
-            if constexpr (G == 32) {  // MFMA e is group 2 q + e: packed piece 2 q + e, its half h
+        for (int q = 0; q < 2; ++q) {
+            if constexpr (G == 32) {  // depth 2 q + e is group 2 q + e: packed piece 2 q + e, its half h
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const uint2 pc = *reinterpret_cast<const uint2 *>(ws + woff(wrow, 2 * q + e) + 8 * h);
-                    fb[e] = SYM ? unpack_sym(pc.x, pc.y) : unpack_asym(pc.x, pc.y, md.zz[2 * q + e]);
+                    fb[2 * q + e] = SYM ? unpack_sym(pc.x, pc.y) : unpack_asym(pc.x, pc.y, md.zz[2 * q + e]);
                 }
-            } else {  // the pair lies in group (2 q) / DPG: packed piece 2 q + h, MFMA e its half e
+            } else {  // pair q lies in group (2 q) / DPG: packed piece 2 q + h, depth 2 q + e its half e
                 const v4i pc = *reinterpret_cast<const v4i *>(ws + woff(wrow, 2 * q + h));
                 const uint32_t zz = md.zz[(2 * q) / DPG];
-                fb[0] = SYM ? unpack_sym(pc[0], pc[1]) : unpack_asym(pc[0], pc[1], zz);
-                fb[1] = SYM ? unpack_sym(pc[2], pc[3]) : unpack_asym(pc[2], pc[3], zz);
-            }
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int xp = G == 32 ? 4 * q + 2 * e + h : 4 * q + 2 * h + e;  // same 16 codes as fb[e]
-                v4i fa[kTM];
-#pragma unroll
-                for (int j = 0; j < kTM; ++j)
-                    fa[j] = *reinterpret_cast<const v4i *>(st + xoff(j * 32 + col, xp));
-#pragma unroll
-                for (int j = 0; j < kTM; ++j)
-                    acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[j], fb[e], acc[j], 0, 0, 0);
-                if ((2 * q + e + 1) % DPG == 0)  // depth 2 q + e ends its group
-                    fold(md.s[(2 * q + e) / DPG]);
+                fb[2 * q] = SYM ? unpack_sym(pc[0], pc[1]) : unpack_asym(pc[0], pc[1], zz);
+                fb[2 * q + 1] = SYM ? unpack_sym(pc[2], pc[3]) : unpack_asym(pc[2], pc[3], zz);
             }
         }
+        auto read_unit = [&](v4i *f, int u) __attribute__((always_inline)) {
+            const int gi = u / kTM, j = u % kTM;
+#pragma unroll
+            for (int dd = 0; dd < DPG; ++dd)
+                f[dd] = *reinterpret_cast<const v4i *>(st + xoff(j * 32 + col, xpiece(gi * DPG + dd)));
+        };
+        v4i fcur[DPG], fnxt[DPG];
+        read_unit(fcur, 0);
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const int gi = u / kTM, j = u % kTM;
+            const int pu = u - L;                             // the unit folded now (< 0: previous step)
+            const int pj = (pu + kUnits) % kTM;
+            const float ps = pu < 0 ? pend_s : md.s[pu / kTM];
+            if (u + 1 < kUnits)
+                read_unit(fnxt, u + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dd = 0; dd < DPG; ++dd) {
+                const v16i c = dd == 0 ? v16i{} : acc[j];
+                acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fcur[dd], fb[gi * DPG + dd], c, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                fold_part(pj, ps, dd, DPG);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int dd = 0; dd < DPG; ++dd)
+                fcur[dd] = fnxt[dd];
+        }
+        pend_s = md.s[GPS - 1];
     };
 
     Meta mcur, mnxt;
@@ -248,6 +279,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_w4a8(const int8_t *__restrict__
         step(s0, s2, k);
     if (k + 1 < nsteps)
         step(s1, s0, k + 1);
+#pragma unroll
+    for (int u = kUnits - L; u < kUnits; ++u)  // the last step's pending folds
+        fold_part(u % kTM, pend_s, 0, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no direct load may land in the stages reused below
     __syncthreads();
 
