@@ -11,7 +11,7 @@ Sources, by page title and section:
   [P2] "模型压缩：量化、ZeroQuant、LLM.int8() 与 SmoothQuant": §3 basic formula; §4 granularity;
        §11 vector-wise scales; §12-13 SmoothQuant and alpha.
   [P3] "第11章 模型量化与压缩": §11.1.1-§11.1.6 affine quantization, granularity, worked INT4 example;
-       §11.4.3-§11.4.5 smoothing factor and W8A8 pipeline.
+       §11.4.3-§11.4.5 smoothing factor and W8A8 pipeline; §11.6.2-§11.6.5 KV-cache quantization.
   [P5] "大模型压缩：从研究到生产的完整攻略（1）": symmetric / asymmetric worked examples; outliers.
 """
 from __future__ import annotations
@@ -63,6 +63,10 @@ def _load():
         lib.or_fold_smoothing_bf16.restype = None
         lib.or_w4a8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, P]
         lib.or_w4a8.restype = I32
+        lib.or_kv_keys.argtypes = [P, I32, I64, I64, I64, I32, P, P, P]
+        lib.or_kv_keys.restype = I32
+        lib.or_kv_dequant_keys.argtypes = [P, P, P, I64, I64, I64, P, P]
+        lib.or_kv_dequant_keys.restype = I32
         lib.or_dequantize.restype = I32
         lib.or_pack_int4.argtypes = [P, I64, I64, P]
         lib.or_pack_int4.restype = I32
@@ -309,3 +313,70 @@ def w4a8_pipeline(x_bf16, w_bf16, alpha: float, group_size: int, symmetric: bool
     q_x, s_x, _ = quantize(x_bf16, 8, True, ROW, smooth=s, smooth_mode=SMOOTH_DIV)
     y = w4a8(q_x.astype(np.int8), s_x, q_w, s_w, z_w, group_size)
     return {"s": s, "q_w": q_w, "s_w": s_w, "z_w": z_w, "q_x": q_x.astype(np.int8), "s_x": s_x, "y": y}
+
+
+# ---------------------------------------------------------------- KV cache
+
+
+def kv_quantize_keys(k, block_tokens: int, symmetric: bool):
+    """Keys per channel over blocks of block_tokens consecutive tokens [P3 §11.6.3-§11.6.5]: k [tokens, channels]
+    -> (codes int32 [tokens, channels], scales float32 [tokens / T, channels], zeros uint8 same shape or None)."""
+    x, dt = _float_input(k)
+    tokens, channels = x.shape
+    nb = tokens // block_tokens if block_tokens > 0 else 0
+    q = np.zeros((tokens, channels), np.int32)
+    s = np.zeros((nb, channels), np.float32)
+    z = None if symmetric else np.zeros((nb, channels), np.uint8)
+    if _load().or_kv_keys(_ptr(x), dt, tokens, channels, block_tokens, int(bool(symmetric)), _ptr(q), _ptr(s),
+                          _ptr(z)) != 0:
+        raise ValueError("block_tokens must divide the token count")
+    return q, s, z
+
+
+def kv_dequantize_keys(q, scales, zeros, block_tokens: int):
+    """x_hat[t, c] = s[t / T, c] (q[t, c] - z[t / T, c]). Returns (fp32 values, their bf16 rounding as uint16)."""
+    q = np.ascontiguousarray(q, dtype=np.int32)
+    tokens, channels = q.shape
+    out32 = np.empty((tokens, channels), np.float32)
+    out16 = np.empty((tokens, channels), np.uint16)
+    z = None if zeros is None else np.ascontiguousarray(zeros, dtype=np.uint8)
+    if _load().or_kv_dequant_keys(_ptr(q), _ptr(np.ascontiguousarray(scales, np.float32)), _ptr(z), tokens, channels,
+                                  block_tokens, _ptr(out32), _ptr(out16)) != 0:
+        raise ValueError("block_tokens must divide the token count")
+    return out32, out16
+
+
+def kv_append(cache, k_new, v_new, positions, block_tokens: int, v_group_size: int, symmetric: bool):
+    """One online append step of a KV cache [P3 §11.6.2: the cache is quantized online, a few new tokens per
+    step; §11.6.5: KIVI's grouped on-demand quantization keeps the most recent keys at full precision and
+    quantizes a group of T keys per channel once it is complete, values per token on arrival].
+
+    cache: dict of numpy arrays, updated in place, for B sequences of at most S tokens and C channels:
+      k_res [B, T, C] (the keys of the incomplete group, as given), k_q [B, S, C], k_s / k_z [B, S / T, C],
+      v_q [B, S, C], v_s / v_z [B, S, nv] (nv = 1 per token, or C / v_group_size per group).
+    k_new, v_new: [B, C] (bf16 as uint16, or fp32); positions: [B], the token index each sequence appends at.
+    A sequence whose position lies outside [0, S) is skipped.
+    Values: quantize(v_new[b], per row or per group) -> v_q[b, p], v_s[b, p]. Keys: k_new[b] goes to slot
+    p % T of k_res[b]; when p % T == T - 1 the group is complete and is quantized per channel into rows
+    [p - T + 1, p] of k_q[b] and block p / T of k_s[b]."""
+    B, C = k_new.shape
+    S = cache["k_q"].shape[1]
+    for b in range(B):
+        p = int(positions[b])
+        if p < 0 or p >= S:
+            continue
+        if v_group_size:
+            vq, vs, vz = quantize(v_new[b:b + 1], 8, symmetric, GROUP, v_group_size)
+        else:
+            vq, vs, vz = quantize(v_new[b:b + 1], 8, symmetric, ROW)
+        cache["v_q"][b, p] = vq[0]
+        cache["v_s"][b, p] = vs
+        if not symmetric:
+            cache["v_z"][b, p] = vz
+        cache["k_res"][b, p % block_tokens] = k_new[b]
+        if p % block_tokens == block_tokens - 1:
+            kq, ks, kz = kv_quantize_keys(cache["k_res"][b], block_tokens, symmetric)
+            cache["k_q"][b, p - block_tokens + 1:p + 1] = kq
+            cache["k_s"][b, p // block_tokens] = ks[0]
+            if not symmetric:
+                cache["k_z"][b, p // block_tokens] = kz[0]

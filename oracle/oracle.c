@@ -274,6 +274,71 @@ static int64_t segment_of(int64_t i, int64_t cols, int granularity, int group_si
     return i / group_size; /* groups are contiguous in row-major order because cols % group_size == 0 */
 }
 
+/* ---------------------------------------------------------------- KV cache */
+
+/*
+ * Keys of a KV cache, INT8 per channel over blocks of consecutive tokens [P3 §11.6.3: per-channel granularity,
+ * one scale per head-dimension channel; §11.6.4: K's outliers sit in a few channels, so K takes per-channel
+ * scales; §11.6.5: KIVI quantizes K per channel within groups of tokens]. x is token-major [tokens, channels]
+ * (one layer's keys, all heads side by side); block b holds tokens [b T, (b + 1) T). For each block and
+ * channel: the range of the channel's T values, (s, z) as for any segment, codes clamp(round(x / s) + z).
+ * Outputs (caller-allocated): q[tokens * channels] unpacked, scales[tokens / T * channels] and zeros (NULL
+ * when symmetric), indexed [block][channel].
+ * Returns 0, or -1 when T does not divide the token count.
+ */
+int or_kv_keys(const void *x, int x_dtype, int64_t tokens, int64_t channels, int64_t block_tokens, int symmetric,
+               int32_t *q, float *scales, uint8_t *zeros)
+{
+    if (block_tokens <= 0 || tokens % block_tokens != 0 || channels <= 0)
+        return -1;
+    int64_t nseg = tokens / block_tokens * channels;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < nseg; ++e) {
+        int64_t b = e / channels, c = e % channels;
+        int64_t t0 = b * block_tokens, t1 = t0 + block_tokens;
+        float absmax = 0.0f, lo = 0.0f, hi = 0.0f;
+        for (int64_t t = t0; t < t1; ++t) {
+            float v = load_elem(x, x_dtype, t * channels + c);
+            float a = fabsf(v);
+            if (a > absmax)
+                absmax = a;
+            if (t == t0 || v < lo)
+                lo = v;
+            if (t == t0 || v > hi)
+                hi = v;
+        }
+        seg_params p = segment_params(absmax, lo, hi, 8, symmetric);
+        scales[e] = p.s;
+        if (zeros)
+            zeros[e] = (uint8_t)p.z;
+        for (int64_t t = t0; t < t1; ++t)
+            q[t * channels + c] = quantize_one(load_elem(x, x_dtype, t * channels + c), p);
+    }
+    return 0;
+}
+
+/* Keys back from their per-channel codes: x_hat[t, c] = s[b, c] (q[t, c] - z[b, c]), b = t / T, one fp32
+ * multiply; fp32 values and their bf16 rounding, as or_dequantize. */
+int or_kv_dequant_keys(const int32_t *q, const float *scales, const uint8_t *zeros, int64_t tokens, int64_t channels,
+                       int64_t block_tokens, float *out_f32, uint16_t *out_bf16)
+{
+    if (block_tokens <= 0 || tokens % block_tokens != 0)
+        return -1;
+    int64_t n = tokens * channels;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = i / channels, c = i % channels;
+        int64_t e = t / block_tokens * channels + c;
+        int z = zeros ? (int)zeros[e] : 0;
+        float v = scales[e] * (float)(q[i] - z);
+        if (out_f32)
+            out_f32[i] = v;
+        if (out_bf16)
+            out_bf16[i] = or_f32_to_bf16(v);
+    }
+    return 0;
+}
+
 /* x_hat = s (q - z), one fp32 multiply [P1 core formula; P2 §3; P3 §11.1.1].
  * Writes fp32 values to out_f32 if non-NULL and their bf16 rounding to out_bf16 if non-NULL. */
 int or_dequantize(const int32_t *q, const float *scales, const uint8_t *zeros, int64_t rows, int64_t cols,

@@ -577,3 +577,105 @@ def test_w4a8_pipeline_approximates_float_product():
     for sym in (True, False):
         r = oracle.w4a8_pipeline(d["x"], d["w"], 0.5, 128, sym)
         assert np.linalg.norm(r["y"] - y_true) / np.linalg.norm(y_true) < 0.2
+
+
+# ---------------------------------------------------------------- KV cache (P3 §11.6)
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_kv_keys_are_row_quantization_of_each_block_transposed(sym):
+    """Per-channel over a block of T tokens is per-row quantization of the block's transpose (the pinned
+    per-row quantizer), block by block: codes, scales and zeros identical."""
+    d = workloads.kv_cache(96, 64, outlier_channels=4)
+    q, s, z = oracle.kv_quantize_keys(d["k"], 32, sym)
+    for b in range(3):
+        blk = np.ascontiguousarray(d["k"][32 * b:32 * b + 32].T)
+        qr, sr, zr = oracle.quantize(blk, 8, sym, oracle.ROW)
+        assert np.array_equal(q[32 * b:32 * b + 32], qr.T)
+        assert np.array_equal(s[b].view(np.uint32), sr.view(np.uint32))
+        if not sym:
+            assert np.array_equal(z[b], zr)
+
+
+def test_kv_keys_channels_are_independent():
+    """Scaling one channel by a power of two scales its block scales by the same power and leaves its codes
+    and every other channel unchanged: an outlier channel does not widen the others' steps."""
+    d = workloads.kv_cache(64, 32, outlier_channels=0)
+    k = workloads.bf16_to_f32(d["k"])
+    k2 = k.copy()
+    k2[:, 5] *= np.float32(64.0)
+    q1, s1, _ = oracle.kv_quantize_keys(k, 32, True)
+    q2, s2, _ = oracle.kv_quantize_keys(k2, 32, True)
+    assert np.array_equal(q1, q2)
+    others = [c for c in range(32) if c != 5]
+    assert np.array_equal(s1[:, others], s2[:, others])
+    assert np.array_equal(s2[:, 5], s1[:, 5] * np.float32(64.0))
+
+
+def test_kv_keys_range_and_error_bound():
+    """Symmetric: each (block, channel)'s absolute maximum codes to +-127, every code lies in [-127, 127], and
+    dequantization is within s/2 of the input (no clipping). Asymmetric: codes span [0, 255] per segment with
+    the error bound on unclamped elements [P1 core formula; P3 §11.1.1]."""
+    d = workloads.kv_cache(128, 48, outlier_channels=3)
+    k = workloads.bf16_to_f32(d["k"])
+    q, s, _ = oracle.kv_quantize_keys(d["k"], 64, True)
+    assert q.min() >= -127 and q.max() <= 127
+    for b in range(2):
+        blk = q[64 * b:64 * b + 64]
+        assert np.array_equal(np.abs(blk).max(axis=0), np.full(48, 127))
+    xh, _ = oracle.kv_dequantize_keys(q, s, None, 64)
+    bound = np.repeat(s, 64, axis=0).astype(np.float64) / 2
+    slack = np.abs(k).astype(np.float64) * 2.0 ** -22  # fp32 rounding of x / s and of s q
+    assert np.all(np.abs(xh.astype(np.float64) - k) <= bound + slack)
+    qa, sa, za = oracle.kv_quantize_keys(d["k"], 64, False)
+    assert qa.min() >= 0 and qa.max() <= 255
+    xa, _ = oracle.kv_dequantize_keys(qa, sa, za, 64)
+    inner = (qa > 0) & (qa < 255)
+    ba = np.repeat(sa, 64, axis=0).astype(np.float64) / 2
+    assert np.all((np.abs(xa.astype(np.float64) - k) <= ba + slack + ba * 2.0 ** -20)[inner])
+
+
+def _empty_cache(B, S, C, T, nv, sym):
+    c = {"k_res": np.zeros((B, T, C), np.uint16), "k_q": np.zeros((B, S, C), np.int32),
+         "k_s": np.zeros((B, S // T, C), np.float32), "v_q": np.zeros((B, S, C), np.int32),
+         "v_s": np.zeros((B, S, nv), np.float32)}
+    if not sym:
+        c["k_z"] = np.zeros((B, S // T, C), np.uint8)
+        c["v_z"] = np.zeros((B, S, nv), np.uint8)
+    return c
+
+
+@pytest.mark.parametrize("sym,vg", [(True, 0), (False, 32)])
+def test_kv_append_online_equals_bulk(sym, vg):
+    """Appending tokens one step at a time [P3 §11.6.2, §11.6.5] gives the cache that bulk quantization of the
+    same tokens gives: complete key groups per channel, values per token (or group); the incomplete group's
+    keys wait at full precision in the residual slots; positions outside the cache are skipped."""
+    B, S, C, T = 3, 96, 64, 32
+    d = workloads.kv_cache(B * S, C, outlier_channels=4)
+    ks, vs = d["k"].reshape(B, S, C), d["v"].reshape(B, S, C)
+    n_tok = [S, 70, 33]  # tokens each sequence ends with
+    nv = C // vg if vg else 1
+    cache = _empty_cache(B, S, C, T, nv, sym)
+    for step in range(S + 2):
+        pos = np.array([step if step < n_tok[b] else (S + 5 if b == 0 else -1) for b in range(B)])
+        kn = np.stack([ks[b, min(step, S - 1)] for b in range(B)])
+        vn = np.stack([vs[b, min(step, S - 1)] for b in range(B)])
+        oracle.kv_append(cache, kn, vn, pos, T, vg, sym)
+    for b in range(B):
+        n = n_tok[b]
+        full = n // T * T
+        if full:
+            q, s, z = oracle.kv_quantize_keys(ks[b, :full], T, sym)
+            assert np.array_equal(cache["k_q"][b, :full], q)
+            assert np.array_equal(cache["k_s"][b, :full // T], s)
+            if not sym:
+                assert np.array_equal(cache["k_z"][b, :full // T], z)
+        assert not cache["k_q"][b, full:].any()
+        assert np.array_equal(cache["k_res"][b, :n - full], ks[b, full:n])
+        gran = oracle.GROUP if vg else oracle.ROW
+        qv, sv, zv = oracle.quantize(vs[b, :n], 8, sym, gran, vg)
+        assert np.array_equal(cache["v_q"][b, :n], qv)
+        assert np.array_equal(cache["v_s"][b, :n].ravel(), sv)
+        if not sym:
+            assert np.array_equal(cache["v_z"][b, :n].ravel(), zv)
+        assert not cache["v_q"][b, n:].any()

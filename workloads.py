@@ -23,7 +23,7 @@ import numpy as np
 SEED = 0
 
 # configuration ids (used only to separate generator streams)
-TINY, ATTN7B, FFN7B, W8A8, L70B = 1, 2, 3, 4, 5
+TINY, ATTN7B, FFN7B, W8A8, L70B, KV = 1, 2, 3, 4, 5, 6
 
 # Llama-70B-shaped decoder layer: (name, d_out, d_in) in draw order
 L70B_PROJ = [
@@ -157,6 +157,20 @@ def l70b_x(i: int, m: int) -> np.ndarray:
     return activations(L70B, 20 + i, m, k)
 
 
+KV_CHANNELS = 1024  # one layer's keys (or values) per token: 8 KV heads x head_dim 128 (Llama-3-70B)
+
+
+def kv_cache(tokens: int, channels: int = KV_CHANNELS, outlier_channels: int = 16):
+    """One layer's keys and values for `tokens` cached tokens (all sequences' tokens stacked), token-major
+    [tokens, channels], bf16: N(0, 1); the keys' outliers sit in `outlier_channels` channels (x10), the values
+    have none. Drawn in blocks of ROW_BLOCK tokens, one generator each."""
+    k = blocked_normal(KV, 1, tokens, channels, 1.0)
+    chans = np.sort(rng(KV, 3).choice(channels, size=min(outlier_channels, channels), replace=False))
+    k[:, chans] *= np.float32(10.0)
+    v = blocked_normal(KV, 2, tokens, channels, 1.0)
+    return {"k": bf16_bits(k), "v": bf16_bits(v), "outlier_chans": chans}
+
+
 def describe() -> dict:
     return {
         "generator": "numpy PCG64, default_rng([0, config, tensor]), standard_normal(float32)",
@@ -167,4 +181,5 @@ def describe() -> dict:
         "w8a8": "X bf16 2048x4096 N(0,1), 41 channels x50; W bf16 11008x4096 N(0,0.02)",
         "l70b": "q,k,v,o,gate,up,down bf16 N(0,0.02) (8192x8192, 1024x8192 x2, 8192x8192, 28672x8192 x2, "
                 "8192x28672); x bf16 [M,d_in], M in {1,8,32}",
+        "kv": "one layer's K and V bf16 [tokens, 1024] N(0,1); 16 key channels x10",
     }
