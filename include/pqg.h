@@ -219,6 +219,61 @@ int32_t pqg_qlinear_w4a8(const int8_t *x_q, const float *x_scales, int64_t M, in
                          const uint8_t *w_packed, const float *w_scales, const uint8_t *w_zeros, int32_t group_size,
                          int32_t symmetric, void *y, int32_t y_dtype, void *stream);
 
+/*
+ * KV cache, keys: INT8 per channel over groups of block_tokens consecutive tokens
+ * [P3 §11.6.3 (per-channel granularity: one scale per head-dimension channel); §11.6.4 (the outliers of K sit
+ * in a few channels, so K takes per-channel scales); §11.6.5 (KIVI: K per channel within groups of tokens)].
+ * For token group b = t / T and channel c: (s, z) from the range of k[bT .. bT + T - 1, c] (symmetric:
+ * s = max|k| / 127; asymmetric: range widened to contain 0, s = (hi - lo) / 255, z = clamp(rne(-lo / s))),
+ * codes clamp(rne(k / s) + z) -- the same arithmetic as pqg_quantize.
+ *   k        : [tokens, channels] token-major, bf16 or fp32 (k_dtype); one layer's keys, heads side by side.
+ *   codes    : int8 (symmetric) or uint8 [tokens, channels] (out).
+ *   scales   : fp32 [tokens / T, channels] (out); zeros: uint8, same shape, NULL iff symmetric (out).
+ *   block_tokens T in {32, 64, 128, 256}; tokens % T == 0 (the tokens of an incomplete group stay at full
+ *   precision with the caller, see pqg_kv_append); channels % 64 == 0.
+ * Alignment: k 16 bytes, codes 8, scales 4.
+ */
+int32_t pqg_kv_quantize_keys(const void *k, int32_t k_dtype, int64_t tokens, int64_t channels, int32_t block_tokens,
+                             int32_t symmetric, void *codes, float *scales, uint8_t *zeros, void *stream);
+
+/*
+ * KV cache, keys back: out[t, c] = s[t / T, c] * (q[t, c] - z[t / T, c]), one fp32 multiply, then rounded to
+ * out_dtype [P1 core formula; P3 §11.1.1].
+ *   codes / scales / zeros as pqg_kv_quantize_keys writes them; out [tokens, channels] of out_dtype.
+ *   tokens % T == 0; channels % 8 == 0. Alignment: codes 8 bytes, scales 4, out 16.
+ * Values (per token or per group) come back with pqg_dequantize (PQG_ROW or PQG_GROUP, bits 8).
+ */
+int32_t pqg_kv_dequantize_keys(const void *codes, const float *scales, const uint8_t *zeros, int64_t tokens,
+                               int64_t channels, int32_t block_tokens, int32_t symmetric, void *out, int32_t out_dtype,
+                               void *stream);
+
+/*
+ * KV cache, one online append step for a batch of sequences, each appending one token
+ * [P3 §11.6.2 (the cache is made during decoding, so it is quantized online, a few tokens per step);
+ * §11.6.3 (per-token scales for V); §11.6.5 (KIVI's grouped on-demand quantization: the most recent keys stay
+ * at full precision, and a complete group of T keys is quantized per channel)].
+ * For each sequence b with 0 <= p = positions[b] < max_tokens (others are skipped):
+ *   values: v_new[b] is quantized to INT8, one scale per token (v_group_size = 0) or per group of
+ *     v_group_size channels (e.g. one head), into row p: v_codes[b, p, :], v_scales[b, p, :], v_zeros[b, p, :];
+ *   keys: k_new[b] is copied to residual slot p % T of k_residual[b]; when p % T == T - 1 the group of tokens
+ *     p - T + 1 .. p is complete and is quantized per channel (as pqg_kv_quantize_keys) into rows
+ *     p - T + 1 .. p of k_codes[b] and group p / T of k_scales[b] (k_zeros[b]).
+ *   k_new, v_new : [batch, channels], bf16 or fp32 (dtype); positions: int64 [batch], device memory.
+ *   k_residual   : [batch, T, channels] of dtype (in/out, caller-owned; slots hold the keys not yet quantized).
+ *   k_codes      : int8 / uint8 [batch, max_tokens, channels]; k_scales fp32 [batch, max_tokens / T, channels];
+ *   k_zeros      : uint8 like k_scales, NULL iff symmetric.
+ *   v_codes      : int8 / uint8 [batch, max_tokens, channels]; v_scales fp32 [batch, max_tokens, nv] with
+ *                  nv = 1 or channels / v_group_size; v_zeros uint8 like v_scales, NULL iff symmetric.
+ *   block_tokens T in {32, 64, 128, 256}; max_tokens % T == 0; v_group_size in {0, 32, 64, 128};
+ *   channels % 8 == 0 (and % v_group_size), channels <= 8192.
+ * Alignment: k_new, v_new, k_residual 16 bytes; positions, codes 8; scales 4. One block per sequence: a step's
+ * cost is one row of values and keys per sequence, plus T rows of keys for each sequence whose group completes.
+ */
+int32_t pqg_kv_append(const void *k_new, const void *v_new, int32_t dtype, int64_t batch, int64_t channels,
+                      const int64_t *positions, int64_t max_tokens, int32_t block_tokens, int32_t v_group_size,
+                      int32_t symmetric, void *k_residual, void *k_codes, float *k_scales, uint8_t *k_zeros,
+                      void *v_codes, float *v_scales, uint8_t *v_zeros, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

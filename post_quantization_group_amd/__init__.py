@@ -30,7 +30,7 @@ EXPORTS = [
     "pqg_abi_version", "pqg_last_error", "pqg_quantize_workspace_bytes", "pqg_quantize", "pqg_quantize_static",
     "pqg_dequantize",
     "pqg_smooth_workspace_bytes", "pqg_smooth", "pqg_qlinear_w4a16", "pqg_qlinear_w8a8", "pqg_gemm_s8s8s32",
-    "pqg_qlinear_w4a8",
+    "pqg_qlinear_w4a8", "pqg_kv_quantize_keys", "pqg_kv_dequantize_keys", "pqg_kv_append",
 ]
 
 _lib = None
@@ -76,6 +76,12 @@ def load(path: str = LIB_PATH):
     lib.pqg_gemm_s8s8s32.argtypes = [P, P, I64, I64, I64, P, P]
     lib.pqg_qlinear_w4a8.restype = I32
     lib.pqg_qlinear_w4a8.argtypes = [P, P, I64, I64, I64, P, P, P, I32, I32, P, I32, P]
+    lib.pqg_kv_quantize_keys.restype = I32
+    lib.pqg_kv_quantize_keys.argtypes = [P, I32, I64, I64, I32, I32, P, P, P, P]
+    lib.pqg_kv_dequantize_keys.restype = I32
+    lib.pqg_kv_dequantize_keys.argtypes = [P, P, P, I64, I64, I32, I32, P, I32, P]
+    lib.pqg_kv_append.restype = I32
+    lib.pqg_kv_append.argtypes = [P, P, I32, I64, I64, P, I64, I32, I32, I32, P, P, P, P, P, P, P, P]
     if lib.pqg_abi_version() != ABI_VERSION:
         raise ImportError("libpqg.so ABI %d != binding ABI %d" % (lib.pqg_abi_version(), ABI_VERSION))
     _lib = lib
@@ -269,3 +275,68 @@ def qlinear_w4a8(x_q: torch.Tensor, x_scales: torch.Tensor, w_packed: torch.Tens
     _check(lib.pqg_qlinear_w4a8(_ptr(x_q), _ptr(x_scales), M, N, K, _ptr(w_packed), _ptr(w_scales), _ptr(w_zeros),
                                 group_size, int(symmetric), _ptr(y), _float_dtype(y), _stream(dev)))
     return y
+
+
+def kv_quantize_keys(k: torch.Tensor, block_tokens: int, symmetric: bool, out=None):
+    """pqg_kv_quantize_keys: keys [tokens, channels] per channel over groups of block_tokens tokens. Returns
+    (codes [tokens, channels] int8 / uint8, scales [tokens / T, channels], zeros or None); `out` may hold
+    preallocated (codes, scales, zeros)."""
+    lib = load()
+    dev = _dev(k)
+    tokens, channels = k.shape
+    if out is None:
+        codes = torch.empty((tokens, channels), dtype=torch.int8 if symmetric else torch.uint8, device=dev)
+        scales = torch.empty((tokens // block_tokens, channels), dtype=torch.float32, device=dev)
+        zeros = None if symmetric else torch.empty((tokens // block_tokens, channels), dtype=torch.uint8, device=dev)
+    else:
+        codes, scales, zeros = out
+    _check(lib.pqg_kv_quantize_keys(_ptr(k), _float_dtype(k), tokens, channels, block_tokens, int(symmetric),
+                                    _ptr(codes), _ptr(scales), _ptr(zeros), _stream(dev)))
+    return codes, scales, zeros
+
+
+def kv_dequantize_keys(codes: torch.Tensor, scales: torch.Tensor, zeros, block_tokens: int, symmetric: bool,
+                       out_dtype=torch.bfloat16, out=None):
+    """pqg_kv_dequantize_keys -> [tokens, channels] of out_dtype."""
+    lib = load()
+    dev = _dev(codes)
+    tokens, channels = codes.shape
+    if out is None:
+        out = torch.empty((tokens, channels), dtype=out_dtype, device=dev)
+    _check(lib.pqg_kv_dequantize_keys(_ptr(codes), _ptr(scales), _ptr(zeros), tokens, channels, block_tokens,
+                                      int(symmetric), _ptr(out), _float_dtype(out), _stream(dev)))
+    return out
+
+
+def kv_cache_alloc(batch: int, max_tokens: int, channels: int, block_tokens: int, v_group_size: int,
+                   symmetric: bool, dtype=torch.bfloat16, device="cuda"):
+    """Zero-filled cache tensors for kv_append: k_res [B, T, C] of dtype; k_q, v_q [B, S, C] int8 / uint8;
+    k_s [B, S / T, C]; v_s [B, S, nv] (nv = 1 per token, else C / v_group_size); k_z / v_z or None."""
+    cd = torch.int8 if symmetric else torch.uint8
+    nv = channels // v_group_size if v_group_size else 1
+    c = {"k_res": torch.zeros((batch, block_tokens, channels), dtype=dtype, device=device),
+         "k_q": torch.zeros((batch, max_tokens, channels), dtype=cd, device=device),
+         "k_s": torch.zeros((batch, max_tokens // block_tokens, channels), dtype=torch.float32, device=device),
+         "v_q": torch.zeros((batch, max_tokens, channels), dtype=cd, device=device),
+         "v_s": torch.zeros((batch, max_tokens, nv), dtype=torch.float32, device=device),
+         "k_z": None, "v_z": None}
+    if not symmetric:
+        c["k_z"] = torch.zeros((batch, max_tokens // block_tokens, channels), dtype=torch.uint8, device=device)
+        c["v_z"] = torch.zeros((batch, max_tokens, nv), dtype=torch.uint8, device=device)
+    return c
+
+
+def kv_append(cache: dict, k_new: torch.Tensor, v_new: torch.Tensor, positions: torch.Tensor, block_tokens: int,
+              v_group_size: int, symmetric: bool):
+    """pqg_kv_append: one online step; k_new / v_new [B, C], positions int64 [B] on the device; `cache` as
+    kv_cache_alloc returns it (updated in place)."""
+    lib = load()
+    dev = _dev(k_new)
+    if positions.dtype != torch.int64 or positions.device != k_new.device:
+        raise TypeError("positions must be an int64 tensor on the same device")
+    B, C = k_new.shape
+    S = cache["k_q"].shape[1]
+    _check(lib.pqg_kv_append(_ptr(k_new), _ptr(v_new), _float_dtype(k_new), B, C, _ptr(positions), S, block_tokens,
+                             v_group_size, int(symmetric), _ptr(cache["k_res"]), _ptr(cache["k_q"]),
+                             _ptr(cache["k_s"]), _ptr(cache["k_z"]), _ptr(cache["v_q"]), _ptr(cache["v_s"]),
+                             _ptr(cache["v_z"]), _stream(dev)))

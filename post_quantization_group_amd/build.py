@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpqg.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "smooth.hip", "w4a16.hip", "gemm_i8.hip", "w4a8.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "smooth.hip", "w4a16.hip", "gemm_i8.hip", "w4a8.hip", "kv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -314,4 +314,101 @@ int32_t pqg_qlinear_w4a8(const int8_t *x_q, const float *x_scales, int64_t M, in
     return hip_status(pqg::launch_w4a8(a, as_stream(stream)), "pqg_qlinear_w4a8 launch");
 }
 
+int32_t pqg_kv_quantize_keys(const void *k, int32_t k_dtype, int64_t tokens, int64_t channels, int32_t block_tokens,
+                             int32_t symmetric, void *codes, float *scales, uint8_t *zeros, void *stream)
+{
+    g_err[0] = 0;
+    if (!valid_float_dtype(k_dtype))
+        return fail(PQG_EINVAL, "unknown k_dtype %d", k_dtype);
+    if (block_tokens != 32 && block_tokens != 64 && block_tokens != 128 && block_tokens != 256)
+        return fail(PQG_EINVAL, "block_tokens must be 32, 64, 128 or 256 (got %d)", block_tokens);
+    if (tokens < 0 || channels < 0 || tokens % block_tokens != 0)
+        return fail(PQG_EINVAL, "tokens (%lld) must be a non-negative multiple of block_tokens", (long long)tokens);
+    if (channels % 64 != 0)
+        return fail(PQG_EINVAL, "channels (%lld) must be a multiple of 64", (long long)channels);
+    if (tokens / block_tokens > 0x7FFFFFFF || channels / 64 > 65535)
+        return fail(PQG_EINVAL, "shape too large");
+    if (tokens == 0 || channels == 0)
+        return PQG_OK;
+    if (!k || !codes || !scales)
+        return fail(PQG_EINVAL, "k, codes and scales are required");
+    if (symmetric && zeros)
+        return fail(PQG_EINVAL, "zeros must be NULL for symmetric codes");
+    if (!symmetric && !zeros)
+        return fail(PQG_EINVAL, "zeros are required for asymmetric codes");
+    if (!aligned(k, 16) || !aligned(codes, 8) || !aligned(scales, 4))
+        return fail(PQG_EINVAL, "misaligned pointer (k: 16 bytes, codes: 8, scales: 4)");
+    pqg::KvKeysArgs a{k, k_dtype == PQG_BF16, tokens, channels, block_tokens, symmetric != 0, codes, scales, zeros};
+    return hip_status(pqg::launch_kv_keys(a, as_stream(stream)), "pqg_kv_quantize_keys launch");
+}
+
+int32_t pqg_kv_dequantize_keys(const void *codes, const float *scales, const uint8_t *zeros, int64_t tokens,
+                               int64_t channels, int32_t block_tokens, int32_t symmetric, void *out, int32_t out_dtype,
+                               void *stream)
+{
+    g_err[0] = 0;
+    if (!valid_float_dtype(out_dtype))
+        return fail(PQG_EINVAL, "unknown out_dtype %d", out_dtype);
+    if (block_tokens != 32 && block_tokens != 64 && block_tokens != 128 && block_tokens != 256)
+        return fail(PQG_EINVAL, "block_tokens must be 32, 64, 128 or 256 (got %d)", block_tokens);
+    if (tokens < 0 || channels < 0 || tokens % block_tokens != 0)
+        return fail(PQG_EINVAL, "tokens (%lld) must be a non-negative multiple of block_tokens", (long long)tokens);
+    if (channels % 8 != 0)
+        return fail(PQG_EINVAL, "channels (%lld) must be a multiple of 8", (long long)channels);
+    if (tokens == 0 || channels == 0)
+        return PQG_OK;
+    if (!codes || !scales || !out)
+        return fail(PQG_EINVAL, "codes, scales and out are required");
+    if (symmetric && zeros)
+        return fail(PQG_EINVAL, "zeros must be NULL for symmetric codes");
+    if (!symmetric && !zeros)
+        return fail(PQG_EINVAL, "zeros are required for asymmetric codes");
+    if (!aligned(codes, 8) || !aligned(scales, 4) || !aligned(out, 16))
+        return fail(PQG_EINVAL, "misaligned pointer (codes: 8 bytes, scales: 4, out: 16)");
+    pqg::KvKeysArgs a{nullptr, false, tokens, channels, block_tokens, symmetric != 0, const_cast<void *>(codes),
+                      const_cast<float *>(scales), const_cast<uint8_t *>(zeros)};
+    return hip_status(pqg::launch_kv_dequant_keys(a, out, out_dtype == PQG_BF16, as_stream(stream)),
+                      "pqg_kv_dequantize_keys launch");
+}
+
+int32_t pqg_kv_append(const void *k_new, const void *v_new, int32_t dtype, int64_t batch, int64_t channels,
+                      const int64_t *positions, int64_t max_tokens, int32_t block_tokens, int32_t v_group_size,
+                      int32_t symmetric, void *k_residual, void *k_codes, float *k_scales, uint8_t *k_zeros,
+                      void *v_codes, float *v_scales, uint8_t *v_zeros, void *stream)
+{
+    g_err[0] = 0;
+    if (!valid_float_dtype(dtype))
+        return fail(PQG_EINVAL, "unknown dtype %d", dtype);
+    if (block_tokens != 32 && block_tokens != 64 && block_tokens != 128 && block_tokens != 256)
+        return fail(PQG_EINVAL, "block_tokens must be 32, 64, 128 or 256 (got %d)", block_tokens);
+    if (v_group_size != 0 && v_group_size != 32 && v_group_size != 64 && v_group_size != 128)
+        return fail(PQG_EINVAL, "v_group_size must be 0 (per token), 32, 64 or 128 (got %d)", v_group_size);
+    if (batch < 0 || channels < 0 || max_tokens < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (channels % 8 != 0 || channels > 8192 || (v_group_size && channels % v_group_size != 0))
+        return fail(PQG_EINVAL, "channels (%lld) must be a multiple of 8 (and of v_group_size), at most 8192",
+                    (long long)channels);
+    if (max_tokens % block_tokens != 0)
+        return fail(PQG_EINVAL, "max_tokens (%lld) must be a multiple of block_tokens", (long long)max_tokens);
+    if (batch > 0x7FFFFFFF)
+        return fail(PQG_EINVAL, "batch too large");
+    if (batch == 0 || channels == 0 || max_tokens == 0)
+        return PQG_OK;
+    if (!k_new || !v_new || !positions || !k_residual || !k_codes || !k_scales || !v_codes || !v_scales)
+        return fail(PQG_EINVAL, "k_new, v_new, positions, k_residual, k_codes, k_scales, v_codes and v_scales are "
+                                "required");
+    if (symmetric && (k_zeros || v_zeros))
+        return fail(PQG_EINVAL, "k_zeros and v_zeros must be NULL for symmetric codes");
+    if (!symmetric && (!k_zeros || !v_zeros))
+        return fail(PQG_EINVAL, "k_zeros and v_zeros are required for asymmetric codes");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_residual, 16) || !aligned(positions, 8) ||
+        !aligned(k_codes, 8) || !aligned(v_codes, 8) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
+        return fail(PQG_EINVAL, "misaligned pointer (k_new, v_new, k_residual: 16 bytes; positions, codes: 8; "
+                                "scales: 4)");
+    pqg::KvAppendArgs a{k_new,    v_new,     dtype == PQG_BF16, batch,   channels, positions, max_tokens,
+                        block_tokens, v_group_size, symmetric != 0, k_residual, k_codes, k_scales, k_zeros,
+                        v_codes,  v_scales,  v_zeros};
+    return hip_status(pqg::launch_kv_append(a, as_stream(stream)), "pqg_kv_append launch");
+}
+
 }  // extern "C"

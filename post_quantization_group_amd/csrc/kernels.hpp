@@ -117,4 +117,39 @@ struct W4A8Args {
 
 hipError_t launch_w4a8(const W4A8Args &a, hipStream_t st);
 
+// KV cache: keys per channel over groups of block_tokens tokens (and their dequantization).
+struct KvKeysArgs {
+    const void *x;  // [tokens, channels] bf16 or fp32 (quantize only)
+    bool x_bf16;
+    int64_t tokens, channels;
+    int block_tokens;
+    bool symmetric;
+    void *codes;     // int8 (symmetric) / uint8 [tokens, channels]
+    float *scales;   // [tokens / T, channels]
+    uint8_t *zeros;  // [tokens / T, channels], NULL iff symmetric
+};
+
+hipError_t launch_kv_keys(const KvKeysArgs &a, hipStream_t st);
+hipError_t launch_kv_dequant_keys(const KvKeysArgs &a, void *out, bool out_bf16, hipStream_t st);
+
+// KV cache: one online append step for a batch of sequences.
+struct KvAppendArgs {
+    const void *k_new, *v_new;  // [batch, channels], bf16 or fp32
+    bool x_bf16;
+    int64_t batch, channels;
+    const int64_t *positions;  // [batch]
+    int64_t max_tokens;
+    int block_tokens, v_group_size;
+    bool symmetric;
+    void *k_res;                       // [batch, T, channels], the input dtype
+    void *k_codes;                     // [batch, max_tokens, channels]
+    float *k_scales;                   // [batch, max_tokens / T, channels]
+    uint8_t *k_zeros;                  // same, NULL iff symmetric
+    void *v_codes;                     // [batch, max_tokens, channels]
+    float *v_scales;                   // [batch, max_tokens, channels / v_group_size or 1]
+    uint8_t *v_zeros;                  // same, NULL iff symmetric
+};
+
+hipError_t launch_kv_append(const KvAppendArgs &a, hipStream_t st);
+
 }  // namespace pqg

@@ -143,3 +143,48 @@ def test_w4a8_rejects(lib):
         assert call(**kw) == pqg.EINVAL, kw
         assert needle in lib.pqg_last_error().decode(), kw
     assert call(M=0, xq=None, sx=None, w=None, sw=None, y=None) == pqg.OK
+
+
+def test_kv_quantize_keys_rejects(lib):
+    def call(**kw):
+        a = dict(k=FAKE, kd=1, t=256, c=1024, T=128, sym=1, q=FAKE, s=FAKE, z=None)
+        a.update(kw)
+        return lib.pqg_kv_quantize_keys(a["k"], a["kd"], a["t"], a["c"], a["T"], a["sym"], a["q"], a["s"], a["z"],
+                                        None)
+    for kw, needle in [(dict(T=48), "block_tokens"), (dict(t=200), "multiple of block_tokens"),
+                       (dict(c=1000), "multiple of 64"), (dict(sym=0), "zeros are required"),
+                       (dict(z=FAKE), "must be NULL"), (dict(kd=4), "k_dtype"), (dict(q=None), "required"),
+                       (dict(k=MISALIGNED), "misaligned")]:
+        assert call(**kw) == pqg.EINVAL, kw
+        assert needle in lib.pqg_last_error().decode(), kw
+    assert call(t=0, k=None, q=None, s=None) == pqg.OK
+
+
+def test_kv_dequantize_keys_rejects(lib):
+    def call(**kw):
+        a = dict(q=FAKE, s=FAKE, z=None, t=256, c=1024, T=128, sym=1, o=FAKE, od=1)
+        a.update(kw)
+        return lib.pqg_kv_dequantize_keys(a["q"], a["s"], a["z"], a["t"], a["c"], a["T"], a["sym"], a["o"], a["od"],
+                                          None)
+    for kw, needle in [(dict(T=100), "block_tokens"), (dict(t=130), "multiple of block_tokens"),
+                       (dict(c=12), "multiple of 8"), (dict(sym=0), "zeros are required"),
+                       (dict(od=3), "out_dtype"), (dict(o=None), "required"), (dict(o=MISALIGNED), "misaligned")]:
+        assert call(**kw) == pqg.EINVAL, kw
+        assert needle in lib.pqg_last_error().decode(), kw
+
+
+def test_kv_append_rejects(lib):
+    def call(**kw):
+        a = dict(kn=FAKE, vn=FAKE, d=1, B=4, C=1024, pos=FAKE, S=4096, T=128, vg=0, sym=1, kr=FAKE, kq=FAKE, ks=FAKE,
+                 kz=None, vq=FAKE, vs=FAKE, vz=None)
+        a.update(kw)
+        return lib.pqg_kv_append(a["kn"], a["vn"], a["d"], a["B"], a["C"], a["pos"], a["S"], a["T"], a["vg"],
+                                 a["sym"], a["kr"], a["kq"], a["ks"], a["kz"], a["vq"], a["vs"], a["vz"], None)
+    for kw, needle in [(dict(T=16), "block_tokens"), (dict(vg=48), "v_group_size"), (dict(C=1004), "multiple of 8"),
+                       (dict(C=16384), "at most 8192"), (dict(C=96, vg=64), "multiple of 8"),
+                       (dict(S=4000), "max_tokens"), (dict(sym=0), "required for asymmetric"),
+                       (dict(kz=FAKE), "must be NULL"), (dict(pos=None), "required"),
+                       (dict(kr=MISALIGNED), "misaligned"), (dict(B=-1), "negative"), (dict(d=5), "dtype")]:
+        assert call(**kw) == pqg.EINVAL, kw
+        assert needle in lib.pqg_last_error().decode(), kw
+    assert call(B=0, kn=None, vn=None, pos=None) == pqg.OK

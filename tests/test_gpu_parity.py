@@ -555,6 +555,102 @@ def test_w4a8_full_layer(gpu_lib):
     assert err <= TOL_BF16, err
 
 
+# --------------------------------------------------------------------------- KV cache
+
+
+def _kv_input(k_bits, dtype):
+    return to_gpu_bf16(k_bits) if dtype == "bf16" else to_gpu(W.bf16_to_f32(k_bits))
+
+
+@pytest.mark.parametrize("T", [32, 64, 128, 256])
+@pytest.mark.parametrize("C,nb", [(64, 1), (192, 3), (1024, 2)])
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_keys_bitexact(gpu_lib, T, C, nb, sym, dtype):
+    announce("kv keys T=%d C=%d nb=%d sym=%s %s" % (T, C, nb, sym, dtype))
+    d = W.kv_cache(T * nb, C, outlier_channels=max(1, C // 64))
+    src = d["k"] if dtype == "bf16" else W.bf16_to_f32(d["k"])
+    q, s, z = gpu_lib.kv_quantize_keys(_kv_input(d["k"], dtype), T, sym)
+    torch.cuda.synchronize()
+    qo, so, zo = oracle.kv_quantize_keys(src, T, sym)
+    assert np.array_equal(q.cpu().numpy().astype(np.int32), qo)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    if not sym:
+        assert np.array_equal(z.cpu().numpy(), zo)
+
+
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_kv_dequant_keys_bitexact(gpu_lib, sym, out):
+    announce("kv dequant keys sym=%s %s" % (sym, out))
+    d = W.kv_cache(256, 192, outlier_channels=3)
+    qo, so, zo = oracle.kv_quantize_keys(d["k"], 64, sym)
+    codes = to_gpu(qo.astype(np.int8 if sym else np.uint8))
+    xh = gpu_lib.kv_dequantize_keys(codes, to_gpu(so), None if sym else to_gpu(zo), 64, sym,
+                                    out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    r32, r16 = oracle.kv_dequantize_keys(qo, so, zo, 64)
+    if out == "bf16":
+        assert np.array_equal(bf16_tensor_bits(xh), r16)
+    else:
+        assert np.array_equal(xh.cpu().numpy().view(np.uint32), r32.view(np.uint32))
+
+
+@pytest.mark.parametrize("T,vg,sym,dtype", [(32, 0, True, "bf16"), (64, 64, False, "bf16"), (32, 128, True, "f32"),
+                                            (128, 32, False, "f32")])
+def test_kv_append_online(gpu_lib, T, vg, sym, dtype):
+    """A run of online steps over three sequences that end at different lengths (one is pointed past the cache,
+    one at -1, once they end), then the whole cache against the oracle's step-by-step simulation, bit-exact."""
+    B, S, C = 3, 3 * T, 256
+    announce("kv append T=%d vg=%d sym=%s %s" % (T, vg, sym, dtype))
+    d = W.kv_cache(B * S, C, outlier_channels=4)
+    ks, vs = d["k"].reshape(B, S, C), d["v"].reshape(B, S, C)
+    if dtype == "f32":
+        ks, vs = W.bf16_to_f32(ks), W.bf16_to_f32(vs)
+    n_tok = [S, T + 7, T]
+    nv = C // vg if vg else 1
+    ref = {"k_res": np.zeros((B, T, C), ks.dtype), "k_q": np.zeros((B, S, C), np.int32),
+           "k_s": np.zeros((B, S // T, C), np.float32), "v_q": np.zeros((B, S, C), np.int32),
+           "v_s": np.zeros((B, S, nv), np.float32)}
+    if not sym:
+        ref["k_z"] = np.zeros((B, S // T, C), np.uint8)
+        ref["v_z"] = np.zeros((B, S, nv), np.uint8)
+    cache = gpu_lib.kv_cache_alloc(B, S, C, T, vg, sym, torch.bfloat16 if dtype == "bf16" else torch.float32)
+    conv = to_gpu_bf16 if dtype == "bf16" else to_gpu
+    for step in range(S + 1):
+        pos = np.array([step if step < n_tok[b] else (S + 5 if b == 0 else -1) for b in range(B)], np.int64)
+        kn = np.ascontiguousarray(np.stack([ks[b, min(step, S - 1)] for b in range(B)]))
+        vn = np.ascontiguousarray(np.stack([vs[b, min(step, S - 1)] for b in range(B)]))
+        gpu_lib.kv_append(cache, conv(kn), conv(vn), to_gpu(pos), T, vg, sym)
+        oracle.kv_append(ref, kn, vn, pos, T, vg, sym)
+    torch.cuda.synchronize()
+    for key in ("k_q", "v_q"):
+        assert np.array_equal(cache[key].cpu().numpy().astype(np.int32), ref[key]), key
+    for key in ("k_s", "v_s"):
+        assert np.array_equal(cache[key].cpu().numpy().view(np.uint32), ref[key].view(np.uint32)), key
+    if not sym:
+        for key in ("k_z", "v_z"):
+            assert np.array_equal(cache[key].cpu().numpy(), ref[key]), key
+    res = bf16_tensor_bits(cache["k_res"]) if dtype == "bf16" else cache["k_res"].cpu().numpy()
+    assert np.array_equal(res, ref["k_res"])
+
+
+def test_kv_keys_full_size_sampled(gpu_lib):
+    """The measured workload (32 sequences x 4096 tokens of one layer's keys, 1024 channels, T = 128) in one
+    launch; sampled token groups against the oracle, bit-exact."""
+    announce("kv keys full size")
+    d = W.kv_cache(32 * 4096, W.KV_CHANNELS)
+    for sym in (True, False):
+        q, s, z = gpu_lib.kv_quantize_keys(to_gpu_bf16(d["k"]), 128, sym)
+        torch.cuda.synchronize()
+        for b in (0, 517, 1023):
+            qo, so, zo = oracle.kv_quantize_keys(d["k"][128 * b:128 * b + 128], 128, sym)
+            assert np.array_equal(q[128 * b:128 * b + 128].cpu().numpy().astype(np.int32), qo)
+            assert np.array_equal(s[b].cpu().numpy().view(np.uint32), so[0].view(np.uint32))
+            if not sym:
+                assert np.array_equal(z[b].cpu().numpy(), zo[0])
+
+
 # --------------------------------------------------------------------------- determinism
 
 def test_reruns_are_bit_identical(gpu_lib):
