@@ -19,6 +19,9 @@ One step is one pass over every stage of the quantized linear layer on synthetic
              into its gain emits it) to INT8 with one calibrated per-tensor scale (the GEMM is the same)
   w4a8       the same layer with the smoothed weights as INT4, g = 128 (quantized once, offline), times the
              step's per-token INT8 activation codes                                    <- the W4A8 TOPS
+  kv         one layer's KV cache of 32 sequences x 4096 tokens (8 KV heads x 128 = 1024 channels, bf16):
+             keys per channel over groups of 128 tokens, values per token; then one online append step for
+             the 32 sequences with no group completing, and one where every sequence completes its group
 The packed layer exists twice. A step re-quantizes into one copy, runs the dequantize and the W8A8 layer,
 then the batch-32 and batch-8 passes over the other copy (clean 455 MB reads that also drain the dirty lines
 the 1.7 GB dequantize left in the 256 MB last-level cache), and last the batch-1 decode pass over the copy
@@ -153,6 +156,18 @@ def main():
     xq8s = torch.empty((M8, K8), dtype=torch.int8, device=dev)
     wq4, sw4, _ = pqg.quantize(W8, 4, True, pqg.GROUP, 128, s8, pqg.SMOOTH_MUL)
     y4 = torch.empty((M8, N8), dtype=torch.bfloat16, device=dev)
+    KV_B, KV_S, KV_T = 32, 4096, 128
+    dkv = W.kv_cache(KV_B * KV_S, W.KV_CHANNELS)
+    Kkv, Vkv = bf16(dkv["k"]), bf16(dkv["v"])
+    del dkv
+    KV_C = Kkv.shape[1]
+    kvk = (torch.empty_like(Kkv, dtype=torch.int8), torch.empty((KV_B * KV_S // KV_T, KV_C), dtype=torch.float32,
+                                                                 device=dev), None)
+    kvv = (torch.empty_like(Vkv, dtype=torch.int8), torch.empty(KV_B * KV_S, dtype=torch.float32, device=dev), None)
+    kv_cache = pqg.kv_cache_alloc(KV_B, KV_S, KV_C, KV_T, 0, True, torch.bfloat16, dev)
+    kv_new_k, kv_new_v = Kkv[:KV_B].clone(), Vkv[:KV_B].clone()
+    kv_pos_none = torch.full((KV_B,), 1000, dtype=torch.int64, device=dev)  # slot 1000 % 128 = 104
+    kv_pos_all = torch.full((KV_B,), 1023, dtype=torch.int64, device=dev)   # slot 127: every group completes
     sx8s = torch.empty(M8, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
@@ -162,7 +177,8 @@ def main():
     w8a8_ops = 2.0 * M8 * N8 * K8
 
     parts = ["quantize", "dequantize", "smooth", "wquant", "w8a8_actquant", "w8a8_gemm", "w8a8_static_actquant",
-             "w4a8_gemm", "w4a16_m32", "w4a16_m8", "w4a16_m1"]
+             "w4a8_gemm", "kv_keys", "kv_values", "kv_append", "kv_append_groups", "w4a16_m32", "w4a16_m8",
+             "w4a16_m1"]
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def run_step(i, rec):
@@ -211,6 +227,22 @@ def main():
         if rec:
             marks["w4a8_gemm"] = ev()
             marks["w4a8_gemm"].record(stream)
+        pqg.kv_quantize_keys(Kkv, KV_T, True, out=kvk)  # keys per channel over groups of 128 tokens
+        if rec:
+            marks["kv_keys"] = ev()
+            marks["kv_keys"].record(stream)
+        pqg.quantize(Vkv, 8, True, pqg.ROW, out=kvv)  # values per token
+        if rec:
+            marks["kv_values"] = ev()
+            marks["kv_values"].record(stream)
+        pqg.kv_append(kv_cache, kv_new_k, kv_new_v, kv_pos_none, KV_T, 0, True)
+        if rec:
+            marks["kv_append"] = ev()
+            marks["kv_append"].record(stream)
+        pqg.kv_append(kv_cache, kv_new_k, kv_new_v, kv_pos_all, KV_T, 0, True)
+        if rec:
+            marks["kv_append_groups"] = ev()
+            marks["kv_append_groups"].record(stream)
         for p in projs:  # S7: batch 32
             pqg.qlinear_w4a16(p["x"], p["packed"][o], p["scales"][o], None, 128, True, out=p["y32"])
         if rec:
@@ -332,6 +364,18 @@ def main():
             "avg_launch_us": round(part_ms["w4a8_gemm"] * 1e3, 2),
             "group_size": 128,
             "weight_bytes": N8 * K8 // 2 + N8 * (K8 // 128) * 4,
+        },
+        # the KV cache of one layer (32 x 4096 tokens, 1024 channels): bulk key and value quantization as
+        # bytes moved (bf16 in, INT8 codes and fp32 scales out), and one online append step for 32 sequences
+        "kv_int8": {
+            "tokens": KV_B * KV_S, "channels": KV_C, "block_tokens": KV_T,
+            "keys_us": round(part_ms["kv_keys"] * 1e3, 2),
+            "keys_gbs": round((KV_B * KV_S * KV_C * 3 + KV_B * KV_S // KV_T * KV_C * 4) / (part_ms["kv_keys"] * 1e-3)
+                              / 1e9, 1),
+            "values_us": round(part_ms["kv_values"] * 1e3, 2),
+            "values_gbs": round((KV_B * KV_S * KV_C * 3 + KV_B * KV_S * 4) / (part_ms["kv_values"] * 1e-3) / 1e9, 1),
+            "append_us": round(part_ms["kv_append"] * 1e3, 2),
+            "append_completing_groups_us": round(part_ms["kv_append_groups"] * 1e3, 2),
         },
         "per_projection_event_us": {p["name"]: round(float(t) * 1e3, 2) for p, t in zip(projs, launch_ms)},
         "stage_ms": {k: round(v, 4) for k, v in part_ms.items()},

@@ -265,9 +265,10 @@ int32_t pqg_kv_dequantize_keys(const void *codes, const float *scales, const uin
  *   v_codes      : int8 / uint8 [batch, max_tokens, channels]; v_scales fp32 [batch, max_tokens, nv] with
  *                  nv = 1 or channels / v_group_size; v_zeros uint8 like v_scales, NULL iff symmetric.
  *   block_tokens T in {32, 64, 128, 256}; max_tokens % T == 0; v_group_size in {0, 32, 64, 128};
- *   channels % 8 == 0 (and % v_group_size), channels <= 8192.
- * Alignment: k_new, v_new, k_residual 16 bytes; positions, codes 8; scales 4. One block per sequence: a step's
- * cost is one row of values and keys per sequence, plus T rows of keys for each sequence whose group completes.
+ *   channels % 64 == 0 (and % v_group_size), channels <= 8192.
+ * Alignment: k_new, v_new, k_residual 16 bytes; positions, codes 8; scales 4. One block per sequence and 64
+ * channels: a step reads one row of values and keys per sequence, plus T rows of keys for each sequence whose
+ * group completes.
  */
 int32_t pqg_kv_append(const void *k_new, const void *v_new, int32_t dtype, int64_t batch, int64_t channels,
                       const int64_t *positions, int64_t max_tokens, int32_t block_tokens, int32_t v_group_size,

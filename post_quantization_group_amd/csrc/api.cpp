@@ -385,8 +385,8 @@ int32_t pqg_kv_append(const void *k_new, const void *v_new, int32_t dtype, int64
         return fail(PQG_EINVAL, "v_group_size must be 0 (per token), 32, 64 or 128 (got %d)", v_group_size);
     if (batch < 0 || channels < 0 || max_tokens < 0)
         return fail(PQG_EINVAL, "negative shape");
-    if (channels % 8 != 0 || channels > 8192 || (v_group_size && channels % v_group_size != 0))
-        return fail(PQG_EINVAL, "channels (%lld) must be a multiple of 8 (and of v_group_size), at most 8192",
+    if (channels % 64 != 0 || channels > 8192 || (v_group_size && channels % v_group_size != 0))
+        return fail(PQG_EINVAL, "channels (%lld) must be a multiple of 64 (and of v_group_size), at most 8192",
                     (long long)channels);
     if (max_tokens % block_tokens != 0)
         return fail(PQG_EINVAL, "max_tokens (%lld) must be a multiple of block_tokens", (long long)max_tokens);

@@ -54,6 +54,46 @@ __device__ __forceinline__ void stats_add(float *am, float *lo, float *hi, const
 // xor shuffles, then over the four waves through LDS (max and min are exact in any order).
 constexpr int kKvCols = 64, kKvThreads = 256, kKvRows = kKvThreads / 8;
 
+// Per-channel parameters of a tile of rows x 64 channels held by 256 threads as 32 row lanes x 8 channel lanes
+// (thread tid: channels 8 (tid % 8) .. + 7): the thread's partial ranges are combined over the wave's 8 row
+// lanes by xor shuffles, then over the four waves through `red` (max and min are exact in any order).
+template <bool SYM>
+__device__ __forceinline__ void tile_params(float *am, float *lo, float *hi, float (*red)[kKvThreads / kWave][kKvCols],
+                                            SegParams *p)
+{
+    const int tid = threadIdx.x, lr = tid % 8;
+#pragma unroll
+    for (int off = 8; off < kWave; off <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            am[j] = __builtin_fmaxf(am[j], __shfl_xor(am[j], off, kWave));
+            lo[j] = __builtin_fminf(lo[j], __shfl_xor(lo[j], off, kWave));
+            hi[j] = __builtin_fmaxf(hi[j], __shfl_xor(hi[j], off, kWave));
+        }
+    const int wv = tid / kWave;
+    if (tid % kWave < 8)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            red[0][wv][lr * 8 + j] = am[j];
+            red[1][wv][lr * 8 + j] = lo[j];
+            red[2][wv][lr * 8 + j] = hi[j];
+        }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float a = red[0][0][lr * 8 + j], l = red[1][0][lr * 8 + j], h = red[2][0][lr * 8 + j];
+#pragma unroll
+        for (int w = 1; w < kKvThreads / kWave; ++w) {
+            a = __builtin_fmaxf(a, red[0][w][lr * 8 + j]);
+            l = __builtin_fminf(l, red[1][w][lr * 8 + j]);
+            h = __builtin_fmaxf(h, red[2][w][lr * 8 + j]);
+        }
+        p[j] = seg_params<8, SYM>(a, l, h);
+    }
+}
+
+// Block (group b, 64 channels): a thread keeps its T / 32 rows of 8 values in registers, so the group is read
+// once and written once.
 template <typename XT, bool SYM, int T>
 __global__ __launch_bounds__(kKvThreads) void k_kv_keys(const XT *__restrict__ x, int64_t channels,
                                                         void *__restrict__ codes, float *__restrict__ scales,
@@ -73,36 +113,8 @@ __global__ __launch_bounds__(kKvThreads) void k_kv_keys(const XT *__restrict__ x
 #pragma unroll
     for (int i = 1; i < RP; ++i)
         stats_add<SYM>(am, lo, hi, v[i]);
-    // over the wave's 8 rows (lanes lr, lr + 8, ..., lr + 56)
-#pragma unroll
-    for (int off = 8; off < kWave; off <<= 1)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            am[j] = __builtin_fmaxf(am[j], __shfl_xor(am[j], off, kWave));
-            lo[j] = __builtin_fminf(lo[j], __shfl_xor(lo[j], off, kWave));
-            hi[j] = __builtin_fmaxf(hi[j], __shfl_xor(hi[j], off, kWave));
-        }
-    const int wv = tid / kWave;
-    if (tid % kWave < 8)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            red[0][wv][lr * 8 + j] = am[j];
-            red[1][wv][lr * 8 + j] = lo[j];
-            red[2][wv][lr * 8 + j] = hi[j];
-        }
-    __syncthreads();
     SegParams p[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        float a = red[0][0][lr * 8 + j], l = red[1][0][lr * 8 + j], h = red[2][0][lr * 8 + j];
-#pragma unroll
-        for (int w = 1; w < kKvThreads / kWave; ++w) {
-            a = __builtin_fmaxf(a, red[0][w][lr * 8 + j]);
-            l = __builtin_fminf(l, red[1][w][lr * 8 + j]);
-            h = __builtin_fmaxf(h, red[2][w][lr * 8 + j]);
-        }
-        p[j] = seg_params<8, SYM>(a, l, h);
-    }
+    tile_params<SYM>(am, lo, hi, red, p);
     if (r0 == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -202,9 +214,10 @@ __device__ __forceinline__ void block_range8(float &am, float &lo, float &hi, fl
     }
 }
 
-// One block per sequence. Values: quantized per token (VG = 0) or per group of VG channels into row p of the
-// sequence's value cache. Keys: the new key goes to residual slot p % T; when p % T == T - 1 the group is
-// complete and is quantized per channel into rows p - T + 1 .. p (the new row is read from the input).
+// Block (sequence b, 64-channel slice y). Values: every block of the sequence quantizes the whole new value row
+// (a few KB) per token (VG = 0) or per group of VG channels and writes its slice of row p. Keys: the block copies
+// its slice of the new key to residual slot p % T; when p % T == T - 1 the group of tokens is complete and the
+// block quantizes its T x 64 tile per channel (the new row read from the input) into rows p - T + 1 .. p.
 template <typename XT, bool SYM, int VG>
 __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict__ k_new, const XT *__restrict__ v_new,
                                                            int64_t channels, const int64_t *__restrict__ positions,
@@ -213,8 +226,11 @@ __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict_
                                                            uint8_t *__restrict__ k_zeros, int8_t *__restrict__ v_codes,
                                                            float *__restrict__ v_scales, uint8_t *__restrict__ v_zeros)
 {
+    static_assert(kAppThreads == kKvThreads, "the key tile uses the bulk kernel's thread layout");
     __shared__ float red[3][kAppThreads / kWave];
+    __shared__ float tred[3][kKvThreads / kWave][kKvCols];
     const int64_t b = blockIdx.x;
+    const int y = blockIdx.y;  // channels 64 y .. 64 y + 63 = chunks 8 y .. 8 y + 7
     const int64_t p = positions[b];
     if (p < 0 || p >= max_tokens)
         return;  // uniform over the block
@@ -222,6 +238,7 @@ __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict_
     const int64_t nchunk = channels / 8;
     const XT *kn = k_new + b * channels;
     const XT *vn = v_new + b * channels;
+    auto in_slice = [&](int64_t ci) { return ci >= 8 * (int64_t)y && ci < 8 * (int64_t)y + 8; };
 
     // values
     float v[kAppChunks][8];
@@ -252,10 +269,10 @@ __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict_
 #pragma unroll
         for (int u = 0; u < kAppChunks; ++u) {
             const int64_t ci = tid + (int64_t)kAppThreads * u;
-            if (ci < nchunk)
+            if (ci < nchunk && in_slice(ci))
                 *reinterpret_cast<uint2 *>(v_codes + vrow * channels + ci * 8) = codes8(v[u], ps);
         }
-        if (tid == 0) {
+        if (y == 0 && tid == 0) {
             v_scales[vrow] = sp.s;
             if (!SYM)
                 v_zeros[vrow] = (uint8_t)sp.z;
@@ -281,9 +298,9 @@ __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict_
             hi = wave_max<GL>(hi);
             const SegParams sp = seg_params<8, SYM>(am, lo, hi);
             const SegParams ps[8] = {sp, sp, sp, sp, sp, sp, sp, sp};
-            if (ci < nchunk) {
+            if (ci < nchunk && in_slice(ci)) {
                 *reinterpret_cast<uint2 *>(v_codes + vrow * channels + ci * 8) = codes8(v[u], ps);
-                if (ci % GL == 0) {
+                if (ci % GL == 0) {  // the group's first chunk lies in exactly one slice
                     v_scales[vrow * ngroups + ci / GL] = sp.s;
                     if (!SYM)
                         v_zeros[vrow * ngroups + ci / GL] = (uint8_t)sp.z;
@@ -292,48 +309,59 @@ __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict_
         }
     }
 
-    // keys: residual slot, and the group's quantization when it completes
+    // keys: this slice of the residual slot
     const int slot = (int)(p % T);
     XT *res = k_res + b * (int64_t)T * channels;
-    for (int64_t ci = tid; ci < nchunk; ci += kAppThreads) {
+    const int64_t c0 = (int64_t)y * kKvCols;
+    if (tid < 8) {
+        const int64_t c = c0 + tid * 8;
         if (sizeof(XT) == 2)
-            *reinterpret_cast<uint4 *>(res + slot * channels + ci * 8) = *reinterpret_cast<const uint4 *>(kn + ci * 8);
+            *reinterpret_cast<uint4 *>(res + slot * channels + c) = *reinterpret_cast<const uint4 *>(kn + c);
         else {
-            reinterpret_cast<float4 *>(res + slot * channels + ci * 8)[0] = reinterpret_cast<const float4 *>(kn + ci * 8)[0];
-            reinterpret_cast<float4 *>(res + slot * channels + ci * 8)[1] = reinterpret_cast<const float4 *>(kn + ci * 8)[1];
+            reinterpret_cast<float4 *>(res + slot * channels + c)[0] = reinterpret_cast<const float4 *>(kn + c)[0];
+            reinterpret_cast<float4 *>(res + slot * channels + c)[1] = reinterpret_cast<const float4 *>(kn + c)[1];
         }
     }
     if (slot != T - 1)
-        return;
-    const int64_t first = p - (T - 1);  // the group's first token
-    const int64_t kb = b * (max_tokens / T) + p / T;
-    for (int64_t ci = tid; ci < nchunk; ci += kAppThreads) {
-        float w[8], am[8], lo[8], hi[8];
-        load8<XT>(kn + ci * 8, w);  // row T - 1 is the new key
-        stats_init<SYM>(am, lo, hi, w);
-        for (int r = 0; r < T - 1; ++r) {
-            load8<XT>(res + r * channels + ci * 8, w);
-            stats_add<SYM>(am, lo, hi, w);
+        return;  // uniform
+    // the complete group, as the bulk kernel: rows r0 + 32 i (i < T / 32) of channels c0 + 8 lr .. + 7
+    const int lr = tid % 8, r0 = tid / 8, rp = T / kKvRows;
+    const int64_t c = c0 + lr * 8;
+    float w[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < rp) {
+            const int r = r0 + kKvRows * i;
+            load8<XT>(r == T - 1 ? kn + c : res + r * channels + c, w[i]);  // row T - 1 is the new key
         }
-        SegParams ps[8];
+    float am[8], lo[8], hi[8];
+    stats_init<SYM>(am, lo, hi, w[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        if (i < rp)
+            stats_add<SYM>(am, lo, hi, w[i]);
+    SegParams ps[8];
+    tile_params<SYM>(am, lo, hi, tred, ps);
+    const int64_t kb = b * (max_tokens / T) + p / T;
+    if (r0 == 0)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            ps[j] = seg_params<8, SYM>(am[j], lo[j], hi[j]);
-            k_scales[kb * channels + ci * 8 + j] = ps[j].s;
+            k_scales[kb * channels + c + j] = ps[j].s;
             if (!SYM)
-                k_zeros[kb * channels + ci * 8 + j] = (uint8_t)ps[j].z;
+                k_zeros[kb * channels + c + j] = (uint8_t)ps[j].z;
         }
-        for (int r = 0; r < T; ++r) {
-            load8<XT>(r == T - 1 ? kn + ci * 8 : res + r * channels + ci * 8, w);
-            *reinterpret_cast<uint2 *>(k_codes + ((b * max_tokens + first + r) * channels + ci * 8)) = codes8(w, ps);
-        }
-    }
+    const int64_t first = p - (T - 1);  // the group's first token
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < rp)
+            *reinterpret_cast<uint2 *>(k_codes + ((b * max_tokens + first + r0 + kKvRows * i) * channels + c)) =
+                codes8(w[i], ps);
 }
 
 template <typename XT, bool SYM, int VG>
 hipError_t append_go(const KvAppendArgs &a, hipStream_t st)
 {
-    k_kv_append<XT, SYM, VG><<<dim3((unsigned)a.batch), dim3(kAppThreads), 0, st>>>(
+    k_kv_append<XT, SYM, VG><<<dim3((unsigned)a.batch, (unsigned)(a.channels / kKvCols)), dim3(kAppThreads), 0, st>>>(
         static_cast<const XT *>(a.k_new), static_cast<const XT *>(a.v_new), a.channels, a.positions, a.max_tokens,
         a.block_tokens, static_cast<XT *>(a.k_res), static_cast<int8_t *>(a.k_codes), a.k_scales, a.k_zeros,
         static_cast<int8_t *>(a.v_codes), a.v_scales, a.v_zeros);

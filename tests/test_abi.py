@@ -180,8 +180,8 @@ def test_kv_append_rejects(lib):
         a.update(kw)
         return lib.pqg_kv_append(a["kn"], a["vn"], a["d"], a["B"], a["C"], a["pos"], a["S"], a["T"], a["vg"],
                                  a["sym"], a["kr"], a["kq"], a["ks"], a["kz"], a["vq"], a["vs"], a["vz"], None)
-    for kw, needle in [(dict(T=16), "block_tokens"), (dict(vg=48), "v_group_size"), (dict(C=1004), "multiple of 8"),
-                       (dict(C=16384), "at most 8192"), (dict(C=96, vg=64), "multiple of 8"),
+    for kw, needle in [(dict(T=16), "block_tokens"), (dict(vg=48), "v_group_size"), (dict(C=1000), "multiple of 64"),
+                       (dict(C=16384), "at most 8192"), (dict(C=192, vg=128), "multiple of 64"),
                        (dict(S=4000), "max_tokens"), (dict(sym=0), "required for asymmetric"),
                        (dict(kz=FAKE), "must be NULL"), (dict(pos=None), "required"),
                        (dict(kr=MISALIGNED), "misaligned"), (dict(B=-1), "negative"), (dict(d=5), "dtype")]:
