@@ -11,7 +11,8 @@ Sources, by page title and section:
   [P2] "模型压缩：量化、ZeroQuant、LLM.int8() 与 SmoothQuant": §3 basic formula; §4 granularity;
        §11 vector-wise scales; §12-13 SmoothQuant and alpha.
   [P3] "第11章 模型量化与压缩": §11.1.1-§11.1.6 affine quantization, granularity, worked INT4 example;
-       §11.4.3-§11.4.5 smoothing factor and W8A8 pipeline; §11.6.2-§11.6.5 KV-cache quantization.
+       §11.3.7 metadata share; §11.4.3-§11.4.5 smoothing factor and W8A8 pipeline; §11.6.2-§11.6.5 KV-cache
+       quantization.
   [P5] "大模型压缩：从研究到生产的完整攻略（1）": symmetric / asymmetric worked examples; outliers.
 """
 from __future__ import annotations
@@ -64,6 +65,12 @@ def _load():
         lib.or_w4a8.argtypes = [P, P, I64, I64, I64, P, P, P, I64, P]
         lib.or_w4a8.restype = I32
         lib.or_kv_keys.argtypes = [P, I32, I64, I64, I64, I32, P, P, P]
+        lib.or_quantize_meta16.argtypes = [P, I32, I64, I64, I32, I32, P, P, P]
+        lib.or_quantize_meta16.restype = I32
+        lib.or_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.or_f32_to_f16.restype = ctypes.c_uint16
+        lib.or_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.or_f16_to_f32.restype = ctypes.c_float
         lib.or_kv_keys.restype = I32
         lib.or_kv_dequant_keys.argtypes = [P, P, P, I64, I64, I64, P, P]
         lib.or_kv_dequant_keys.restype = I32
@@ -380,3 +387,42 @@ def kv_append(cache, k_new, v_new, positions, block_tokens: int, v_group_size: i
             cache["k_s"][b, p // block_tokens] = ks[0]
             if not symmetric:
                 cache["k_z"][b, p // block_tokens] = kz[0]
+
+
+# ---------------------------------------------------------------- 16-bit metadata
+
+
+def f32_to_f16(v: float) -> int:
+    """binary16 bits of a binary32 value, round to nearest even."""
+    return int(_load().or_f32_to_f16(float(v)))
+
+
+def f16_to_f32(h) -> np.ndarray:
+    """binary16 bits (array) -> their exact binary32 values."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    f = _load().or_f16_to_f32
+    return np.array([f(int(v)) for v in h.ravel()], np.float32).reshape(h.shape)
+
+
+def quantize_meta16(x, symmetric: bool, group_size: int):
+    """INT4 group quantization with binary16 scales [P1 §1.1; P3 §11.3.7]: returns (codes int32 [rows, cols],
+    s16 uint16 binary16 bits [rows * cols / g], zeros uint8 [rows * cols / g] or None)."""
+    x, dt = _float_input(x)
+    rows, cols = x.shape
+    nseg = rows * cols // group_size if group_size > 0 else 0
+    q = np.zeros((rows, cols), np.int32)
+    s16 = np.zeros(nseg, np.uint16)
+    z = None if symmetric else np.zeros(nseg, np.uint8)
+    if _load().or_quantize_meta16(_ptr(x), dt, rows, cols, int(bool(symmetric)), group_size, _ptr(q), _ptr(s16),
+                                  _ptr(z)) != 0:
+        raise ValueError("group_size must divide cols")
+    return q, s16, z
+
+
+def pack_zeros4(z) -> np.ndarray:
+    """Zero points two per byte, the flattened group index 2i in the low nibble (an odd count ends with a
+    high nibble of 0), using the INT4 pack."""
+    z = np.ascontiguousarray(z, dtype=np.int32).ravel()
+    if z.size % 2:
+        z = np.concatenate([z, np.zeros(1, np.int32)])
+    return pack_int4(z.reshape(1, -1)).ravel()

@@ -274,6 +274,103 @@ static int64_t segment_of(int64_t i, int64_t cols, int granularity, int group_si
     return i / group_size; /* groups are contiguous in row-major order because cols % group_size == 0 */
 }
 
+/* ---------------------------------------------------------------- 16-bit metadata */
+
+/* binary32 -> binary16 bits, round to nearest, ties to even, with subnormal results; overflow gives inf. */
+uint16_t or_f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t sign = (u >> 16) & 0x8000u;
+    int32_t exp = (int32_t)((u >> 23) & 0xFFu);
+    uint32_t mant = u & 0x7FFFFFu;
+    if (exp == 0xFF)
+        return (uint16_t)(sign | 0x7C00u | (mant ? 0x200u : 0u));
+    int32_t e = exp - 127 + 15; /* binary16 biased exponent */
+    if (e >= 31)
+        return (uint16_t)(sign | 0x7C00u);
+    uint32_t m;
+    int shift;
+    if (e <= 0) { /* subnormal result: value / 2^-24 */
+        if (e < -10)
+            return (uint16_t)sign; /* below 2^-25: rounds to zero */
+        m = mant | 0x800000u;
+        shift = 14 - e;
+    } else {
+        m = mant;
+        shift = 13;
+    }
+    uint32_t q = m >> shift, rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u)))
+        q += 1u;
+    if (e <= 0)
+        return (uint16_t)(sign | q); /* q = 0x400 is the smallest normal, encoded as such */
+    return (uint16_t)(sign | (((uint32_t)e << 10) + q)); /* a carry moves into the exponent (up to inf) */
+}
+
+float or_f16_to_f32(uint16_t h)
+{
+    int exp = (h >> 10) & 0x1F, mant = h & 0x3FF;
+    float v;
+    if (exp == 0)
+        v = ldexpf((float)mant, -24);
+    else if (exp == 31)
+        v = mant ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(1024 + mant), exp - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
+/*
+ * INT4 group quantization with 16-bit metadata [P1 §1.1 and P3 §11.3.7 count one 16-bit scale per group:
+ * about 3 % of the INT4 weight bytes at g = 128 and 13 % at g = 32]. Per group: the range and (s, z) as in
+ * or_quantize; the scale is stored as binary16, s16 = fp16(s) rounded to nearest even (a result of 0 becomes
+ * the smallest subnormal 2^-24, an overflow the largest finite 65504); the codes (and the asymmetric zero
+ * point) are computed with the stored scale, q = clamp(round(x / s16) + z), z = clamp(round(-lo / s16)), so
+ * that s16 (q - z) is the value the stored metadata encodes.
+ * Outputs: q[rows * cols] unpacked, s16[rows * cols / g] binary16 bits, zeros[rows * cols / g] (NULL when
+ * symmetric). Returns 0, or -1 on bad arguments.
+ */
+int or_quantize_meta16(const void *x, int x_dtype, int64_t rows, int64_t cols, int symmetric, int group_size,
+                       int32_t *q, uint16_t *s16, uint8_t *zeros)
+{
+    if (group_size <= 0 || cols % group_size != 0)
+        return -1;
+    int64_t nseg = rows * (cols / group_size);
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < nseg; ++e) {
+        int64_t i0 = e * group_size; /* groups are contiguous in row-major order */
+        float absmax = 0.0f, lo = 0.0f, hi = 0.0f;
+        for (int64_t i = i0; i < i0 + group_size; ++i) {
+            float v = load_elem(x, x_dtype, i);
+            float a = fabsf(v);
+            if (a > absmax)
+                absmax = a;
+            if (i == i0 || v < lo)
+                lo = v;
+            if (i == i0 || v > hi)
+                hi = v;
+        }
+        seg_params p = segment_params(absmax, lo, hi, 4, symmetric);
+        uint16_t h = or_f32_to_f16(p.s);
+        if ((h & 0x7FFFu) == 0)
+            h = 0x0001u;
+        else if ((h & 0x7C00u) == 0x7C00u)
+            h = 0x7BFFu;
+        s16[e] = h;
+        p.s = or_f16_to_f32(h);
+        if (!symmetric) {
+            float l = lo > 0.0f ? 0.0f : lo;
+            int z = (int)nearbyintf(-l / p.s);
+            p.z = z < 0 ? 0 : z > 15 ? 15 : z;
+            zeros[e] = (uint8_t)p.z;
+        }
+        for (int64_t i = i0; i < i0 + group_size; ++i)
+            q[i] = quantize_one(load_elem(x, x_dtype, i), p);
+    }
+    return 0;
+}
+
 /* ---------------------------------------------------------------- KV cache */
 
 /*

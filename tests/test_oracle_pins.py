@@ -679,3 +679,89 @@ def test_kv_append_online_equals_bulk(sym, vg):
         if not sym:
             assert np.array_equal(cache["v_z"][b, :n].ravel(), zv)
         assert not cache["v_q"][b, n:].any()
+
+
+# ---------------------------------------------------------------- 16-bit metadata (P1 §1.1; P3 §11.3.7)
+
+
+def test_f16_conversion_matches_numpy():
+    """The oracle's binary32 -> binary16 rounding (nearest even, subnormals, overflow) agrees with numpy's cast,
+    and binary16 -> binary32 is exact, over normal, subnormal, tie and overflow inputs."""
+    rng = np.random.default_rng(30)
+    v = np.concatenate([
+        (rng.standard_normal(4000) * np.exp2(rng.integers(-30, 17, 4000))).astype(np.float32),
+        np.float32([2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -24, 65504.0, 65519.99, 65520.0, 1 + 2.0 ** -11,
+                    1 + 3 * 2.0 ** -11, 6.1e-5, 0.0])])
+    with np.errstate(over="ignore"):
+        ref = np.abs(v).astype(np.float16).view(np.uint16)
+    mine = np.array([oracle.f32_to_f16(abs(float(x))) for x in v], np.uint16)
+    assert np.array_equal(mine, ref)
+    h = np.arange(0, 0x7C00, 7, dtype=np.uint16)
+    assert np.array_equal(oracle.f16_to_f32(h), h.view(np.float16).astype(np.float32))
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_meta16_scale_is_the_rounded_fp32_scale(sym):
+    """The stored scale is the binary16 rounding of the pinned fp32 group scale; a scale that rounds to 0
+    is stored as the smallest subnormal."""
+    d = workloads.ffn7b(ms=(1,))
+    w = d["w"][:64, :512]
+    _, s32, _ = oracle.quantize(w, 4, sym, oracle.GROUP, 128)
+    _, s16, _ = oracle.quantize_meta16(w, sym, 128)
+    assert np.array_equal(s16, s32.astype(np.float16).view(np.uint16))
+    tiny = np.full((1, 32), 1e-9, np.float32)
+    _, st, _ = oracle.quantize_meta16(tiny, True, 32)
+    assert st[0] == 0x0001
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_meta16_codes_equal_fp32_path_when_the_scale_is_exact(sym):
+    """Groups whose fp32 scale is exact in binary16 get the codes (and zero points) of the pinned fp32 path."""
+    rng = np.random.default_rng(31)
+    x = rng.uniform(-0.8, 0.8, (16, 256)).astype(np.float32)
+    x.reshape(-1, 32)[:, 0] = 7 * 2.0 ** -3 if sym else -1.5  # symmetric: s = 2^-3 exactly
+    x.reshape(-1, 32)[:, 1] = -7 * 2.0 ** -3 if sym else 2.25  # asymmetric: s = (2.25 + 1.5) / 15 = 0.25
+    q32, s32, z32 = oracle.quantize(x, 4, sym, oracle.GROUP, 32)
+    q16, s16, z16 = oracle.quantize_meta16(x, sym, 32)
+    assert np.array_equal(oracle.f16_to_f32(s16), s32)
+    assert np.array_equal(q16, q32)
+    if not sym:
+        assert np.array_equal(z16, z32)
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_meta16_error_bound(sym):
+    """s16 (q - z) is within s16 / 2 of every unclamped input [P1 core formula]."""
+    d = workloads.ffn7b(ms=(1,))
+    w = workloads.bf16_to_f32(d["w"][:32, :1024])
+    q, s16, z = oracle.quantize_meta16(w, sym, 64)
+    s = np.repeat(oracle.f16_to_f32(s16), 64).reshape(w.shape).astype(np.float64)
+    zz = 0 if sym else np.repeat(z, 64).reshape(w.shape).astype(np.float64)
+    err = np.abs(s * (q - zz) - w)
+    inner = (q > (-7 if sym else 0)) & (q < (7 if sym else 15))
+    assert np.all((err <= s / 2 * (1 + 2.0 ** -20) + np.abs(w) * 2.0 ** -22)[inner])
+
+
+def test_metadata_share_matches_the_pages():
+    """With binary16 scales the metadata of INT4 weights is 1/32 of the code bytes at g = 128 (the pages: about
+    3 %) and 1/8 at g = 32 (about 13 %) [P3 §11.3.7; P1 §1.1: 3-5 % and 10-15 %]; fp32 scales double it."""
+    w = np.zeros((64, 1024), np.float32)
+    w[:, ::7] = 1.0
+    codes_bytes = oracle.pack_int4(oracle.quantize_meta16(w, True, 128)[0]).nbytes
+    for g, pages in ((128, 0.03), (32, 0.13)):
+        _, s16, _ = oracle.quantize_meta16(w, True, g)
+        _, s32, _ = oracle.quantize(w, 4, True, oracle.GROUP, g)
+        share16 = s16.nbytes / codes_bytes
+        assert abs(share16 - pages) < 0.006
+        assert s32.nbytes / codes_bytes == 2 * share16
+
+
+def test_pack_zeros4_round_trip():
+    """Packed zero points (two per byte) unpack to the zero points, odd counts included."""
+    rng = np.random.default_rng(32)
+    for n in (6, 7, 129):
+        z = rng.integers(0, 16, n).astype(np.uint8)
+        p = oracle.pack_zeros4(z)
+        assert p.size == (n + 1) // 2
+        lo, hi = p & 0xF, p >> 4
+        assert np.array_equal(np.stack([lo, hi], 1).ravel()[:n], z)
