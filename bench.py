@@ -7,8 +7,9 @@ One step is one pass over every stage of the quantized linear layer on synthetic
              INT4, g = 128, packed                                                  (range, scale, codes, pack)
   dequantize the packed layer back to bf16                                          (standalone dequantize)
   w4a16_m1   the seven projections at batch 1 (decode)       <- the headline weight-stream GB/s
-             (every third step instead: the same weights as four launches, q|k|v and gate|up stored as
-             concatenated matrices sharing their input, as serving engines store them; reported apart)
+             (one step in four instead: the same weights as four launches, q|k|v and gate|up stored as
+             concatenated matrices sharing their input, as serving engines store them; and one step in four
+             a third copy of the layer with 16-bit metadata: binary16 scales; both reported apart)
   w4a16_m32  the seven projections at batch 32
   w4a16_m8   the seven projections at batch 8
   smooth     SmoothQuant factor, alpha = 0.5, X 2048x4096 (41 channels x50), W 11008x4096
@@ -132,7 +133,8 @@ def main():
             r0 += n
             for c in range(2):
                 pqg.quantize(w, 4, True, pqg.GROUP, 128, out=(packed[c], scales[c], None))
-            projs.append(dict(name=name, n=n, k=k, w=w, x=x, packed=packed, scales=scales,
+            packed16, s16, _ = pqg.quantize_meta16(w, True, 128)  # the third copy, 16-bit metadata
+            projs.append(dict(name=name, n=n, k=k, w=w, x=x, packed=packed, scales=scales, packed16=packed16, s16=s16,
                               y1=torch.empty((1, n), dtype=torch.bfloat16, device=dev),
                               y8=torch.empty((8, n), dtype=torch.bfloat16, device=dev),
                               y32=torch.empty((32, n), dtype=torch.bfloat16, device=dev)))
@@ -173,6 +175,7 @@ def main():
     setup_s = time.time() - t_setup
 
     gemv_bytes = sum(p["n"] * p["k"] // 2 + p["n"] * (p["k"] // 128) * 4 for p in projs)
+    gemv_bytes16 = sum(p["n"] * p["k"] // 2 + p["n"] * (p["k"] // 128) * 2 for p in projs)
     gemv_bytes_total = gemv_bytes + sum(p["k"] * 2 + p["n"] * 2 for p in projs)  # + x and y
     w8a8_ops = 2.0 * M8 * N8 * K8
 
@@ -253,12 +256,16 @@ def main():
         if rec:
             marks["w4a16_m8"] = ev()
             marks["w4a16_m8"].record(stream)
-        # The decode pass takes one of three forms by step: the seven launches back to back (mode 0: the
+        # The decode pass takes one of four forms by step: the seven launches back to back (mode 0: the
         # sequence time, value), the same with events between the launches (mode 1: per-kernel durations;
-        # the events break back-to-back dispatch), or the four launches of the concatenated layout (mode 2).
-        mode = i % 3
+        # the events break back-to-back dispatch), the four launches of the concatenated layout (mode 2), or
+        # the seven launches over the copy with 16-bit metadata (mode 3).
+        mode = i % 4
         gemv_ev = []
-        if mode == 2:
+        if mode == 3:
+            for p in projs:  # S6 with binary16 scales
+                pqg.qlinear_w4a16_meta16(p["x"][:1], p["packed16"], p["s16"], None, 128, True, out=p["y1"])
+        elif mode == 2:
             for f in fused:  # S6 over the concatenated layout
                 pqg.qlinear_w4a16(f["x"][:1], f["packed"][c], f["scales"][c], None, 128, True, out=f["y1"])
         else:
@@ -292,6 +299,7 @@ def main():
     gemv_launch_ms = []
     gemv_seq_ms = []
     fused_seq_ms = []
+    meta16_seq_ms = []
     for marks, gemv_ev, mode in records:
         prev = marks["start"]
         for k in parts:
@@ -301,6 +309,8 @@ def main():
                 per_part[k].append(t)
             elif mode == 2:
                 fused_seq_ms.append(t)
+            elif mode == 3:
+                meta16_seq_ms.append(t)
         if mode == 1:  # per-launch kernel durations
             gemv_launch_ms.append([a.elapsed_time(b) for a, b in gemv_ev])
     gemv_seq_ms = per_part["w4a16_m1"]  # mode 0: the seven launches back to back, between the surrounding marks
@@ -391,6 +401,11 @@ def main():
                         "calibrated_scale": s_static},
         # the same decode weight stream as four launches (q|k|v, o, gate|up, down), each group stored as one
         # concatenated matrix and sharing its input
+        # the same decode pass over a third copy of the layer quantized with 16-bit metadata (binary16 scales;
+        # the codes use the stored scales), as weight-stream GB/s over its own bytes
+        "w4a16_m1_meta16": {"bytes": gemv_bytes16,
+                            "value": round(gemv_bytes16 / (med(meta16_seq_ms) * 1e-3) / 1e9, 1) if meta16_seq_ms else None,
+                            "unit": "GB/s", "ms": round(med(meta16_seq_ms), 4) if meta16_seq_ms else None},
         "w4a16_m1_fused_layout": {"launches": ["+".join(W.L70B_PROJ[i][0] for i in g) for g in groups],
                                   "value": round(gemv_bytes / (med(fused_seq_ms) * 1e-3) / 1e9, 1),
                                   "unit": "GB/s",

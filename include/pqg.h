@@ -275,6 +275,45 @@ int32_t pqg_kv_append(const void *k_new, const void *v_new, int32_t dtype, int64
                       int32_t symmetric, void *k_residual, void *k_codes, float *k_scales, uint8_t *k_zeros,
                       void *v_codes, float *v_scales, uint8_t *v_zeros, void *stream);
 
+/*
+ * INT4 group quantization with 16-bit metadata [P1 §1.1 and P3 §11.3.7: one 16-bit scale per group, about 3 %
+ * of the INT4 weight bytes at g = 128 and 13 % at g = 32; the fp32 scales of pqg_quantize take twice that].
+ * Per group of group_size consecutive elements of a row: the range and (s, z) exactly as pqg_quantize (bits 4,
+ * PQG_GROUP); the scale is stored as binary16 s16 = fp16(s), round to nearest even (a result of 0 becomes the
+ * smallest subnormal 2^-24, an overflow the largest finite 65504); the codes and the asymmetric zero point use
+ * the stored scale: q = clamp(rne(x / s16) + z), z = clamp(rne(-lo / s16)), so s16 (q - z) is what the
+ * metadata encodes.
+ *   x        : [rows, cols] bf16 or fp32 (x_dtype). cols % group_size == 0; group_size in {32, 64, 128}.
+ *   codes    : packed INT4 [rows, cols / 2], as pqg_quantize writes them (out).
+ *   scales16 : binary16 bits [rows * cols / group_size], row-major, the group index fastest (out).
+ *   zeros4   : asymmetric zero points two per byte over the flattened group index e: byte e / 2, low nibble
+ *              for even e; (rows * cols / group_size + 1) / 2 bytes; NULL iff symmetric (out).
+ * Alignment: x 16 bytes, codes 4, scales16 2.
+ */
+int32_t pqg_quantize_meta16(const void *x, int32_t x_dtype, int64_t rows, int64_t cols, int32_t symmetric,
+                            int32_t group_size, uint8_t *codes, uint16_t *scales16, uint8_t *zeros4, void *stream);
+
+/*
+ * Dequantization of INT4 groups with 16-bit metadata: out = s16 * (q - z), one fp32 multiply, rounded to
+ * out_dtype [P1 core formula; P3 §11.1.1]. Arguments as pqg_quantize_meta16 writes them; out [rows, cols].
+ * Alignment: codes 4 bytes, scales16 2, out 16.
+ */
+int32_t pqg_dequantize_meta16(const uint8_t *codes, const uint16_t *scales16, const uint8_t *zeros4, int64_t rows,
+                              int64_t cols, int32_t symmetric, int32_t group_size, void *out, int32_t out_dtype,
+                              void *stream);
+
+/*
+ * W4A16 decode with 16-bit metadata: y = x W^T as pqg_qlinear_w4a16, with the weights' scales as binary16 and
+ * asymmetric zero points packed (pqg_quantize_meta16), which halves the metadata bytes the decode stream reads
+ * [P3 §11.1.6, §11.10.1 (decode reads every weight); P3 §11.3.7 (metadata share)].
+ *   M in [0, 4] (the decode kernel; larger M returns PQG_EUNSUPPORTED: the batched kernels are bound by
+ *   compute, not by these bytes). Other arguments as pqg_qlinear_w4a16.
+ * Alignment: x, w_packed 16 bytes; scales16 2; y 4.
+ */
+int32_t pqg_qlinear_w4a16_meta16(const void *x, int64_t M, int64_t N, int64_t K, const uint8_t *w_packed,
+                                 const uint16_t *scales16, const uint8_t *zeros4, int32_t group_size,
+                                 int32_t symmetric, void *y, int32_t y_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,6 +31,7 @@ EXPORTS = [
     "pqg_dequantize",
     "pqg_smooth_workspace_bytes", "pqg_smooth", "pqg_qlinear_w4a16", "pqg_qlinear_w8a8", "pqg_gemm_s8s8s32",
     "pqg_qlinear_w4a8", "pqg_kv_quantize_keys", "pqg_kv_dequantize_keys", "pqg_kv_append",
+    "pqg_quantize_meta16", "pqg_dequantize_meta16", "pqg_qlinear_w4a16_meta16",
 ]
 
 _lib = None
@@ -81,6 +82,12 @@ def load(path: str = LIB_PATH):
     lib.pqg_kv_dequantize_keys.restype = I32
     lib.pqg_kv_dequantize_keys.argtypes = [P, P, P, I64, I64, I32, I32, P, I32, P]
     lib.pqg_kv_append.restype = I32
+    lib.pqg_quantize_meta16.restype = I32
+    lib.pqg_quantize_meta16.argtypes = [P, I32, I64, I64, I32, I32, P, P, P, P]
+    lib.pqg_dequantize_meta16.restype = I32
+    lib.pqg_dequantize_meta16.argtypes = [P, P, P, I64, I64, I32, I32, P, I32, P]
+    lib.pqg_qlinear_w4a16_meta16.restype = I32
+    lib.pqg_qlinear_w4a16_meta16.argtypes = [P, I64, I64, I64, P, P, P, I32, I32, P, I32, P]
     lib.pqg_kv_append.argtypes = [P, P, I32, I64, I64, P, I64, I32, I32, I32, P, P, P, P, P, P, P, P]
     if lib.pqg_abi_version() != ABI_VERSION:
         raise ImportError("libpqg.so ABI %d != binding ABI %d" % (lib.pqg_abi_version(), ABI_VERSION))
@@ -340,3 +347,48 @@ def kv_append(cache: dict, k_new: torch.Tensor, v_new: torch.Tensor, positions: 
                              v_group_size, int(symmetric), _ptr(cache["k_res"]), _ptr(cache["k_q"]),
                              _ptr(cache["k_s"]), _ptr(cache["k_z"]), _ptr(cache["v_q"]), _ptr(cache["v_s"]),
                              _ptr(cache["v_z"]), _stream(dev)))
+
+
+def quantize_meta16(x: torch.Tensor, symmetric: bool, group_size: int, out=None):
+    """pqg_quantize_meta16: INT4 groups with binary16 scales. Returns (codes uint8 [rows, cols / 2], scales16 int16
+    tensor of binary16 bits [rows * cols / g] (view it as torch.float16 for values), zeros4 uint8 or None)."""
+    lib = load()
+    dev = _dev(x)
+    rows, cols = x.shape
+    ng = rows * cols // group_size
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales16 = torch.empty(ng, dtype=torch.float16, device=dev)
+        zeros4 = None if symmetric else torch.empty((ng + 1) // 2, dtype=torch.uint8, device=dev)
+    else:
+        codes, scales16, zeros4 = out
+    _check(lib.pqg_quantize_meta16(_ptr(x), _float_dtype(x), rows, cols, int(symmetric), group_size, _ptr(codes),
+                                   _ptr(scales16), _ptr(zeros4), _stream(dev)))
+    return codes, scales16, zeros4
+
+
+def dequantize_meta16(codes: torch.Tensor, scales16: torch.Tensor, zeros4, rows: int, cols: int, symmetric: bool,
+                      group_size: int, out_dtype=torch.float32, out=None):
+    """pqg_dequantize_meta16 -> [rows, cols] of out_dtype."""
+    lib = load()
+    dev = _dev(codes)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=dev)
+    _check(lib.pqg_dequantize_meta16(_ptr(codes), _ptr(scales16), _ptr(zeros4), rows, cols, int(symmetric),
+                                     group_size, _ptr(out), _float_dtype(out), _stream(dev)))
+    return out
+
+
+def qlinear_w4a16_meta16(x: torch.Tensor, w_packed: torch.Tensor, scales16: torch.Tensor, zeros4, group_size: int,
+                         symmetric: bool, out_dtype=torch.bfloat16, out=None):
+    """pqg_qlinear_w4a16_meta16: decode (M <= 4) with binary16 scales and packed zero points."""
+    lib = load()
+    dev = _dev(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    M, K = x.shape
+    N = w_packed.shape[0]
+    y = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    _check(lib.pqg_qlinear_w4a16_meta16(_ptr(x), M, N, K, _ptr(w_packed), _ptr(scales16), _ptr(zeros4), group_size,
+                                        int(symmetric), _ptr(y), _float_dtype(y), _stream(dev)))
+    return y

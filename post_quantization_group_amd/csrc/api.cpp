@@ -411,4 +411,91 @@ int32_t pqg_kv_append(const void *k_new, const void *v_new, int32_t dtype, int64
     return hip_status(pqg::launch_kv_append(a, as_stream(stream)), "pqg_kv_append launch");
 }
 
+int32_t pqg_quantize_meta16(const void *x, int32_t x_dtype, int64_t rows, int64_t cols, int32_t symmetric,
+                            int32_t group_size, uint8_t *codes, uint16_t *scales16, uint8_t *zeros4, void *stream)
+{
+    g_err[0] = 0;
+    if (!valid_float_dtype(x_dtype))
+        return fail(PQG_EINVAL, "unknown x_dtype %d", x_dtype);
+    if (rows < 0 || cols < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(PQG_EINVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+    if (cols % group_size != 0)
+        return fail(PQG_EINVAL, "cols (%lld) must be a multiple of group_size", (long long)cols);
+    if (rows == 0 || cols == 0)
+        return PQG_OK;
+    if (!x || !codes || !scales16)
+        return fail(PQG_EINVAL, "x, codes and scales16 are required");
+    if (symmetric && zeros4)
+        return fail(PQG_EINVAL, "zeros4 must be NULL for symmetric codes");
+    if (!symmetric && !zeros4)
+        return fail(PQG_EINVAL, "zeros4 is required for asymmetric codes");
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(scales16, 2))
+        return fail(PQG_EINVAL, "misaligned pointer (x: 16 bytes, codes: 4, scales16: 2)");
+    pqg::Meta16Args a{x, x_dtype == PQG_BF16, rows, cols, symmetric != 0, group_size, codes, scales16, zeros4};
+    return hip_status(pqg::launch_quantize_meta16(a, as_stream(stream)), "pqg_quantize_meta16 launch");
+}
+
+int32_t pqg_dequantize_meta16(const uint8_t *codes, const uint16_t *scales16, const uint8_t *zeros4, int64_t rows,
+                              int64_t cols, int32_t symmetric, int32_t group_size, void *out, int32_t out_dtype,
+                              void *stream)
+{
+    g_err[0] = 0;
+    if (!valid_float_dtype(out_dtype))
+        return fail(PQG_EINVAL, "unknown out_dtype %d", out_dtype);
+    if (rows < 0 || cols < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(PQG_EINVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+    if (cols % group_size != 0)
+        return fail(PQG_EINVAL, "cols (%lld) must be a multiple of group_size", (long long)cols);
+    if (rows == 0 || cols == 0)
+        return PQG_OK;
+    if (!codes || !scales16 || !out)
+        return fail(PQG_EINVAL, "codes, scales16 and out are required");
+    if (symmetric && zeros4)
+        return fail(PQG_EINVAL, "zeros4 must be NULL for symmetric codes");
+    if (!symmetric && !zeros4)
+        return fail(PQG_EINVAL, "zeros4 is required for asymmetric codes");
+    if (!aligned(codes, 4) || !aligned(scales16, 2) || !aligned(out, 16))
+        return fail(PQG_EINVAL, "misaligned pointer (codes: 4 bytes, scales16: 2, out: 16)");
+    pqg::Meta16Args a{nullptr, false, rows, cols, symmetric != 0, group_size, const_cast<uint8_t *>(codes),
+                      const_cast<uint16_t *>(scales16), const_cast<uint8_t *>(zeros4)};
+    return hip_status(pqg::launch_dequantize_meta16(a, out, out_dtype == PQG_BF16, as_stream(stream)),
+                      "pqg_dequantize_meta16 launch");
+}
+
+int32_t pqg_qlinear_w4a16_meta16(const void *x, int64_t M, int64_t N, int64_t K, const uint8_t *w_packed,
+                                 const uint16_t *scales16, const uint8_t *zeros4, int32_t group_size,
+                                 int32_t symmetric, void *y, int32_t y_dtype, void *stream)
+{
+    g_err[0] = 0;
+    if (M < 0 || N < 0 || K < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (M > 4)
+        return fail(PQG_EUNSUPPORTED, "16-bit metadata is read by the decode kernel only: M must be at most 4");
+    if (!valid_float_dtype(y_dtype))
+        return fail(PQG_EINVAL, "unknown y_dtype %d", y_dtype);
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(PQG_EINVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+    if (K % group_size != 0)
+        return fail(PQG_EINVAL, "K (%lld) must be a multiple of group_size (%d)", (long long)K, group_size);
+    if (M == 0 || N == 0)
+        return PQG_OK;
+    if (K == 0)
+        return fail(PQG_EUNSUPPORTED, "K == 0");
+    if (!x || !w_packed || !scales16 || !y)
+        return fail(PQG_EINVAL, "x, w_packed, scales16 and y are required");
+    if (symmetric && zeros4)
+        return fail(PQG_EINVAL, "zeros4 must be NULL for symmetric codes");
+    if (!symmetric && !zeros4)
+        return fail(PQG_EINVAL, "zeros4 is required for asymmetric codes");
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(scales16, 2) || !aligned(y, 4))
+        return fail(PQG_EINVAL, "misaligned pointer (x, w_packed: 16 bytes; scales16: 2; y: 4)");
+    pqg::W4A16Args a{static_cast<const uint16_t *>(x), M, N, K, w_packed, nullptr, zeros4, group_size, symmetric != 0,
+                     y, y_dtype == PQG_BF16, true, scales16};
+    return hip_status(pqg::launch_w4a16(a, as_stream(stream)), "pqg_qlinear_w4a16_meta16 launch");
+}
+
 }  // extern "C"

@@ -76,6 +76,8 @@ struct W4A16Args {
     bool symmetric;
     void *y;
     bool y_bf16;
+    bool meta16 = false;                // 16-bit metadata (decode path only): binary16 scales in scales16,
+    const uint16_t *scales16 = nullptr;  // [N, K/g]; zeros then packed two per byte (flattened group index)
 };
 
 struct GemmI8Args {
@@ -116,6 +118,21 @@ struct W4A8Args {
 };
 
 hipError_t launch_w4a8(const W4A8Args &a, hipStream_t st);
+
+// INT4 groups with 16-bit metadata: binary16 scales, zero points two per byte (flattened group index).
+struct Meta16Args {
+    const void *x;  // quantize input [rows, cols] (bf16 or fp32)
+    bool x_bf16;
+    int64_t rows, cols;
+    bool symmetric;
+    int group_size;
+    uint8_t *codes;      // packed [rows, cols / 2]
+    uint16_t *scales16;  // [rows * cols / g] binary16
+    uint8_t *zeros4;     // [(rows * cols / g + 1) / 2], NULL iff symmetric
+};
+
+hipError_t launch_quantize_meta16(const Meta16Args &a, hipStream_t st);
+hipError_t launch_dequantize_meta16(const Meta16Args &a, void *out, bool out_bf16, hipStream_t st);
 
 // KV cache: keys per channel over groups of block_tokens tokens (and their dequantization).
 struct KvKeysArgs {

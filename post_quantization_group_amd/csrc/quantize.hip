@@ -98,6 +98,72 @@ __global__ __launch_bounds__(256) void k_quant_group(const XT *__restrict__ x, c
     }
 }
 
+// ------------------------------------------------------------------ per-group, 16-bit metadata
+//
+// INT4 groups with binary16 scales and zero points packed two per byte ("第11章 模型量化与压缩" §11.3.7 and
+// the atlas's §1.1 count one 16-bit scale per group). The group's (s, z) as above; the scale is stored as the
+// nearest-even binary16 (0 -> the smallest subnormal, overflow -> the largest finite value), and the codes and
+// the asymmetric zero point are computed with the stored scale, so that s16 (q - z) is what the metadata encodes.
+template <bool SYM>
+__device__ __forceinline__ uint16_t meta16_params(SegParams &p, float lo)
+{
+    uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)p.s);
+    if ((h & 0x7FFFu) == 0)
+        h = 0x0001u;
+    else if ((h & 0x7C00u) == 0x7C00u)
+        h = 0x7BFFu;
+    p.s = (float)__builtin_bit_cast(_Float16, h);
+    p.r = 1.0f / p.s;
+    if (!SYM) {
+        const float l = lo > 0.0f ? 0.0f : lo;
+        p.z = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(-l / p.s), 0.0f), 15.0f);
+    }
+    return h;
+}
+
+// One thread per chunk of 8 as k_quant_group; the zero points of groups 2i and 2i + 1 (LPG lanes apart, in one
+// wave) are combined by the first group's leader into byte i.
+template <typename XT, bool SYM, int G>
+__global__ __launch_bounds__(256) void k_quant_group16(const XT *__restrict__ x, int64_t n_chunks,
+                                                       uint8_t *__restrict__ codes, uint16_t *__restrict__ scales16,
+                                                       uint8_t *__restrict__ zeros4)
+{
+    constexpr int LPG = G / 8;
+    static_assert(2 * LPG <= kWave, "a pair of groups lies in one wave");
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = c < n_chunks;  // groups are wholly in or out of range (n_chunks % LPG == 0)
+    float v[8];
+    if (live)
+        load8<XT>(x + c * 8, v);
+    else
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = 0.0f;
+    float absmax = 0.0f, lo = v[0], hi = v[0];
+    range8<SYM>(v, absmax, lo, hi);
+    if (SYM) {
+        absmax = wave_max<LPG>(absmax);
+    } else {
+        lo = wave_min<LPG>(lo);
+        hi = wave_max<LPG>(hi);
+    }
+    SegParams p = seg_params<4, SYM>(absmax, lo, hi);
+    const uint16_t h = meta16_params<SYM>(p, lo);
+    const int zn = __shfl_down((int)p.z, LPG, kWave);  // the next group's zero point (leader lanes only)
+    if (!live)
+        return;
+    store_codes8<4>(v, p, codes, c * 8);
+    if ((c % LPG) == 0) {
+        const int64_t e = c / LPG;
+        scales16[e] = h;
+        if (!SYM && (e % 2) == 0) {
+            const int64_t ngroups = n_chunks / LPG;
+            const uint32_t hi4 = e + 1 < ngroups ? (uint32_t)zn : 0u;
+            zeros4[e / 2] = (uint8_t)((uint32_t)p.z | (hi4 << 4));
+        }
+    }
+}
+
 // ------------------------------------------------------------------ per-row
 
 constexpr int kRowCache = 8;  // chunks of 8 kept in registers per thread: cols <= 1024 * 8 * 8
@@ -310,6 +376,36 @@ __global__ __launch_bounds__(256) void k_dequant(const void *__restrict__ codes,
     }
 }
 
+// INT4 groups with binary16 scales and packed zero points back to fp32 / bf16.
+template <bool SYM, bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_dequant16(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales16,
+                                                   const uint8_t *__restrict__ zeros4, int64_t n_chunks, int group_size,
+                                                   void *__restrict__ out)
+{
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= n_chunks)
+        return;
+    const int64_t seg = c * 8 / group_size;
+    const float s = (float)__builtin_bit_cast(_Float16, scales16[seg]);
+    const int z = SYM ? 0 : (int)((zeros4[seg / 2] >> (4 * (seg % 2))) & 0xFu);
+    const uint32_t w = reinterpret_cast<const uint32_t *>(codes)[c];
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int nib = (int)((w >> (4 * i)) & 0xFu);
+        const int q = (SYM && nib >= 8) ? nib - 16 : nib;
+        v[i] = s * (float)(q - z);
+    }
+    if (OUT_BF16) {
+        reinterpret_cast<uint4 *>(out)[c] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    } else {
+        float4 *o = reinterpret_cast<float4 *>(out) + 2 * c;
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
 // ------------------------------------------------------------------ host-side dispatch
 
 namespace {
@@ -445,6 +541,54 @@ hipError_t static_type(const StaticQuantArgs &a, hipStream_t st)
 hipError_t launch_quantize_static(const StaticQuantArgs &a, hipStream_t st)
 {
     return a.x_bf16 ? static_type<uint16_t>(a, st) : static_type<float>(a, st);
+}
+
+namespace {
+
+template <typename XT, bool SYM>
+hipError_t quant16_go(const Meta16Args &a, hipStream_t st)
+{
+    const int64_t n_chunks = a.rows * a.cols / 8;
+    const unsigned nb = nblocks(n_chunks, 256);
+    const XT *x = static_cast<const XT *>(a.x);
+    switch (a.group_size) {
+    case 32:
+        k_quant_group16<XT, SYM, 32><<<nb, 256, 0, st>>>(x, n_chunks, a.codes, a.scales16, a.zeros4);
+        break;
+    case 64:
+        k_quant_group16<XT, SYM, 64><<<nb, 256, 0, st>>>(x, n_chunks, a.codes, a.scales16, a.zeros4);
+        break;
+    default:
+        k_quant_group16<XT, SYM, 128><<<nb, 256, 0, st>>>(x, n_chunks, a.codes, a.scales16, a.zeros4);
+        break;
+    }
+    return hipGetLastError();
+}
+
+template <bool SYM>
+hipError_t dequant16_go(const Meta16Args &a, void *out, bool out_bf16, hipStream_t st)
+{
+    const int64_t n_chunks = a.rows * a.cols / 8;
+    const unsigned nb = nblocks(n_chunks, 256);
+    if (out_bf16)
+        k_dequant16<SYM, true><<<nb, 256, 0, st>>>(a.codes, a.scales16, a.zeros4, n_chunks, a.group_size, out);
+    else
+        k_dequant16<SYM, false><<<nb, 256, 0, st>>>(a.codes, a.scales16, a.zeros4, n_chunks, a.group_size, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_meta16(const Meta16Args &a, hipStream_t st)
+{
+    if (a.x_bf16)
+        return a.symmetric ? quant16_go<uint16_t, true>(a, st) : quant16_go<uint16_t, false>(a, st);
+    return a.symmetric ? quant16_go<float, true>(a, st) : quant16_go<float, false>(a, st);
+}
+
+hipError_t launch_dequantize_meta16(const Meta16Args &a, void *out, bool out_bf16, hipStream_t st)
+{
+    return a.symmetric ? dequant16_go<true>(a, out, out_bf16, st) : dequant16_go<false>(a, out, out_bf16, st);
 }
 
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t st)

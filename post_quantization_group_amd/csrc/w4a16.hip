@@ -77,16 +77,18 @@ struct Stage {
     uint4 x[MT][4];
 };
 
-// Uniform (per block) base pointers of the R weight rows, their metadata and the MT activation rows.
+// Uniform (per block) base pointers of the R weight rows, their metadata and the MT activation rows. With
+// 16-bit metadata s points at binary16 scales, z at the packed zero points and zr is the row's first group.
 template <int MT, int R>
 struct Bases {
     const uint8_t *w[R];
-    const float *s[R];
+    const void *s[R];
     const uint8_t *z[R];
+    int64_t zr[R];
     const uint16_t *x[MT];
 };
 
-template <int MT, int R, int G, bool SYM>
+template <int MT, int R, int G, bool SYM, bool M16>
 __device__ __forceinline__ void stage_load(Stage<MT, R> &st, const Bases<MT, R> &b, uint32_t c)
 {
     constexpr int kGroupShift = (G == 128) ? 2 : (G == 64) ? 1 : 0;  // chunk -> group index
@@ -98,8 +100,14 @@ __device__ __forceinline__ void stage_load(Stage<MT, R> &st, const Bases<MT, R> 
     const uint32_t gi = c >> kGroupShift;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        st.s[r] = b.s[r][gi];
-        st.z[r] = SYM ? 8.0f : (float)b.z[r][gi];
+        if (M16) {
+            st.s[r] = (float)static_cast<const _Float16 *>(b.s[r])[gi];
+            const int64_t e = b.zr[r] + gi;
+            st.z[r] = SYM ? 8.0f : (float)((b.z[r][e >> 1] >> (4 * (e & 1))) & 0xFu);
+        } else {
+            st.s[r] = static_cast<const float *>(b.s[r])[gi];
+            st.z[r] = SYM ? 8.0f : (float)b.z[r][gi];
+        }
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -162,9 +170,9 @@ __device__ __forceinline__ void stage_compute(const Stage<MT, R> &st, float acc[
 }
 
 // MT activation rows (1..4), R weight rows per block, group size G; S = blockDim.x / 64 waves split K.
-template <int MT, int R, int G, bool SYM, bool OUT_BF16>
+template <int MT, int R, int G, bool SYM, bool OUT_BF16, bool M16 = false>
 __global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__ x, int64_t N, int64_t K,
-                                                    const uint8_t *__restrict__ w, const float *__restrict__ scales,
+                                                    const uint8_t *__restrict__ w, const void *__restrict__ scales,
                                                     const uint8_t *__restrict__ zeros, void *__restrict__ y,
                                                     int64_t y_ld)
 {
@@ -186,8 +194,15 @@ __global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__
     for (int r = 0; r < R; ++r) {
         const int64_t row = row0 + r < N ? row0 + r : N - 1;  // rows past N read row N-1, never stored
         bp.w[r] = w + row * (K / 2);
-        bp.s[r] = scales + row * (K / G);
-        bp.z[r] = SYM ? nullptr : zeros + row * (K / G);
+        if (M16) {
+            bp.s[r] = static_cast<const uint16_t *>(scales) + row * (K / G);
+            bp.z[r] = zeros;
+            bp.zr[r] = row * (K / G);
+        } else {
+            bp.s[r] = static_cast<const float *>(scales) + row * (K / G);
+            bp.z[r] = SYM ? nullptr : zeros + row * (K / G);
+            bp.zr[r] = 0;
+        }
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -205,7 +220,7 @@ __global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__
     Stage<MT, R> st[2];
     auto step = [&](int h, int it) {
         const int cn = c_begin + lane + kWave * (it + 1);
-        stage_load<MT, R, G, SYM>(st[h ^ 1], bp, (uint32_t)(cn < c_last ? cn : c_last));
+        stage_load<MT, R, G, SYM, M16>(st[h ^ 1], bp, (uint32_t)(cn < c_last ? cn : c_last));
         __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads stay ahead of this chunk's math
         const bool ok = c_begin + lane + kWave * it < c_end;
 #pragma unroll
@@ -216,7 +231,7 @@ __global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__
     };
     {
         const int c = c_begin + lane;
-        stage_load<MT, R, G, SYM>(st[0], bp, (uint32_t)(c < c_last ? c : c_last));
+        stage_load<MT, R, G, SYM, M16>(st[0], bp, (uint32_t)(c < c_last ? c : c_last));
     }
     int it = 0;
     for (; it + 2 <= iters; it += 2) {
@@ -770,7 +785,14 @@ hipError_t gemv_launch(const W4A16Args &a, const uint16_t *x, void *y, hipStream
     const int64_t rowblocks = (a.N + R - 1) / R;
     const int S = waves_per_row_block(rowblocks, a.K, 4096);
     const dim3 grid((unsigned)rowblocks), block(kWave * S);
-    if (a.y_bf16)
+    if (a.meta16) {
+        if (a.y_bf16)
+            k_w4a16_gemv<MT, R, G, SYM, true, true><<<grid, block, 0, st>>>(x, a.N, a.K, a.w, a.scales16, a.zeros, y,
+                                                                           a.N);
+        else
+            k_w4a16_gemv<MT, R, G, SYM, false, true><<<grid, block, 0, st>>>(x, a.N, a.K, a.w, a.scales16, a.zeros, y,
+                                                                            a.N);
+    } else if (a.y_bf16)
         k_w4a16_gemv<MT, R, G, SYM, true><<<grid, block, 0, st>>>(x, a.N, a.K, a.w, a.scales, a.zeros, y, a.N);
     else
         k_w4a16_gemv<MT, R, G, SYM, false><<<grid, block, 0, st>>>(x, a.N, a.K, a.w, a.scales, a.zeros, y, a.N);
@@ -898,6 +920,8 @@ constexpr int64_t kStagedMaxTokens = 64;
 hipError_t launch_w4a16(const W4A16Args &a, hipStream_t st)
 {
     const size_t ysz = a.y_bf16 ? 2 : 4;
+    if (a.meta16 && a.M >= kMfmaMinTokens)
+        return hipErrorInvalidValue;  // 16-bit metadata: the vector (decode) kernel only
     // the staged kernel works in 128-code steps and addresses scales through 32-bit buffer offsets (and,
     // with zero points, reads them four bytes at a time from an array of at least four)
     const int64_t groups = a.K / a.group_size;

@@ -188,3 +188,29 @@ def test_kv_append_rejects(lib):
         assert call(**kw) == pqg.EINVAL, kw
         assert needle in lib.pqg_last_error().decode(), kw
     assert call(B=0, kn=None, vn=None, pos=None) == pqg.OK
+
+
+def test_meta16_rejects(lib):
+    def quant(**kw):
+        a = dict(x=FAKE, xd=1, r=64, c=1024, sym=1, g=128, q=FAKE, s=FAKE, z=None)
+        a.update(kw)
+        return lib.pqg_quantize_meta16(a["x"], a["xd"], a["r"], a["c"], a["sym"], a["g"], a["q"], a["s"], a["z"], None)
+    for kw, needle in [(dict(g=96), "group_size"), (dict(c=1000), "multiple of group_size"),
+                       (dict(sym=0), "zeros4 is required"), (dict(z=FAKE), "must be NULL"), (dict(xd=4), "x_dtype"),
+                       (dict(q=None), "required"), (dict(x=MISALIGNED), "misaligned"), (dict(r=-1), "negative")]:
+        assert quant(**kw) == pqg.EINVAL, kw
+        assert needle in lib.pqg_last_error().decode(), kw
+
+    def lin(**kw):
+        a = dict(x=FAKE, M=1, N=64, K=1024, w=FAKE, s=FAKE, z=None, g=128, sym=1, y=FAKE, yd=1)
+        a.update(kw)
+        return lib.pqg_qlinear_w4a16_meta16(a["x"], a["M"], a["N"], a["K"], a["w"], a["s"], a["z"], a["g"], a["sym"],
+                                            a["y"], a["yd"], None)
+    assert lin(M=5) == pqg.EUNSUPPORTED
+    assert "decode kernel only" in lib.pqg_last_error().decode()
+    for kw, needle in [(dict(g=48), "group_size"), (dict(K=1000), "multiple of group_size"),
+                       (dict(sym=0), "zeros4 is required"), (dict(s=None), "required"),
+                       (dict(w=MISALIGNED), "misaligned"), (dict(yd=7), "y_dtype")]:
+        assert lin(**kw) == pqg.EINVAL, kw
+        assert needle in lib.pqg_last_error().decode(), kw
+    assert lin(M=0, x=None, w=None, s=None, y=None) == pqg.OK

@@ -651,6 +651,85 @@ def test_kv_keys_full_size_sampled(gpu_lib):
                 assert np.array_equal(z[b].cpu().numpy(), zo[0])
 
 
+# --------------------------------------------------------------------------- 16-bit metadata
+
+
+@pytest.mark.parametrize("shape,gs", [((64, 1024), 128), ((77, 384), 64), ((3, 96), 32), ((130, 2048), 32)])
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_meta16_quantize_bitexact(gpu_lib, shape, gs, sym, dtype):
+    """Codes, binary16 scales and packed zero points bit-exact (odd group counts included)."""
+    announce("meta16 quantize %s g=%d sym=%s %s" % (shape, gs, sym, dtype))
+    rng = np.random.default_rng(shape[0] * 7 + gs)
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    w[rng.random(shape) < 0.005] *= 20
+    src = W.bf16_bits(w) if dtype == "bf16" else w
+    xg = to_gpu_bf16(src) if dtype == "bf16" else to_gpu(src)
+    codes, s16, z4 = gpu_lib.quantize_meta16(xg, sym, gs)
+    torch.cuda.synchronize()
+    q, so, zo = oracle.quantize_meta16(src, sym, gs)
+    assert np.array_equal(codes.cpu().numpy(), oracle.pack_int4(q))
+    assert np.array_equal(s16.cpu().numpy().view(np.uint16), so)
+    if not sym:
+        assert np.array_equal(z4.cpu().numpy(), oracle.pack_zeros4(zo))
+
+
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_meta16_dequant_bitexact(gpu_lib, sym, out):
+    announce("meta16 dequant sym=%s %s" % (sym, out))
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((48, 768)) * 0.02).astype(np.float32)
+    q, so, zo = oracle.quantize_meta16(w, sym, 32)
+    xh = gpu_lib.dequantize_meta16(to_gpu(oracle.pack_int4(q)), to_gpu(so.view(np.float16)),
+                                   None if sym else to_gpu(oracle.pack_zeros4(zo)), 48, 768, sym, 32,
+                                   out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    r32, r16 = oracle.dequantize(q, oracle.f16_to_f32(so), zo, oracle.GROUP, 32)
+    if out == "bf16":
+        assert np.array_equal(bf16_tensor_bits(xh), r16)
+    else:
+        assert np.array_equal(xh.cpu().numpy().view(np.uint32), r32.view(np.uint32))
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("nk,gs", [((1000, 4096), 128), ((257, 2048), 32), ((64, 384), 64)])
+@pytest.mark.parametrize("sym", [True, False])
+def test_meta16_gemv(gpu_lib, m, nk, gs, sym):
+    """Decode with binary16 scales and packed zero points against the W4A16 reference on the stored values."""
+    n, k = nk
+    announce("meta16 gemv m=%d %s g=%d sym=%s" % (m, nk, gs, sym))
+    rng = np.random.default_rng(n + k + m)
+    w = W.bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    x = W.bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    codes, s16, z4 = gpu_lib.quantize_meta16(to_gpu_bf16(w), sym, gs)
+    y = gpu_lib.qlinear_w4a16_meta16(to_gpu_bf16(x), codes, s16, z4, gs, sym, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    q, so, zo = oracle.quantize_meta16(w, sym, gs)
+    y_ref = oracle.w4a16(x, q, oracle.f16_to_f32(so), zo, gs)
+    err = normwise(to_f64(y), y_ref)
+    assert err <= TOL_F32, err
+
+
+def test_meta16_gemv_70b_gate(gpu_lib):
+    """The 70B layer's gate projection (28672 x 8192, INT4 g = 128) at M = 1 with 16-bit metadata: codes and
+    scales bit-exact on sampled rows, the output within tolerance on those rows."""
+    announce("meta16 gemv 70b gate")
+    rows = np.sort(np.random.default_rng(9).choice(28672, 256, replace=False))
+    wg = to_gpu_bf16(W.l70b_weight(4))
+    x = W.l70b_x(4, 1)
+    codes, s16, _ = gpu_lib.quantize_meta16(wg, True, 128)
+    y = gpu_lib.qlinear_w4a16_meta16(to_gpu_bf16(x), codes, s16, None, 128, True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    wr = W.l70b_weight(4, rows)
+    q, so, _ = oracle.quantize_meta16(wr, True, 128)
+    assert np.array_equal(codes.cpu().numpy()[rows], oracle.pack_int4(q))
+    assert np.array_equal(s16.cpu().numpy().view(np.uint16).reshape(28672, 64)[rows].ravel(), so)
+    y_ref = oracle.w4a16(x, q, oracle.f16_to_f32(so), None, 128)
+    err = normwise(to_f64(y)[:, rows], y_ref)
+    assert err <= TOL_F32, err
+
+
 # --------------------------------------------------------------------------- determinism
 
 def test_reruns_are_bit_identical(gpu_lib):
