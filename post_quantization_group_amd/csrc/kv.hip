@@ -54,16 +54,17 @@ __device__ __forceinline__ void stats_add(float *am, float *lo, float *hi, const
 // xor shuffles, then over the four waves through LDS (max and min are exact in any order).
 constexpr int kKvCols = 64, kKvThreads = 256, kKvRows = kKvThreads / 8;
 
-// Per-channel parameters of a tile of rows x 64 channels held by 256 threads as 32 row lanes x 8 channel lanes
-// (thread tid: channels 8 (tid % 8) .. + 7): the thread's partial ranges are combined over the wave's 8 row
-// lanes by xor shuffles, then over the four waves through `red` (max and min are exact in any order).
-template <bool SYM>
-__device__ __forceinline__ void tile_params(float *am, float *lo, float *hi, float (*red)[kKvThreads / kWave][kKvCols],
+// Per-channel parameters of a tile of rows x CW channels held by 256 threads as 256 / LR row lanes x LR = CW / 8
+// channel lanes (thread tid: channels 8 (tid % LR) .. + 7): the thread's partial ranges are combined over the
+// wave's row lanes by xor shuffles, then over the four waves through `red` (max and min are exact in any order).
+template <bool SYM, int CW = kKvCols>
+__device__ __forceinline__ void tile_params(float *am, float *lo, float *hi, float (*red)[kKvThreads / kWave][CW],
                                             SegParams *p)
 {
-    const int tid = threadIdx.x, lr = tid % 8;
+    constexpr int LR = CW / 8;
+    const int tid = threadIdx.x, lr = tid % LR;
 #pragma unroll
-    for (int off = 8; off < kWave; off <<= 1)
+    for (int off = LR; off < kWave; off <<= 1)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             am[j] = __builtin_fmaxf(am[j], __shfl_xor(am[j], off, kWave));
@@ -71,7 +72,7 @@ __device__ __forceinline__ void tile_params(float *am, float *lo, float *hi, flo
             hi[j] = __builtin_fmaxf(hi[j], __shfl_xor(hi[j], off, kWave));
         }
     const int wv = tid / kWave;
-    if (tid % kWave < 8)
+    if (tid % kWave < LR)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             red[0][wv][lr * 8 + j] = am[j];
@@ -92,29 +93,30 @@ __device__ __forceinline__ void tile_params(float *am, float *lo, float *hi, flo
     }
 }
 
-// Block (group b, 64 channels): a thread keeps its T / 32 rows of 8 values in registers, so the group is read
-// once and written once.
-template <typename XT, bool SYM, int T>
+// Block (group b, CW channels): a thread keeps its rows of 8 values in registers, so the group is read once and
+// written once. With CW = 128 a row's 16 lanes read 256 bytes (bf16) and write whole 128-byte lines of codes.
+template <typename XT, bool SYM, int T, int CW>
 __global__ __launch_bounds__(kKvThreads) void k_kv_keys(const XT *__restrict__ x, int64_t channels,
                                                         void *__restrict__ codes, float *__restrict__ scales,
                                                         uint8_t *__restrict__ zeros)
 {
-    constexpr int RP = T / kKvRows;  // rows per thread
-    __shared__ float red[3][kKvThreads / kWave][kKvCols];
+    constexpr int LR = CW / 8, ROWS = kKvThreads / LR, RP = T / ROWS;  // lanes per row, rows per pass, per thread
+    static_assert(RP >= 1 && RP * ROWS == T, "whole rows per thread");
+    __shared__ float red[3][kKvThreads / kWave][CW];
     const int64_t b = blockIdx.x;
-    const int tid = threadIdx.x, lr = tid % 8, r0 = tid / 8;
-    const int64_t c0 = (int64_t)blockIdx.y * kKvCols + lr * 8;
+    const int tid = threadIdx.x, lr = tid % LR, r0 = tid / LR;
+    const int64_t c0 = (int64_t)blockIdx.y * CW + lr * 8;
     float v[RP][8];
 #pragma unroll
     for (int i = 0; i < RP; ++i)
-        load8<XT>(x + (b * T + r0 + kKvRows * i) * channels + c0, v[i]);
+        load8<XT>(x + (b * T + r0 + ROWS * i) * channels + c0, v[i]);
     float am[8], lo[8], hi[8];
     stats_init<SYM>(am, lo, hi, v[0]);
 #pragma unroll
     for (int i = 1; i < RP; ++i)
         stats_add<SYM>(am, lo, hi, v[i]);
     SegParams p[8];
-    tile_params<SYM>(am, lo, hi, red, p);
+    tile_params<SYM, CW>(am, lo, hi, red, p);
     if (r0 == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -125,30 +127,39 @@ __global__ __launch_bounds__(kKvThreads) void k_kv_keys(const XT *__restrict__ x
     }
 #pragma unroll
     for (int i = 0; i < RP; ++i)
-        *reinterpret_cast<uint2 *>(static_cast<int8_t *>(codes) + (b * T + r0 + kKvRows * i) * channels + c0) =
+        *reinterpret_cast<uint2 *>(static_cast<int8_t *>(codes) + (b * T + r0 + ROWS * i) * channels + c0) =
             codes8(v[i], p);
 }
 
-template <typename XT, bool SYM>
-hipError_t keys_go(const KvKeysArgs &a, hipStream_t st)
+template <typename XT, bool SYM, int CW>
+hipError_t keys_cw(const KvKeysArgs &a, hipStream_t st)
 {
-    const dim3 grid((unsigned)(a.tokens / a.block_tokens), (unsigned)(a.channels / kKvCols)), block(kKvThreads);
+    const dim3 grid((unsigned)(a.tokens / a.block_tokens), (unsigned)(a.channels / CW)), block(kKvThreads);
     const XT *x = static_cast<const XT *>(a.x);
     switch (a.block_tokens) {
     case 32:
-        k_kv_keys<XT, SYM, 32><<<grid, block, 0, st>>>(x, a.channels, a.codes, a.scales, a.zeros);
+        k_kv_keys<XT, SYM, 32, CW><<<grid, block, 0, st>>>(x, a.channels, a.codes, a.scales, a.zeros);
         break;
     case 64:
-        k_kv_keys<XT, SYM, 64><<<grid, block, 0, st>>>(x, a.channels, a.codes, a.scales, a.zeros);
+        k_kv_keys<XT, SYM, 64, CW><<<grid, block, 0, st>>>(x, a.channels, a.codes, a.scales, a.zeros);
         break;
     case 128:
-        k_kv_keys<XT, SYM, 128><<<grid, block, 0, st>>>(x, a.channels, a.codes, a.scales, a.zeros);
+        k_kv_keys<XT, SYM, 128, CW><<<grid, block, 0, st>>>(x, a.channels, a.codes, a.scales, a.zeros);
         break;
     default:
-        k_kv_keys<XT, SYM, 256><<<grid, block, 0, st>>>(x, a.channels, a.codes, a.scales, a.zeros);
+        k_kv_keys<XT, SYM, 256, CW><<<grid, block, 0, st>>>(x, a.channels, a.codes, a.scales, a.zeros);
         break;
     }
     return hipGetLastError();
+}
+
+// 128-channel tiles when the channels allow it (whole 128-byte lines of codes per row), else 64.
+template <typename XT, bool SYM>
+hipError_t keys_go(const KvKeysArgs &a, hipStream_t st)
+{
+    if (a.channels % 128 == 0)
+        return keys_cw<XT, SYM, 128>(a, st);
+    return keys_cw<XT, SYM, 64>(a, st);
 }
 
 // ------------------------------------------------------------------ keys back
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict_
         if (i < rp)
             stats_add<SYM>(am, lo, hi, w[i]);
     SegParams ps[8];
-    tile_params<SYM>(am, lo, hi, tred, ps);
+    tile_params<SYM, kKvCols>(am, lo, hi, tred, ps);
     const int64_t kb = b * (max_tokens / T) + p / T;
     if (r0 == 0)
 #pragma unroll
