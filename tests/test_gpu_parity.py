@@ -493,7 +493,8 @@ def test_w8a8_static_full_layer(gpu_lib):
 # --------------------------------------------------------------------------- W4A8
 
 # Ragged M and N (partial 128-token and 64 / 128-channel tiles), one K step (K = 128), three, eight.
-@pytest.mark.parametrize("mnk", [(5, 77, 128), (130, 200, 384), (257, 129, 1024), (64, 264, 256), (300, 385, 512)])
+@pytest.mark.parametrize("mnk", [(5, 77, 128), (130, 200, 384), (257, 129, 1024), (64, 264, 256), (300, 385, 512),
+                                 (1, 8, 128), (1, 11008, 4096)])
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("sym", [True, False])
 def test_w4a8_small_fp32(gpu_lib, mnk, gs, sym):
@@ -633,6 +634,39 @@ def test_kv_append_online(gpu_lib, T, vg, sym, dtype):
             assert np.array_equal(cache[key].cpu().numpy(), ref[key]), key
     res = bf16_tensor_bits(cache["k_res"]) if dtype == "bf16" else cache["k_res"].cpu().numpy()
     assert np.array_equal(res, ref["k_res"])
+
+
+@pytest.mark.parametrize("C,dtype,sym", [(64, "bf16", True), (8192, "bf16", False), (8192, "f32", True)])
+def test_kv_append_channel_extremes(gpu_lib, C, dtype, sym):
+    """The smallest (64) and largest (8192) channel counts of an append step, over two complete groups."""
+    B, S, T, vg = 2, 64, 32, 0 if sym else 128
+    announce("kv append C=%d %s sym=%s" % (C, dtype, sym))
+    d = W.kv_cache(B * S, C, outlier_channels=2)
+    ks, vs = d["k"].reshape(B, S, C), d["v"].reshape(B, S, C)
+    if dtype == "f32":
+        ks, vs = W.bf16_to_f32(ks), W.bf16_to_f32(vs)
+    nv = C // vg if vg else 1
+    ref = {"k_res": np.zeros((B, T, C), ks.dtype), "k_q": np.zeros((B, S, C), np.int32),
+           "k_s": np.zeros((B, S // T, C), np.float32), "v_q": np.zeros((B, S, C), np.int32),
+           "v_s": np.zeros((B, S, nv), np.float32)}
+    if not sym:
+        ref["k_z"] = np.zeros((B, S // T, C), np.uint8)
+        ref["v_z"] = np.zeros((B, S, nv), np.uint8)
+    cache = gpu_lib.kv_cache_alloc(B, S, C, T, vg, sym, torch.bfloat16 if dtype == "bf16" else torch.float32)
+    conv = to_gpu_bf16 if dtype == "bf16" else to_gpu
+    for step in range(S):
+        pos = np.full(B, step, np.int64)
+        kn, vn = np.ascontiguousarray(ks[:, step]), np.ascontiguousarray(vs[:, step])
+        gpu_lib.kv_append(cache, conv(kn), conv(vn), to_gpu(pos), T, vg, sym)
+        oracle.kv_append(ref, kn, vn, pos, T, vg, sym)
+    torch.cuda.synchronize()
+    for key in ("k_q", "v_q"):
+        assert np.array_equal(cache[key].cpu().numpy().astype(np.int32), ref[key]), key
+    for key in ("k_s", "v_s"):
+        assert np.array_equal(cache[key].cpu().numpy().view(np.uint32), ref[key].view(np.uint32)), key
+    if not sym:
+        for key in ("k_z", "v_z"):
+            assert np.array_equal(cache[key].cpu().numpy(), ref[key]), key
 
 
 def test_kv_keys_full_size_sampled(gpu_lib):
