@@ -212,7 +212,8 @@ int32_t pqg_gemm_s8s8s32(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
  *   w_packed : uint8 [N, K / 2] INT4 codes as pqg_quantize writes them with PQG_GROUP, bits 4 (symmetric:
  *              two's complement; asymmetric: unsigned with zero points), e.g. on diag(s) W (PQG_SMOOTH_MUL);
  *              w_scales fp32 [N, K / group_size]; w_zeros uint8 [N, K / group_size], NULL iff symmetric.
- *   group_size in {32, 64, 128}. Requires K % 128 == 0.
+ *   group_size in {32, 64, 128}. Requires K % 128 == 0 and K <= 2^24 (the kernel addresses a tile's rows with
+ *   32-bit offsets).
  *   y (out)  : [M, N] of y_dtype (PQG_F32 or PQG_BF16).
  */
 int32_t pqg_qlinear_w4a8(const int8_t *x_q, const float *x_scales, int64_t M, int64_t N, int64_t K,

@@ -298,6 +298,8 @@ int32_t pqg_qlinear_w4a8(const int8_t *x_q, const float *x_scales, int64_t M, in
         return fail(PQG_EINVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
     if (K % 128 != 0)
         return fail(PQG_EINVAL, "K (%lld) must be a multiple of 128", (long long)K);
+    if (K > ((int64_t)1 << 24))
+        return fail(PQG_EINVAL, "K (%lld) must be at most 2^24", (long long)K);
     if (M == 0 || N == 0)
         return PQG_OK;
     if (!x_q || !x_scales || !w_packed || !w_scales || !y)

@@ -137,7 +137,8 @@ def test_w4a8_rejects(lib):
         a.update(kw)
         return lib.pqg_qlinear_w4a8(a["xq"], a["sx"], a["M"], a["N"], a["K"], a["w"], a["sw"], a["zw"], a["g"],
                                     a["sym"], a["y"], a["yd"], None)
-    for kw, needle in [(dict(g=96), "group_size"), (dict(K=192), "multiple of 128"), (dict(sym=0), "w_zeros"),
+    for kw, needle in [(dict(g=96), "group_size"), (dict(K=192), "multiple of 128"), (dict(K=(1 << 24) + 128), "2^24"),
+                       (dict(sym=0), "w_zeros"),
                        (dict(zw=FAKE), "must be NULL"), (dict(yd=4), "y_dtype"), (dict(xq=None), "required"),
                        (dict(w=MISALIGNED), "misaligned"), (dict(M=-1), "negative")]:
         assert call(**kw) == pqg.EINVAL, kw
