@@ -91,7 +91,7 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (each GPU would run the same "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (each GPU would run the same "
               "kernels on its own shard of the output rows); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
