@@ -193,8 +193,11 @@ int32_t pqg_qlinear_w8a8(const void *x, const float *smooth, const int8_t *w_q, 
 
 /*
  * The INT8 x INT8 -> INT32 product of the W8A8 layer without the epilogue:
- *   c[m, n] = sum_k a[m, k] * b[n, k]   (exact; |c| < 2^31 whenever K * 127^2 < 2^31, i.e. K <= 133,144).
- *   a : int8 [M, K]; b : int8 [N, K]; c (out) : int32 [M, N]. Requires K % 16 == 0.
+ *   c[m, n] = sum_k a[m, k] * b[n, k]   (exact: |c| <= K * 128^2 < 2^31 for every K the call accepts).
+ *   a : int8 [M, K]; b : int8 [N, K]; c (out) : int32 [M, N].
+ * Requires K % 16 == 0 and 0 < K <= 65536 (the bound of pqg_qlinear_w8a8; it keeps the int32 accumulators
+ * exact and the kernels' 32-bit offsets inside a tile in range). K == 0 with M, N > 0 returns
+ * PQG_EUNSUPPORTED, K above the bound PQG_EUNSUPPORTED; neither enqueues anything.
  * Same kernel and tiling as pqg_qlinear_w8a8; exposed so the accumulators can be checked bit-exactly.
  */
 int32_t pqg_gemm_s8s8s32(const int8_t *a, const int8_t *b, int64_t M, int64_t N, int64_t K, int32_t *c,
@@ -212,8 +215,8 @@ int32_t pqg_gemm_s8s8s32(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
  *   w_packed : uint8 [N, K / 2] INT4 codes as pqg_quantize writes them with PQG_GROUP, bits 4 (symmetric:
  *              two's complement; asymmetric: unsigned with zero points), e.g. on diag(s) W (PQG_SMOOTH_MUL);
  *              w_scales fp32 [N, K / group_size]; w_zeros uint8 [N, K / group_size], NULL iff symmetric.
- *   group_size in {32, 64, 128}. Requires K % 128 == 0 and K <= 2^24 (the kernel addresses a tile's rows with
- *   32-bit offsets).
+ *   group_size in {32, 64, 128}. Requires K % 128 == 0 and 0 < K <= 2^24 (the kernel addresses a tile's rows
+ *   with 32-bit offsets); K == 0 with M, N > 0 returns PQG_EUNSUPPORTED and enqueues nothing.
  *   y (out)  : [M, N] of y_dtype (PQG_F32 or PQG_BF16).
  */
 int32_t pqg_qlinear_w4a8(const int8_t *x_q, const float *x_scales, int64_t M, int64_t N, int64_t K,

@@ -275,8 +275,14 @@ int32_t pqg_gemm_s8s8s32(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
         return fail(PQG_EINVAL, "negative shape");
     if (K % 16 != 0)
         return fail(PQG_EINVAL, "K (%lld) must be a multiple of 16", (long long)K);
+    // The kernels form 32-bit element offsets inside a tile (row * K + k) and accumulate in int32: K <= 65536
+    // keeps both in range (|acc| <= 65536 * 127^2 < 2^31).
+    if (K > 65536)
+        return fail(PQG_EUNSUPPORTED, "K (%lld) above 65536", (long long)K);
     if (M == 0 || N == 0)
         return PQG_OK;
+    if (K == 0)
+        return fail(PQG_EUNSUPPORTED, "K == 0");
     if (!a || !b || !c)
         return fail(PQG_EINVAL, "a, b and c are required");
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 4))
@@ -302,6 +308,8 @@ int32_t pqg_qlinear_w4a8(const int8_t *x_q, const float *x_scales, int64_t M, in
         return fail(PQG_EINVAL, "K (%lld) must be at most 2^24", (long long)K);
     if (M == 0 || N == 0)
         return PQG_OK;
+    if (K == 0)
+        return fail(PQG_EUNSUPPORTED, "K == 0");
     if (!x_q || !x_scales || !w_packed || !w_scales || !y)
         return fail(PQG_EINVAL, "x_q, x_scales, w_packed, w_scales and y are required");
     if (symmetric && w_zeros)

@@ -131,6 +131,25 @@ def test_w8a8_and_gemm_reject(lib):
     assert rc == pqg.EINVAL and "misaligned" in lib.pqg_last_error().decode()
 
 
+@pytest.mark.parametrize("K,needle", [(0, "K == 0"), (65536 + 16, "above 65536"), (1 << 24, "above 65536"),
+                                      (11 << 20, "above 65536")])
+def test_gemm_rejects_k_outside_the_exact_range(lib, K, needle):
+    """K == 0 would give the kernels zero K steps (their first load address wraps below the operands) and K
+    beyond 65536 overflows the 32-bit offsets within a tile or the int32 accumulators: both are rejected on
+    the host before any launch, with every pointer a fake that must never be touched."""
+    rc = lib.pqg_gemm_s8s8s32(FAKE, FAKE, 2048, 11008, K, FAKE, None)
+    assert rc == pqg.EUNSUPPORTED and needle in lib.pqg_last_error().decode()
+    rc = lib.pqg_qlinear_w8a8(FAKE, None, FAKE, FAKE, 2048, 11008, K, FAKE, 1, FAKE, FAKE, None)
+    assert rc in (pqg.EUNSUPPORTED, pqg.EINVAL) and lib.pqg_last_error().decode()
+    if K == 0:
+        assert lib.pqg_gemm_s8s8s32(None, None, 0, 11008, 0, None, None) == pqg.OK  # empty: nothing to do
+
+
+def test_w4a8_rejects_k_zero(lib):
+    rc = lib.pqg_qlinear_w4a8(FAKE, FAKE, 4, 64, 0, FAKE, FAKE, None, 128, 1, FAKE, 1, None)
+    assert rc == pqg.EUNSUPPORTED and "K == 0" in lib.pqg_last_error().decode()
+
+
 def test_w4a8_rejects(lib):
     def call(**kw):
         a = dict(xq=FAKE, sx=FAKE, M=4, N=64, K=256, w=FAKE, sw=FAKE, zw=None, g=128, sym=1, y=FAKE, yd=1)
