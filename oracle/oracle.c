@@ -106,29 +106,32 @@ static seg_params segment_params(float absmax, float lo, float hi, int bits, int
             p.s = 1.0f;
             p.z = 0;
         } else {
+            /* clamped as a float, then converted (the quotient is in range here, but the order is that of
+             * the definition: clamp the rounded value) */
             float zf = nearbyintf(-lo / p.s);
-            int z = (int)zf;
-            if (z < p.qmin)
-                z = p.qmin;
-            if (z > p.qmax)
-                z = p.qmax;
-            p.z = z;
+            if (zf < (float)p.qmin)
+                zf = (float)p.qmin;
+            if (zf > (float)p.qmax)
+                zf = (float)p.qmax;
+            p.z = (int)zf;
         }
     }
     return p;
 }
 
 /* q = clamp(round(x / s) + z, qmin, qmax)  [P1 core formula; P2 §3; P3 §11.1.1].
- * The rounding applies to x/s and z is added afterwards, as the formula is written. */
+ * The rounding applies to x/s and z is added afterwards, as the formula is written. The sum and the clamp
+ * are taken in binary32 before the conversion to int: the rounded quotient can lie far outside the int
+ * range (a binary16 scale saturated at 65504 under values of 1e14 and more), and the clamp belongs to the
+ * mathematical integer. Below 2^24 the sum is exact; above it, it stays beyond the code range either way. */
 static int quantize_one(float v, seg_params p)
 {
-    float t = nearbyintf(v / p.s);
-    int q = (int)t + p.z;
-    if (q < p.qmin)
-        q = p.qmin;
-    if (q > p.qmax)
-        q = p.qmax;
-    return q;
+    float t = nearbyintf(v / p.s) + (float)p.z;
+    if (t < (float)p.qmin)
+        t = (float)p.qmin;
+    if (t > (float)p.qmax)
+        t = (float)p.qmax;
+    return (int)t;
 }
 
 /* The value that enters quantization: the input, optionally divided (activations, X diag(s)^-1) or
@@ -360,9 +363,11 @@ int or_quantize_meta16(const void *x, int x_dtype, int64_t rows, int64_t cols, i
         s16[e] = h;
         p.s = or_f16_to_f32(h);
         if (!symmetric) {
+            /* -l / s16 can lie far beyond the int range when s16 saturated at 65504: clamp the rounded
+             * value as a float, then convert */
             float l = lo > 0.0f ? 0.0f : lo;
-            int z = (int)nearbyintf(-l / p.s);
-            p.z = z < 0 ? 0 : z > 15 ? 15 : z;
+            float zf = nearbyintf(-l / p.s);
+            p.z = zf < 0.0f ? 0 : zf > 15.0f ? 15 : (int)zf;
             zeros[e] = (uint8_t)p.z;
         }
         for (int64_t i = i0; i < i0 + group_size; ++i)

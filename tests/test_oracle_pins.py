@@ -765,3 +765,20 @@ def test_pack_zeros4_round_trip():
         assert p.size == (n + 1) // 2
         lo, hi = p & 0xF, p >> 4
         assert np.array_equal(np.stack([lo, hi], 1).ravel()[:n], z)
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_meta16_saturated_scale_clamps_the_code(sym):
+    """A group holding values of 1e14 and more: its fp32 scale exceeds binary16, the stored scale saturates at
+    65504, and x / s16 lies far beyond the int range. The clamp of the core formula applies to the rounded
+    quotient plus z ("量化、蒸馏与模型压缩", core formula), so the largest positive value codes to the top
+    of the range and the most negative one to the bottom -- never to a wrapped integer."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, :5] = [1e38, -7e37, 3e37, -1e36, 2e14]
+    q, s16, z = oracle.quantize_meta16(x, sym, 32)
+    assert s16[0] == 0x7BFF  # 65504
+    top, bottom = (7, -7) if sym else (15, 0)
+    assert q[0, 0] == top and q[0, 2] == top and q[0, 4] == top
+    assert q[0, 1] == bottom and q[0, 3] == bottom
+    if not sym:
+        assert z[0] == 15  # -lo / 65504 is far above 15: the zero point clamps too
