@@ -13,7 +13,8 @@
  *
  * Conventions shared by every entry point:
  *   - All pointers except `stream` are DEVICE pointers into memory the caller allocated and owns; the
- *     library allocates nothing and keeps no state besides a thread-local error string.
+ *     library allocates nothing and keeps no state besides a thread-local error string (the one exception,
+ *     pqg_qlinear_w8a8_noalloc, uses a fixed device array of the library's own, described there).
  *   - Tensors are row-major and contiguous. bf16 is the 16-bit brain float (upper half of a binary32).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is enqueued on it and never
  *     synchronised: execution errors surface at the caller's next synchronisation.
@@ -317,6 +318,25 @@ int32_t pqg_dequantize_meta16(const uint8_t *codes, const uint16_t *scales16, co
 int32_t pqg_qlinear_w4a16_meta16(const void *x, int64_t M, int64_t N, int64_t K, const uint8_t *w_packed,
                                  const uint16_t *scales16, const uint8_t *zeros4, int32_t group_size,
                                  int32_t symmetric, void *y, int32_t y_dtype, void *stream);
+
+/*
+ * W8A8 linear layer without any allocation: the same computation, kernels and results as pqg_qlinear_w8a8 with
+ * x given, for callers that cannot allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Here the caller passes only the inputs and the output; the
+ * per-token activation codes and scales that pqg_qlinear_w8a8 keeps in the caller's x_q / x_scales live in
+ * a fixed device array inside the library (16 MiB of codes + 64 KiB of scales, one copy per GPU, held until
+ * the process ends). The call itself allocates nothing.
+ *   x (bf16 [M, K], required), smooth, w_q, w_scales, y, y_dtype: as pqg_qlinear_w8a8.
+ *   Limits: M <= 16384 and M * K <= 2^24 (the array's size), besides those of pqg_qlinear_w8a8; larger shapes
+ *   return PQG_EUNSUPPORTED before anything is enqueued.
+ *   The device of `stream` must be the current device (else PQG_EINVAL). The first call on a device looks up
+ *   the array's address there (a failure returns PQG_EHIP).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's codes and scales: two calls that
+ * overlap on one GPU (different streams, or different threads without ordering) race and give undefined
+ * results. Calls ordered on one stream are safe; nothing in the array needs to start at zero.
+ */
+int32_t pqg_qlinear_w8a8_noalloc(const void *x, const float *smooth, const int8_t *w_q, const float *w_scales,
+                                 int64_t M, int64_t N, int64_t K, void *y, int32_t y_dtype, void *stream);
 
 #ifdef __cplusplus
 }

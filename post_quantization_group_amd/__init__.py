@@ -31,7 +31,7 @@ EXPORTS = [
     "pqg_dequantize",
     "pqg_smooth_workspace_bytes", "pqg_smooth", "pqg_qlinear_w4a16", "pqg_qlinear_w8a8", "pqg_gemm_s8s8s32",
     "pqg_qlinear_w4a8", "pqg_kv_quantize_keys", "pqg_kv_dequantize_keys", "pqg_kv_append",
-    "pqg_quantize_meta16", "pqg_dequantize_meta16", "pqg_qlinear_w4a16_meta16",
+    "pqg_quantize_meta16", "pqg_dequantize_meta16", "pqg_qlinear_w4a16_meta16", "pqg_qlinear_w8a8_noalloc",
 ]
 
 _lib = None
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH):
     lib.pqg_qlinear_w4a16_meta16.restype = I32
     lib.pqg_qlinear_w4a16_meta16.argtypes = [P, I64, I64, I64, P, P, P, I32, I32, P, I32, P]
     lib.pqg_kv_append.argtypes = [P, P, I32, I64, I64, P, I64, I32, I32, I32, P, P, P, P, P, P, P, P]
+    lib.pqg_qlinear_w8a8_noalloc.restype = I32
+    lib.pqg_qlinear_w8a8_noalloc.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
     if lib.pqg_abi_version() != ABI_VERSION:
         raise ImportError("libpqg.so ABI %d != binding ABI %d" % (lib.pqg_abi_version(), ABI_VERSION))
     _lib = lib
@@ -253,6 +255,23 @@ def qlinear_w8a8(x, smooth_s, w_q: torch.Tensor, w_scales: torch.Tensor, out_dty
     _check(lib.pqg_qlinear_w8a8(_ptr(x), _ptr(smooth_s), _ptr(w_q), _ptr(w_scales), M, N, K, _ptr(y),
                                 _float_dtype(y), _ptr(x_q), _ptr(x_scales), _stream(dev)))
     return y, x_q, x_scales
+
+
+def qlinear_w8a8_noalloc(x: torch.Tensor, smooth_s, w_q: torch.Tensor, w_scales: torch.Tensor,
+                         out_dtype=torch.bfloat16, out=None):
+    """pqg_qlinear_w8a8_noalloc: as qlinear_w8a8 with x given, the activation codes and scales kept in the
+    library's own device array (nothing is allocated by the call; `out` may pass a preallocated y). Returns y."""
+    lib = load()
+    dev = _dev(w_q)
+    _dev(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    N, K = w_q.shape
+    M = x.shape[0]
+    y = torch.empty((M, N), dtype=out_dtype, device=dev) if out is None else out
+    _check(lib.pqg_qlinear_w8a8_noalloc(_ptr(x), _ptr(smooth_s), _ptr(w_q), _ptr(w_scales), M, N, K, _ptr(y),
+                                        _float_dtype(y), _stream(dev)))
+    return y
 
 
 def gemm_s8s8s32(a: torch.Tensor, b: torch.Tensor, out=None):

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/pqg.h"
 #include "kernels.hpp"
@@ -53,6 +54,46 @@ int32_t check_qspec(int32_t bits, int32_t symmetric, int32_t granularity, int32_
                         group_size);
     }
     return PQG_OK;
+}
+
+// Checks shared by the two W8A8 entry points (everything but the activation scratch x_q / x_scales).
+int32_t check_w8a8(const void *x, const float *smooth, const int8_t *w_q, const float *w_scales, int64_t M, int64_t N,
+                   int64_t K, const void *y, int32_t y_dtype)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (!valid_float_dtype(y_dtype))
+        return fail(PQG_EINVAL, "unknown y_dtype %d", y_dtype);
+    if (K % 32 != 0)
+        return fail(PQG_EINVAL, "K (%lld) must be a multiple of 32", (long long)K);
+    if (K > 65536)
+        return fail(PQG_EUNSUPPORTED, "K (%lld) above 65536", (long long)K);
+    if (M == 0 || N == 0)
+        return PQG_OK;
+    if (K == 0)
+        return fail(PQG_EUNSUPPORTED, "K == 0");
+    if (!w_q || !w_scales || !y)
+        return fail(PQG_EINVAL, "w_q, w_scales and y are required");
+    if (!x && smooth)
+        return fail(PQG_EINVAL, "smooth must be NULL when x is NULL (x_q / x_scales are then inputs)");
+    if ((x && !aligned(x, 16)) || !aligned(w_q, 16) || !aligned(w_scales, 4) || !aligned(y, 4) ||
+        (smooth && !aligned(smooth, 16)))
+        return fail(PQG_EINVAL, "misaligned pointer (x, w_q, smooth: 16 bytes; scales, y: 4 bytes)");
+    return PQG_OK;
+}
+
+// The activation quantize (when x is given) and the GEMM + epilogue, after the checks.
+int32_t run_w8a8(const void *x, const float *smooth, const int8_t *w_q, const float *w_scales, int64_t M, int64_t N,
+                 int64_t K, void *y, int32_t y_dtype, int8_t *x_q, float *x_scales, hipStream_t st)
+{
+    if (x) {
+        pqg::QuantArgs q{x, true, M, K, smooth, smooth ? pqg::SMOOTH_DIV : pqg::SMOOTH_NONE, 8, true, pqg::QG_ROW, 0,
+                         x_q, x_scales, nullptr, nullptr};
+        if (int32_t e = hip_status(pqg::launch_quantize(q, st), "W8A8 activation quantize launch"))
+            return e;
+    }
+    pqg::GemmI8Args g{x_q, w_q, M, N, K, x_scales, w_scales, y, y_dtype == PQG_BF16};
+    return hip_status(pqg::launch_gemm_i8(g, st), "W8A8 gemm launch");
 }
 
 }  // namespace
@@ -237,34 +278,15 @@ int32_t pqg_qlinear_w8a8(const void *x, const float *smooth, const int8_t *w_q, 
                          int64_t N, int64_t K, void *y, int32_t y_dtype, int8_t *x_q, float *x_scales, void *stream)
 {
     g_err[0] = 0;
-    if (M < 0 || N < 0 || K < 0)
-        return fail(PQG_EINVAL, "negative shape");
-    if (!valid_float_dtype(y_dtype))
-        return fail(PQG_EINVAL, "unknown y_dtype %d", y_dtype);
-    if (K % 32 != 0)
-        return fail(PQG_EINVAL, "K (%lld) must be a multiple of 32", (long long)K);
-    if (K > 65536)
-        return fail(PQG_EUNSUPPORTED, "K (%lld) above 65536", (long long)K);
+    if (int32_t e = check_w8a8(x, smooth, w_q, w_scales, M, N, K, y, y_dtype))
+        return e;
     if (M == 0 || N == 0)
         return PQG_OK;
-    if (K == 0)
-        return fail(PQG_EUNSUPPORTED, "K == 0");
-    if (!w_q || !w_scales || !y || !x_q || !x_scales)
-        return fail(PQG_EINVAL, "w_q, w_scales, y, x_q and x_scales are required");
-    if (!x && smooth)
-        return fail(PQG_EINVAL, "smooth must be NULL when x is NULL (x_q / x_scales are then inputs)");
-    if ((x && !aligned(x, 16)) || !aligned(w_q, 16) || !aligned(x_q, 16) || !aligned(w_scales, 4) ||
-        !aligned(x_scales, 4) || !aligned(y, 4) || (smooth && !aligned(smooth, 16)))
-        return fail(PQG_EINVAL, "misaligned pointer (x, w_q, x_q, smooth: 16 bytes; scales, y: 4 bytes)");
-    hipStream_t st = as_stream(stream);
-    if (x) {
-        pqg::QuantArgs q{x, true, M, K, smooth, smooth ? pqg::SMOOTH_DIV : pqg::SMOOTH_NONE, 8, true, pqg::QG_ROW, 0,
-                         x_q, x_scales, nullptr, nullptr};
-        if (int32_t e = hip_status(pqg::launch_quantize(q, st), "pqg_qlinear_w8a8 activation quantize launch"))
-            return e;
-    }
-    pqg::GemmI8Args g{x_q, w_q, M, N, K, x_scales, w_scales, y, y_dtype == PQG_BF16};
-    return hip_status(pqg::launch_gemm_i8(g, st), "pqg_qlinear_w8a8 gemm launch");
+    if (!x_q || !x_scales)
+        return fail(PQG_EINVAL, "x_q and x_scales are required");
+    if (!aligned(x_q, 16) || !aligned(x_scales, 4))
+        return fail(PQG_EINVAL, "misaligned pointer (x_q: 16 bytes; x_scales: 4 bytes)");
+    return run_w8a8(x, smooth, w_q, w_scales, M, N, K, y, y_dtype, x_q, x_scales, as_stream(stream));
 }
 
 int32_t pqg_gemm_s8s8s32(const int8_t *a, const int8_t *b, int64_t M, int64_t N, int64_t K, int32_t *c,
@@ -506,6 +528,87 @@ int32_t pqg_qlinear_w4a16_meta16(const void *x, int64_t M, int64_t N, int64_t K,
     pqg::W4A16Args a{static_cast<const uint16_t *>(x), M, N, K, w_packed, nullptr, zeros4, group_size, symmetric != 0,
                      y, y_dtype == PQG_BF16, true, scales16};
     return hip_status(pqg::launch_w4a16(a, as_stream(stream)), "pqg_qlinear_w4a16_meta16 launch");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free W8A8 (scratch)
+//
+// pqg_qlinear_w8a8_noalloc keeps the activation codes and per-token scales between its two kernels in the
+// file-scope device array `scratch`: codes at offset 0 (at most kScratchCodeBytes = M * K bytes), scales at
+// kScratchCodeBytes (at most kScratchTokens floats). Every GPU the library runs on holds its own copy for the
+// life of the process. In host code `scratch` only names the symbol: its device address on the current device
+// comes from hipGetSymbolAddress, looked up once per device on the first call there and kept in
+// g_scratch_addr, and only that address is ever passed to kernels.
+namespace {
+
+constexpr int64_t kScratchCodeBytes = int64_t(1) << 24;  // 16 MiB of INT8 activation codes
+constexpr int64_t kScratchTokens = 16384;                // per-token scales
+constexpr int kScratchMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) int8_t scratch[kScratchCodeBytes + kScratchTokens * sizeof(float)];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kScratchMaxDevices];  // device address of `scratch` per device, null until looked up
+
+// The scratch address on the current device, which must be the device of `stream` (a non-null stream).
+int32_t scratch_address(void *stream, int8_t **out)
+{
+    int dev = -1;
+    if (int32_t e = hip_status(hipGetDevice(&dev), "hipGetDevice"))
+        return e;
+    if (dev < 0 || dev >= kScratchMaxDevices)
+        return fail(PQG_EUNSUPPORTED, "device %d: at most %d devices", dev, kScratchMaxDevices);
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (int32_t e = hip_status(hipStreamGetDevice(as_stream(stream), &sdev), "hipStreamGetDevice"))
+            return e;
+        if (sdev != dev)
+            return fail(PQG_EINVAL, "the stream belongs to device %d but device %d is current", (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        if (int32_t e = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))
+            return e;
+        if (!p)
+            return fail(PQG_EHIP, "hipGetSymbolAddress(scratch) returned a null address");
+        g_scratch_addr[dev] = p;
+    }
+    *out = static_cast<int8_t *>(g_scratch_addr[dev]);
+    return PQG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pqg_qlinear_w8a8_noalloc(const void *x, const float *smooth, const int8_t *w_q, const float *w_scales,
+                                 int64_t M, int64_t N, int64_t K, void *y, int32_t y_dtype, void *stream)
+{
+    g_err[0] = 0;
+    if (int32_t e = check_w8a8(x, smooth, w_q, w_scales, M, N, K, y, y_dtype))
+        return e;
+    if (M > kScratchTokens)
+        return fail(PQG_EUNSUPPORTED, "M (%lld) above the %lld tokens the scratch holds", (long long)M,
+                    (long long)kScratchTokens);
+    if (M * K > kScratchCodeBytes)
+        return fail(PQG_EUNSUPPORTED, "M * K (%lld) above the %lld activation codes the scratch holds",
+                    (long long)(M * K), (long long)kScratchCodeBytes);
+    if (M == 0 || N == 0)
+        return PQG_OK;
+    if (!x)
+        return fail(PQG_EINVAL, "x is required (the activation codes live in the library's scratch)");
+    int8_t *base = nullptr;
+    if (int32_t e = scratch_address(stream, &base))
+        return e;
+    int8_t *x_q = base;
+    float *x_scales = reinterpret_cast<float *>(base + kScratchCodeBytes);
+    return run_w8a8(x, smooth, w_q, w_scales, M, N, K, y, y_dtype, x_q, x_scales, as_stream(stream));
 }
 
 }  // extern "C"

@@ -234,3 +234,23 @@ def test_meta16_rejects(lib):
         assert lin(**kw) == pqg.EINVAL, kw
         assert needle in lib.pqg_last_error().decode(), kw
     assert lin(M=0, x=None, w=None, s=None, y=None) == pqg.OK
+
+
+def test_w8a8_noalloc_rejects_before_touching_the_device(lib):
+    """Shapes beyond the library's activation array and bad arguments are rejected on the host before the
+    device is queried (no GPU here): M above 16384 tokens, M * K above 2^24 codes, x missing."""
+    def call(**kw):
+        a = dict(x=FAKE, sm=None, wq=FAKE, sw=FAKE, M=2048, N=11008, K=4096, y=FAKE, yd=1)
+        a.update(kw)
+        return lib.pqg_qlinear_w8a8_noalloc(a["x"], a["sm"], a["wq"], a["sw"], a["M"], a["N"], a["K"], a["y"],
+                                            a["yd"], None)
+    for kw, rc, needle in [(dict(M=16385, K=32), pqg.EUNSUPPORTED, "16384 tokens"),
+                           (dict(M=4097, K=4096), pqg.EUNSUPPORTED, "activation codes"),
+                           (dict(M=256, K=65536 + 32), pqg.EUNSUPPORTED, "above 65536"),
+                           (dict(x=None), pqg.EINVAL, "x is required"), (dict(K=100), pqg.EINVAL, "multiple of 32"),
+                           (dict(yd=9), pqg.EINVAL, "y_dtype"), (dict(wq=None), pqg.EINVAL, "required"),
+                           (dict(x=MISALIGNED), pqg.EINVAL, "misaligned"), (dict(M=-1), pqg.EINVAL, "negative"),
+                           (dict(K=0, M=4), pqg.EUNSUPPORTED, "K == 0")]:
+        assert call(**kw) == rc, kw
+        assert needle in lib.pqg_last_error().decode(), (kw, lib.pqg_last_error())
+    assert call(M=0, x=None) == pqg.OK
