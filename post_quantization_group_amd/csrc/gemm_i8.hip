@@ -9,9 +9,9 @@
 // 16x16x64 form on gfx950, so it is the building block. The weight tile is the MFMA "A" operand and the
 // activation tile "B": lane l holds output column m = l % 32 and, in accumulator register r, output row
 // n = 8 (r / 4) + 4 (l / 32) + r % 4, i.e. four consecutive output channels per group of four registers.
-// The bf16 epilogue (when output rows are 16-byte aligned) stages the scaled tile in LDS and writes it back
-// as 16-byte stores along output rows; otherwise each group of four registers is one 16-byte (int32 /
-// fp32) or 8-byte (bf16) store.
+// In the 128 x 128 and ring kernels the bf16 epilogue (when output rows are 16-byte aligned) stages the scaled
+// tile in LDS and writes it back as 16-byte stores along output rows; otherwise, and always in the wide
+// kernel, each group of four registers is one 16-byte (int32 / fp32) or 8-byte (bf16) store.
 // Three kernels share this layout. With K % 64 == 0, the wide kernel at the end (256 x 384 tiles, one block
 // of eight waves per CU) takes shapes whose tiles fill three quarters to all of the CUs in one round, and the
 // ring kernel (256 x 128 tiles) other shapes with M >= 256; both load their operands straight into a
@@ -51,10 +51,11 @@ __device__ __forceinline__ int lds_off(int r, int c)
     return r * BK + 16 * (c ^ (((r >> 1) & 3) | ((r >> 2) & 4)));
 }
 
-// Epilogue for four consecutive output channels nb .. nb + 3 at token m.
+// Epilogue for four consecutive output channels nb .. nb + 3 at token m, with their weight scales sw[0..3]
+// (unused for MODE 0).
 template <int MODE>
-__device__ __forceinline__ void store4(const int v[4], int64_t m, int64_t nb, int64_t M, int64_t N, float sxm,
-                                       const float *__restrict__ sb, void *__restrict__ c, bool vec_ok)
+__device__ __forceinline__ void store4s(const int v[4], int64_t m, int64_t nb, int64_t M, int64_t N, float sxm,
+                                        const float sw[4], void *__restrict__ c, bool vec_ok)
 {
     if (m >= M)
         return;
@@ -71,10 +72,8 @@ __device__ __forceinline__ void store4(const int v[4], int64_t m, int64_t nb, in
     }
     float f[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float swn = (nb + r < N) ? sb[nb + r] : 0.0f;
-        f[r] = (float)v[r] * (sxm * swn);
-    }
+    for (int r = 0; r < 4; ++r)
+        f[r] = (float)v[r] * (sxm * sw[r]);
     if (MODE == 1) {
         uint16_t *out = static_cast<uint16_t *>(c) + m * N + nb;
         if (vec_ok && nb + 3 < N) {
@@ -94,6 +93,19 @@ __device__ __forceinline__ void store4(const int v[4], int64_t m, int64_t nb, in
                     out[r] = f[r];
         }
     }
+}
+
+// The same with the weight scales read from sb (zero past N).
+template <int MODE>
+__device__ __forceinline__ void store4(const int v[4], int64_t m, int64_t nb, int64_t M, int64_t N, float sxm,
+                                       const float *__restrict__ sb, void *__restrict__ c, bool vec_ok)
+{
+    float sw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (MODE != 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sw[r] = (nb + r < N) ? sb[nb + r] : 0.0f;
+    store4s<MODE>(v, m, nb, M, N, sxm, sw, c, vec_ok);
 }
 
 template <int BN, int BM, int WN, int WM, int BK, int MODE>  // MODE 0: raw int32, 1: bf16, 2: fp32 epilogue
@@ -488,11 +500,16 @@ hipError_t ring_launch(const GemmI8Args &g, hipStream_t st)
 //   * 64-byte K steps in a three-stage direct-to-LDS ring (3 x 40 KB), loads two steps ahead, as in the
 //     ring kernel. Stages are separate LDS blocks so that the compiler can tell a direct load into one
 //     stage from the fragment reads of another.
-//   * bf16 output is staged through the stages in two halves of 128 tokens (96 KB each) and written as
-//     16-byte stores along output rows; int32 and fp32 output, and bf16 with N % 8 != 0, use store4.
+//   * The tile's 384 weight and 256 token scales are loaded straight into LDS (640 floats) before the ring
+//     starts, so the epilogue reads each group of four weight scales with one LDS read. Taking them from
+//     global memory per output group cost 16 us of the 114 us the layer took; the epilogue then stores each
+//     group of four outputs from the accumulators (8-byte bf16 / 16-byte fp32 or int32 stores), which was
+//     3 us faster than staging bf16 rows through the ring stages.
+//   * Operand loads carry the sc0 cache-policy bit (3 % faster on the layer; sc1 or both were slower).
 // Taken when its tiles fill between three quarters and all of the CUs in a single round; otherwise the
 // ring kernel (more, smaller tiles) balances better.
 constexpr int kWideBM = 256, kWideBN = 384, kWideWM = 128, kWideWN = 96, kWideBK = 64;
+constexpr int kLoadSc0 = 1;  // cache-policy bits of the wide kernel's direct operand loads: sc0
 constexpr int kWideWaves = (kWideBM / kWideWM) * (kWideBN / kWideWN);
 constexpr int kWideThreads = kWideWaves * kWave;
 constexpr int kWideStage = (kWideBM + kWideBN) * kWideBK;         // 40960 bytes
@@ -549,7 +566,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_gemm_i8_wide(const int8_t *
 #pragma unroll
         for (int i = 0; i < kWideLoads; ++i)
             __builtin_amdgcn_global_load_lds((global_void_t *)((i < kWideALoads ? abase : bbase) + (off[i] + kk)),
-                                             (lds_void_t *)(stage + (i * kWideWaves + w) * kWave * 16), 16, 0, 0);
+                                             (lds_void_t *)(stage + (i * kWideWaves + w) * kWave * 16), 16, 0,
+                                             kLoadSc0);
     };
 
     v16i acc[TN][TM];
@@ -585,6 +603,18 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_gemm_i8_wide(const int8_t *
         __builtin_amdgcn_s_barrier();
     };
 
+    // The tile's scales, straight into LDS before the ring starts: BN weight scales, then BM token scales (rows
+    // past N or M repeat the last one; their outputs are never stored). They land long before the epilogue.
+    float *const lsc = reinterpret_cast<float *>(lds_block<(BN + BM) * 4, 3>());
+    if (MODE != 0) {
+        for (int base = w * kWave; base < BN + BM; base += kWideThreads) {
+            const int idx = base + lane;
+            const float *src = idx < BN ? sb + std::min<int64_t>(n0 + idx, N - 1)
+                                        : sa + std::min<int64_t>(m0 + (idx - BN), M - 1);
+            if (idx < BN + BM)
+                __builtin_amdgcn_global_load_lds((global_void_t *)src, (lds_void_t *)(lsc + base), 4, 0, 0);
+        }
+    }
     issue(s0, 0);
     issue(s1, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWideLoads, 15));
@@ -601,65 +631,27 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_gemm_i8_wide(const int8_t *
         step(s1, s0, k + 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no direct load may land in the stages reused below
 
-    if (MODE == 1 && (N % 8) == 0 && (reinterpret_cast<uintptr_t>(c) % 16) == 0) {
-        // two halves of 128 tokens, each staged as [token][channel] bf16 rows of 768 bytes over the stages
-        constexpr int ROWB = BN * 2, RPS = kWideStage / ROWB, CPR = ROWB / 16;
-        static_assert(3 * RPS >= BM / 2, "half an output tile fits in the stages");
-        auto rowp = [&](int ml) __attribute__((always_inline)) -> int8_t * {
-            return ml < RPS ? s0 + ml * ROWB : ml < 2 * RPS ? s1 + (ml - RPS) * ROWB : s2 + (ml - 2 * RPS) * ROWB;
-        };
-        uint16_t *y = static_cast<uint16_t *>(c);
-        __syncthreads();
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (wm == h) {
-#pragma unroll
-                for (int j = 0; j < TM; ++j) {
-                    const int ml = j * 32 + fr;
-                    const int64_t m = m0 + h * WM + ml;
-                    const float sxm = m < M ? sa[m] : 0.0f;
-                    int8_t *rp = rowp(ml);
-#pragma unroll
-                    for (int i = 0; i < TN; ++i)
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const int nl = wn * WN + i * 32 + 8 * g + 4 * fh;
-                            const int64_t nb = n0 + nl;
-                            float f[4];
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const float swn = (nb + r < N) ? sb[nb + r] : 0.0f;
-                                f[r] = (float)acc[i][j][4 * g + r] * (sxm * swn);
-                            }
-                            const int chunk = (nl * 2 / 16) ^ (ml & 15);  // 48 chunks per row: stays in range
-                            *reinterpret_cast<uint2 *>(rp + chunk * 16 + (nl * 2) % 16) =
-                                make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
-                        }
-                }
-            }
-            __syncthreads();
-            for (int q = tid; q < WM * CPR; q += kWideThreads) {
-                const int ml = q / CPR, cl = q % CPR;
-                const int64_t m = m0 + h * WM + ml, nb = n0 + cl * 8;
-                if (m < M && nb < N)  // N % 8 == 0: a chunk never crosses N
-                    *reinterpret_cast<uint4 *>(y + m * N + nb) =
-                        *reinterpret_cast<const uint4 *>(rowp(ml) + ((cl ^ (ml & 15)) * 16));
-            }
-            __syncthreads();
-        }
-        return;
-    }
+    __syncthreads();  // every wave's scale loads have landed (each waited for its own above)
     const bool vec_ok = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(c) % (MODE == 1 ? 8 : 16)) == 0;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-        const int64_t m = m0 + wm * WM + j * 32 + fr;
-        const float sxm = (MODE == 0 || m >= M) ? 0.0f : sa[m];
+        const int ml = wm * WM + j * 32 + fr;
+        const float sxm = MODE == 0 ? 0.0f : lsc[BN + ml];
 #pragma unroll
         for (int i = 0; i < TN; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
+                const int nl = wn * WN + i * 32 + 8 * g + 4 * fh;
+                float sw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (MODE != 0) {
+                    const float4 s4 = *reinterpret_cast<const float4 *>(lsc + nl);
+                    sw[0] = s4.x;
+                    sw[1] = s4.y;
+                    sw[2] = s4.z;
+                    sw[3] = s4.w;
+                }
                 const int v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                store4<MODE>(v, m, n0 + wn * WN + i * 32 + 8 * g + 4 * fh, M, N, sxm, sb, c, vec_ok);
+                store4s<MODE>(v, m0 + ml, n0 + nl, M, N, sxm, sw, c, vec_ok);
             }
     }
 }
