@@ -6,10 +6,12 @@ One step is one pass over every stage of the quantized linear layer on synthetic
   quantize   Llama-70B-shaped decoder layer (q, k, v, o, gate, up, down; 855.6 M bf16 weights) to symmetric
              INT4, g = 128, packed                                                  (range, scale, codes, pack)
   dequantize the packed layer back to bf16                                          (standalone dequantize)
-  w4a16_m1   the seven projections at batch 1 (decode)       <- the headline weight-stream GB/s
-             (one step in four instead: the same weights as four launches, q|k|v and gate|up stored as
-             concatenated matrices sharing their input, as serving engines store them; and one step in four
-             a third copy of the layer with 16-bit metadata: binary16 scales; both reported apart)
+  w4a16_m1   the seven projections at batch 1 (decode) in one grouped launch (pqg_qlinear_w4a16_grouped)
+                                                             <- the headline weight-stream GB/s
+             (by step, four other forms of the same pass are measured and reported apart: the seven
+             launches back to back; the seven launches with events between them, for per-projection times;
+             four launches over q|k|v and gate|up stored as concatenated matrices sharing their input, as
+             serving engines store them; and a third copy of the layer with 16-bit metadata)
   w4a16_m32  the seven projections at batch 32
   w4a16_m8   the seven projections at batch 8
   smooth     SmoothQuant factor, alpha = 0.5, X 2048x4096 (41 channels x50), W 11008x4096
@@ -29,11 +31,15 @@ the 1.7 GB dequantize left in the 256 MB last-level cache), and last the batch-1
 quantized at the start of the step: cold weights streamed from HBM behind a clean cache, as in a decode
 loop where each layer's weight stream follows the previous one.
 
+After the timed steps, the Llama-7B attention and FFN configurations are measured on their own (quantize and
+W4A16 throughput over device copies rotated past the last-level cache, metadata bytes against weight bytes),
+and the oracle is timed on the host: the decode sample (cpu_baseline) and each function on all threads and on
+one.
+
 Output: one JSON line. `value` = the decode weight stream (packed INT4 bytes + fp32 scales of all seven
-projections) divided by the time of the seven back-to-back W4A16 launches, taken with HIP events recorded on
-the stream the kernels run on, in GB/s. The roofline entry uses the same measurement: its average launch
-duration is that sequence time over seven, which agrees with the kernel trace (events placed between single
-launches add the dispatch gap, about 2 us each, and are reported only as a per-projection breakdown).
+projections) divided by the duration of the grouped launch that streams it, taken with HIP events recorded on
+the stream the kernel runs on, in GB/s. The roofline entry uses the same measurement (one launch, all the
+bytes), which agrees with the kernel trace.
 """
 from __future__ import annotations
 
@@ -63,6 +69,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-function-seconds", type=float, default=1.5,
+                    help="target CPU time per oracle function and thread count")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -256,13 +264,16 @@ def main():
         if rec:
             marks["w4a16_m8"] = ev()
             marks["w4a16_m8"].record(stream)
-        # The decode pass takes one of four forms by step: the seven launches back to back (mode 0: the
-        # sequence time, value), the same with events between the launches (mode 1: per-kernel durations;
-        # the events break back-to-back dispatch), the four launches of the concatenated layout (mode 2), or
-        # the seven launches over the copy with 16-bit metadata (mode 3).
-        mode = i % 4
+        # The decode pass takes one of five forms by step: the seven projections in one grouped launch (mode
+        # 0: value), the seven launches with events between them (mode 1: per-kernel durations; the events
+        # break back-to-back dispatch), the four launches of the concatenated layout (mode 2), the seven
+        # launches over the copy with 16-bit metadata (mode 3), or the seven launches back to back (mode 4).
+        mode = i % 5
         gemv_ev = []
-        if mode == 3:
+        if mode == 0:
+            pqg.qlinear_w4a16_grouped([p["x"][:1] for p in projs], [p["packed"][c] for p in projs],
+                                      [p["scales"][c] for p in projs], None, 128, True, outs=[p["y1"] for p in projs])
+        elif mode == 3:
             for p in projs:  # S6 with binary16 scales
                 pqg.qlinear_w4a16_meta16(p["x"][:1], p["packed16"], p["s16"], None, 128, True, out=p["y1"])
         elif mode == 2:
@@ -297,7 +308,7 @@ def main():
 
     per_part = {k: [] for k in parts}
     gemv_launch_ms = []
-    gemv_seq_ms = []
+    seven_seq_ms = []
     fused_seq_ms = []
     meta16_seq_ms = []
     for marks, gemv_ev, mode in records:
@@ -311,9 +322,11 @@ def main():
                 fused_seq_ms.append(t)
             elif mode == 3:
                 meta16_seq_ms.append(t)
+            elif mode == 4:
+                seven_seq_ms.append(t)
         if mode == 1:  # per-launch kernel durations
             gemv_launch_ms.append([a.elapsed_time(b) for a, b in gemv_ev])
-    gemv_seq_ms = per_part["w4a16_m1"]  # mode 0: the seven launches back to back, between the surrounding marks
+    gemv_seq_ms = per_part["w4a16_m1"]  # mode 0: the grouped launch, between the surrounding marks
     med = lambda v: float(np.median(v))  # noqa: E731
     part_ms = {k: med(v) for k, v in per_part.items()}
     launch_ms = np.median(np.array(gemv_launch_ms), axis=0)  # per projection
@@ -321,8 +334,8 @@ def main():
     gemm_ms = part_ms["w8a8_gemm"]  # one launch per step: event pair around the GEMM + epilogue kernel
 
     value = gemv_bytes / (seq_ms * 1e-3) / 1e9
-    avg_launch_ms = seq_ms / len(projs)
-    achieved = (gemv_bytes / len(projs)) / (avg_launch_ms * 1e-3) / 1e9
+    avg_launch_ms = seq_ms  # one grouped launch streams the whole layer
+    achieved = gemv_bytes / (avg_launch_ms * 1e-3) / 1e9
     tops = w8a8_ops / (gemm_ms * 1e-3) / 1e12
     traffic = read_traffic(GEMV_TRAFFIC_FILE, GEMV_SOURCE)
     gemm_traffic = read_traffic(GEMM_TRAFFIC_FILE, GEMM_SOURCE)
@@ -349,13 +362,13 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_w4a16_gemv (M=1, seven 70B-layer projections)",
+            "kernel": "k_w4a16_gemv_grouped (M=1, the seven 70B-layer projections in one launch)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "bytes_per_launch": gemv_bytes / len(projs),
+            "bytes_per_launch": gemv_bytes,
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
         },
         "w8a8_gemm": {
@@ -406,6 +419,10 @@ def main():
         "w4a16_m1_meta16": {"bytes": gemv_bytes16,
                             "value": round(gemv_bytes16 / (med(meta16_seq_ms) * 1e-3) / 1e9, 1) if meta16_seq_ms else None,
                             "unit": "GB/s", "ms": round(med(meta16_seq_ms), 4) if meta16_seq_ms else None},
+        "w4a16_m1_seven_launches": {"value": round(gemv_bytes / (med(seven_seq_ms) * 1e-3) / 1e9, 1),
+                                    "unit": "GB/s",
+                                    "hbm_frac": round(gemv_bytes / (med(seven_seq_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    "ms": round(med(seven_seq_ms), 4)},
         "w4a16_m1_fused_layout": {"launches": ["+".join(W.L70B_PROJ[i][0] for i in g) for g in groups],
                                   "value": round(gemv_bytes / (med(fused_seq_ms) * 1e-3) / 1e9, 1),
                                   "unit": "GB/s",
@@ -420,9 +437,80 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = 1 << 30
+    out["llama7b_configs"] = llama7b_configs(pqg, W, dev, bf16)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_oracle_per_function"] = cpu_per_function(args.cpu_function_seconds)
     print(json.dumps(out), flush=True)
+
+
+def llama7b_configs(pqg, W, dev, bf16, reps=8, rounds=6):
+    """The Llama-7B attention (4096 x 4096, symmetric INT4 g = 128) and FFN (11008 x 4096 with 41 input columns
+    x10, asymmetric UINT4 at g = 32 and g = 128) configurations: quantize and W4A16 throughput with the
+    weights rotated over R device copies (R x packed bytes >= 512 MB, twice the last-level cache), so every
+    timed call streams its copy from HBM. `reps` launches back to back on consecutive copies are timed as one
+    event pair and averaged; the median over `rounds` such blocks is reported. Also the metadata bytes
+    against the packed weight bytes, as stored (fp32 scales + uint8 zero points) and with 16-bit metadata
+    (binary16 scales + 4-bit zero points)."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+
+    def timed(fn):
+        ts = []
+        for r in range(rounds + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for j in range(reps):
+                fn(r * reps + j)
+            e1.record(stream)
+            e1.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1) / reps)
+        return float(np.median(ts))
+
+    cases = [("attn7b_4096x4096_sym_g128", W.attn7b(ms=(16,)), True, 128, (1, 16)),
+             ("ffn7b_11008x4096_asym_g32", W.ffn7b(ms=(64,)), False, 32, (1, 8, 64)),
+             ("ffn7b_11008x4096_asym_g128", None, False, 128, (1, 8, 64))]
+    ffn = cases[1][1]
+    for name, d, sym, g, ms in cases:
+        d = d if d is not None else ffn
+        w = bf16(d["w"])
+        x = bf16(d["x"])
+        n, k = w.shape
+        packed_b = n * k // 2
+        meta_b = n * (k // g) * (4 + (0 if sym else 1))
+        meta16_b = n * (k // g) * 2 + (0 if sym else (n * (k // g) + 1) // 2)
+        R = max(2, -(-512 * 2 ** 20 // (packed_b + meta_b)))
+        wr = [w] + [w.clone() for _ in range(min(R, 24) - 1)]  # bf16 inputs: 32-86 MiB each, >= 24 copies
+        codes = [torch.empty((n, k // 2), dtype=torch.uint8, device=dev) for _ in range(R)]
+        scales = [torch.empty(n * k // g, dtype=torch.float32, device=dev) for _ in range(R)]
+        zeros = [None if sym else torch.empty(n * k // g, dtype=torch.uint8, device=dev) for _ in range(R)]
+        for c in range(R):
+            pqg.quantize(w, 4, sym, pqg.GROUP, g, out=(codes[c], scales[c], zeros[c]))
+        ys = {m: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for m in ms}
+        torch.cuda.synchronize()
+        q_ms = timed(lambda i: pqg.quantize(wr[i % len(wr)], 4, sym, pqg.GROUP, g,
+                                            out=(codes[i % R], scales[i % R], zeros[i % R])))
+        q_bytes = n * k * 2 + packed_b + meta_b
+        e = {"N": n, "K": k, "symmetric": sym, "group_size": g, "copies": R,
+             "quantize_us": round(q_ms * 1e3, 2), "quantize_gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+             "quantize_hbm_frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "weight_bytes": packed_b + meta_b, "packed_bytes": packed_b, "metadata_bytes": meta_b,
+             "metadata_share": round(meta_b / packed_b, 5), "metadata16_bytes": meta16_b,
+             "metadata16_share": round(meta16_b / packed_b, 5), "w4a16": {}}
+        for m in ms:
+            t = timed(lambda i, m=m: pqg.qlinear_w4a16(x[:m], codes[i % R], scales[i % R], zeros[i % R], g, sym,
+                                                        out=ys[m]))
+            gbs = (packed_b + meta_b) / (t * 1e-3) / 1e9
+            e["w4a16"][str(m)] = {"us": round(t * 1e3, 2), "weight_gbs": round(gbs, 1),
+                                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        out[name] = e
+        del wr, codes, scales, zeros, ys, w
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(target_s):
@@ -451,6 +539,49 @@ def cpu_baseline(target_s):
     return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "first %d rows of each of the seven 70B projections (all of k and v), INT4 g=128 quantize "
                       "+ binary64 W4A16 at M=1, %d passes, %.1f s" % (rows, passes, t_total)}
+
+
+def cpu_per_function(target_s):
+    """Each oracle function timed on bounded samples of the workloads, on all the host threads and on one:
+    quantize (INT4 g = 128, 70B q projection rows), dequantize, smooth (W8A8 layer rows), the W4A16 product at
+    M = 1 and the W8A8 pipeline (smooth, both quantizations, the int64 GEMM, the epilogue) on a token sample.
+    Rates in the unit of each function's own bytes (GB/s) or integer multiply-adds (GMAC/s)."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    w70 = W.l70b_weight(0, rows=np.arange(512))   # 512 x 8192 bf16
+    x70 = W.l70b_x(0, 1)
+    q70, s70, _ = oracle.quantize(w70, 4, True, oracle.GROUP, 128)
+    d8 = W.w8a8(m=64, n=1024, k=4096)
+    nw = w70.size
+    funcs = {
+        "quantize_int4_g128": (lambda: oracle.quantize(w70, 4, True, oracle.GROUP, 128),
+                               nw * 2 + nw // 2 + nw // 128 * 4, "GB/s"),
+        "dequantize_int4_g128": (lambda: oracle.dequantize(q70, s70, None, oracle.GROUP, 128),
+                                 nw // 2 + nw // 128 * 4 + nw * 2, "GB/s"),
+        "w4a16_m1": (lambda: oracle.w4a16(x70, q70, s70, None, 128), nw // 2 + nw // 128 * 4, "GB/s"),
+        "smooth_alpha05": (lambda: oracle.smooth(d8["x"], d8["w"], 0.5), (d8["x"].size + d8["w"].size) * 2, "GB/s"),
+        "w8a8_pipeline": (lambda: oracle.w8a8(d8["x"], d8["w"], 0.5), 64 * 1024 * 4096, "GMAC/s"),
+    }
+    all_threads = oracle.num_threads()
+    res = {"threads_all": all_threads, "sample": "512 x 8192 rows of the 70B q projection; W8A8 64 tokens x 1024 "
+           "channels x 4096", "functions": {}}
+    for name, (fn, units, unit) in funcs.items():
+        row = {"unit": unit}
+        for label, nt in (("all", all_threads), ("one", 1)):
+            oracle.set_num_threads(nt)
+            n, t_total = 0, 0.0
+            while t_total < target_s or n == 0:
+                t0 = time.perf_counter()
+                fn()
+                t_total += time.perf_counter() - t0
+                n += 1
+            row[label] = round(units * n / t_total / 1e9, 4)
+        res["functions"][name] = row
+    oracle.set_num_threads(all_threads)
+    return res
 
 
 if __name__ == "__main__":

@@ -170,6 +170,40 @@ int32_t pqg_qlinear_w4a16(const void *x, int64_t M, int64_t N, int64_t K, const 
                           void *y, int32_t y_dtype, void *stream);
 
 /*
+ * Grouped decode: several independent W4A16 products y_i = x_i W_i^T (as pqg_qlinear_w4a16) in ONE launch
+ * [P3 §11.10.1: at decode every weight of the layer is read once per generated token, so the time is the
+ * whole weight stream; P3 §11.1.6: INT4 groups]. Streaming the row blocks of all the problems as one grid
+ * removes the launch gap and the partly idle tail of each small product (the Llama-70B k and v projections,
+ * 1024 x 8192, do not fill the GPU on their own). Use it for products whose inputs are ready together: the
+ * projections that read the same normalised hidden state, or expert weights.
+ *   problems : HOST array of `count` descriptors (1 <= count <= 8), read during the call only (they are
+ *              copied into the launch), each with
+ *                x        bf16 [M, K] activations (device),
+ *                w_packed uint8 [N, K / 2] INT4 codes as pqg_quantize writes them (device),
+ *                scales   fp32 [N, K / group_size]; zeros uint8 [N, K / group_size], NULL iff symmetric (device),
+ *                y        [M, N] of y_dtype (device, out),
+ *                N, K     the problem's shape (K % group_size == 0; a problem with N == 0 is skipped).
+ *   M        : tokens, 0 <= M <= 4 (the decode kernel; larger M returns PQG_EUNSUPPORTED), common to all.
+ *   group_size, symmetric, y_dtype : common to all problems, as pqg_qlinear_w4a16.
+ * Every problem is checked before anything is enqueued. Each result is that of pqg_qlinear_w4a16 on the
+ * problem alone up to the order of the fp32 partial sums: both run the same per-row-block code, but a single
+ * small product may split K over more waves than the grouped grid does (the grid size decides the split), so
+ * partial sums are added in a different order. Both are within the tolerance of the exact product.
+ * Alignment per problem as pqg_qlinear_w4a16.
+ */
+typedef struct {
+    const void *x;
+    const uint8_t *w_packed;
+    const float *scales;
+    const uint8_t *zeros;
+    void *y;
+    int64_t N, K;
+} pqg_w4a16_problem;
+
+int32_t pqg_qlinear_w4a16_grouped(const pqg_w4a16_problem *problems, int32_t count, int64_t M, int32_t group_size,
+                                  int32_t symmetric, int32_t y_dtype, void *stream);
+
+/*
  * W8A8 linear layer  y[m, n] = (sum_k q_x[m, k] q_w[n, k]) * s_x[m] * s_w[n]
  * [P3 §11.4.5 steps 5-6 (INT8 GEMM, INT32 accumulation, dequantized output); P3 §11.1.4 dynamic
  * activation statistics; P2 §11 vector-wise scales].

@@ -32,9 +32,16 @@ EXPORTS = [
     "pqg_smooth_workspace_bytes", "pqg_smooth", "pqg_qlinear_w4a16", "pqg_qlinear_w8a8", "pqg_gemm_s8s8s32",
     "pqg_qlinear_w4a8", "pqg_kv_quantize_keys", "pqg_kv_dequantize_keys", "pqg_kv_append",
     "pqg_quantize_meta16", "pqg_dequantize_meta16", "pqg_qlinear_w4a16_meta16", "pqg_qlinear_w8a8_noalloc",
+    "pqg_qlinear_w4a16_grouped",
 ]
 
 _lib = None
+
+
+class W4A16Problem(ctypes.Structure):
+    """pqg_w4a16_problem of include/pqg.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("w_packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 class PqgError(RuntimeError):
@@ -89,6 +96,8 @@ def load(path: str = LIB_PATH):
     lib.pqg_qlinear_w4a16_meta16.restype = I32
     lib.pqg_qlinear_w4a16_meta16.argtypes = [P, I64, I64, I64, P, P, P, I32, I32, P, I32, P]
     lib.pqg_kv_append.argtypes = [P, P, I32, I64, I64, P, I64, I32, I32, I32, P, P, P, P, P, P, P, P]
+    lib.pqg_qlinear_w4a16_grouped.restype = I32
+    lib.pqg_qlinear_w4a16_grouped.argtypes = [ctypes.POINTER(W4A16Problem), I32, I64, I32, I32, I32, P]
     lib.pqg_qlinear_w8a8_noalloc.restype = I32
     lib.pqg_qlinear_w8a8_noalloc.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
     if lib.pqg_abi_version() != ABI_VERSION:
@@ -230,6 +239,37 @@ def qlinear_w4a16(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
     _check(lib.pqg_qlinear_w4a16(_ptr(x), M, N, K, _ptr(w_packed), _ptr(scales), _ptr(zeros), group_size,
                                  int(symmetric), _ptr(y), _float_dtype(y), _stream(dev)))
     return y
+
+
+def qlinear_w4a16_grouped(xs, ws, scales, zeros, group_size: int, symmetric: bool, out_dtype=torch.bfloat16,
+                          outs=None):
+    """pqg_qlinear_w4a16_grouped: one launch over several decode products y_i = x_i @ dequant(w_i)^T. xs: bf16
+    [M, K_i] (M <= 4, common); ws: packed [N_i, K_i / 2]; scales / zeros: per problem (zeros None when
+    symmetric). Returns the list of y_i ([M, N_i] of out_dtype, or the tensors of `outs`)."""
+    lib = load()
+    n = len(xs)
+    if not (len(ws) == len(scales) == n and (zeros is None or len(zeros) == n)):
+        raise ValueError("one weight, scale (and zero) tensor per activation tensor")
+    dev = _dev(xs[0])
+    M = xs[0].shape[0]
+    ys = []
+    table = (W4A16Problem * n)()
+    for i in range(n):
+        x, w = xs[i], ws[i]
+        _dev(x)
+        _dev(w)
+        if x.dtype != torch.bfloat16 or x.shape[0] != M:
+            raise ValueError("every x must be bfloat16 with the same number of rows")
+        N, K = w.shape[0], x.shape[1]
+        if w.shape[1] * 2 != K:
+            raise ValueError("w_packed must be [N, K/2]")
+        y = torch.empty((M, N), dtype=out_dtype, device=dev) if outs is None else outs[i]
+        ys.append(y)
+        z = None if zeros is None else zeros[i]
+        table[i] = W4A16Problem(x.data_ptr(), w.data_ptr(), scales[i].data_ptr(), None if z is None else z.data_ptr(),
+                                y.data_ptr(), N, K)
+    _check(lib.pqg_qlinear_w4a16_grouped(table, n, M, group_size, int(symmetric), _float_dtype(ys[0]), _stream(dev)))
+    return ys
 
 
 def qlinear_w8a8(x, smooth_s, w_q: torch.Tensor, w_scales: torch.Tensor, out_dtype=torch.bfloat16, out=None,

@@ -274,6 +274,58 @@ int32_t pqg_qlinear_w4a16(const void *x, int64_t M, int64_t N, int64_t K, const 
     return hip_status(pqg::launch_w4a16(a, as_stream(stream)), "pqg_qlinear_w4a16 launch");
 }
 
+int32_t pqg_qlinear_w4a16_grouped(const pqg_w4a16_problem *problems, int32_t count, int64_t M, int32_t group_size,
+                                  int32_t symmetric, int32_t y_dtype, void *stream)
+{
+    g_err[0] = 0;
+    if (count < 1 || count > pqg::kMaxGroupedProblems)
+        return fail(PQG_EINVAL, "count must be 1 .. %d (got %d)", pqg::kMaxGroupedProblems, count);
+    if (!problems)
+        return fail(PQG_EINVAL, "problems is required");
+    if (M < 0)
+        return fail(PQG_EINVAL, "negative shape");
+    if (M > 4)
+        return fail(PQG_EUNSUPPORTED, "the grouped decode takes M <= 4 tokens (got %lld)", (long long)M);
+    if (!valid_float_dtype(y_dtype))
+        return fail(PQG_EINVAL, "unknown y_dtype %d", y_dtype);
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(PQG_EINVAL, "group_size must be 32, 64 or 128 (got %d)", group_size);
+    if (symmetric != 0 && symmetric != 1)
+        return fail(PQG_EINVAL, "symmetric must be 0 or 1");
+    pqg::W4A16Args q[pqg::kMaxGroupedProblems];
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i) {
+        const pqg_w4a16_problem &p = problems[i];
+        if (p.N < 0 || p.K < 0)
+            return fail(PQG_EINVAL, "problem %d: negative shape", i);
+        if (p.K % group_size != 0)
+            return fail(PQG_EINVAL, "problem %d: K (%lld) must be a multiple of group_size (%d)", i, (long long)p.K,
+                        group_size);
+        if (M > 0 && p.N > 0) {
+            if (p.K == 0)
+                return fail(PQG_EUNSUPPORTED, "problem %d: K == 0", i);
+            if (!p.x || !p.w_packed || !p.scales || !p.y)
+                return fail(PQG_EINVAL, "problem %d: x, w_packed, scales and y are required", i);
+            if (symmetric && p.zeros)
+                return fail(PQG_EINVAL, "problem %d: zeros must be NULL for symmetric codes", i);
+            if (!symmetric && !p.zeros)
+                return fail(PQG_EINVAL, "problem %d: zeros is required for asymmetric codes", i);
+            if (!aligned(p.x, 16) || !aligned(p.w_packed, 16) || !aligned(p.scales, 4) || !aligned(p.y, 4))
+                return fail(PQG_EINVAL, "problem %d: misaligned pointer (x, w_packed: 16 bytes; scales, y: 4 bytes)",
+                            i);
+            rows += p.N;
+        }
+        q[i] = pqg::W4A16Args{static_cast<const uint16_t *>(p.x), M, p.N, p.K, p.w_packed, p.scales, p.zeros,
+                              group_size, symmetric != 0, p.y, y_dtype == PQG_BF16};
+    }
+    if (M == 0 || rows == 0)
+        return PQG_OK;
+    if (rows > ((int64_t)1 << 33))
+        return fail(PQG_EUNSUPPORTED, "more than 2^33 output rows in one launch");
+    pqg::W4A16GroupedArgs a{q, count, M, group_size, symmetric != 0, y_dtype == PQG_BF16};
+    return hip_status(pqg::launch_w4a16_grouped(a, as_stream(stream)), "pqg_qlinear_w4a16_grouped launch");
+}
+
 int32_t pqg_qlinear_w8a8(const void *x, const float *smooth, const int8_t *w_q, const float *w_scales, int64_t M,
                          int64_t N, int64_t K, void *y, int32_t y_dtype, int8_t *x_q, float *x_scales, void *stream)
 {

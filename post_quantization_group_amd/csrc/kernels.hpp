@@ -101,6 +101,34 @@ hipError_t launch_smooth(const SmoothArgs &a, hipStream_t st);
 
 hipError_t launch_w4a16(const W4A16Args &a, hipStream_t st);
 
+// Several independent decode products (M <= 4 tokens each, one group size / symmetry / output type) in one
+// launch; the table travels in the kernel arguments.
+constexpr int kMaxGroupedProblems = 8;
+struct GroupedW4A16 {
+    struct Problem {
+        const uint16_t *x;  // bf16 [M, K]
+        const uint8_t *w;   // [N, K/2]
+        const float *scales;
+        const uint16_t *scales16;  // unused here (fp32 scales); kept so the row-block code takes either
+        const uint8_t *zeros;
+        void *y;            // [M, N]
+        int64_t N, K;
+    } p[kMaxGroupedProblems];
+    int64_t begin[kMaxGroupedProblems + 1];  // first row block of each problem, begin[count] = total
+    int count;
+};
+
+struct W4A16GroupedArgs {
+    const W4A16Args *problems;  // host array: x, N, K, w, scales, zeros, y of each problem
+    int count;
+    int64_t M;
+    int group_size;
+    bool symmetric;
+    bool y_bf16;
+};
+
+hipError_t launch_w4a16_grouped(const W4A16GroupedArgs &a, hipStream_t st);
+
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st);
 
 // W4A8: INT8 per-token activation codes x INT4 per-group weight codes.

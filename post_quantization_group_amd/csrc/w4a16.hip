@@ -28,6 +28,8 @@
 //
 // The matrix-core variant below keeps ordinary (allocating) weight loads: with non-temporal ones it ran
 // slower and left dirty lines in the last-level cache that slowed the kernels after it.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -169,18 +171,18 @@ __device__ __forceinline__ void stage_compute(const Stage<MT, R> &st, float acc[
     }
 }
 
-// MT activation rows (1..4), R weight rows per block, group size G; S = blockDim.x / 64 waves split K.
-template <int MT, int R, int G, bool SYM, bool OUT_BF16, bool M16 = false>
-__global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__ x, int64_t N, int64_t K,
-                                                    const uint8_t *__restrict__ w, const void *__restrict__ scales,
-                                                    const uint8_t *__restrict__ zeros, void *__restrict__ y,
-                                                    int64_t y_ld)
+// One row block (rows rb * R .. rb * R + R - 1) of the decode product: MT activation rows (1..4), R weight rows,
+// group size G; S = blockDim.x / 64 waves split K. `red` is the block's LDS for combining the S partial sums.
+template <int MT, int R, int G, bool SYM, bool OUT_BF16, bool M16>
+__device__ __forceinline__ void gemv_rowblock(const uint16_t *__restrict__ x, int64_t N, int64_t K,
+                                              const uint8_t *__restrict__ w, const void *__restrict__ scales,
+                                              const uint8_t *__restrict__ zeros, void *__restrict__ y, int64_t y_ld,
+                                              int64_t rb, float (*red)[R * MT])
 {
-    __shared__ float red[kMaxWavesPerRow][R * MT];
     const int lane = threadIdx.x % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar loop bounds
     const int S = blockDim.x / kWave;
-    const int64_t row0 = (int64_t)blockIdx.x * R;
+    const int64_t row0 = rb * R;
     const int chunks = (int)(K / 32);  // 32 codes = 16 bytes per lane
     const int s_shift = __builtin_ctz(S);  // S is a power of two
     const int c_begin = (chunks * wv) >> s_shift;
@@ -282,6 +284,34 @@ __global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__
                         yf[m * y_ld + row0 + r] = acc[r][m];
                 }
     }
+}
+
+// MT activation rows (1..4), R weight rows per block, group size G; S = blockDim.x / 64 waves split K.
+template <int MT, int R, int G, bool SYM, bool OUT_BF16, bool M16 = false>
+__global__ __launch_bounds__(512) void k_w4a16_gemv(const uint16_t *__restrict__ x, int64_t N, int64_t K,
+                                                    const uint8_t *__restrict__ w, const void *__restrict__ scales,
+                                                    const uint8_t *__restrict__ zeros, void *__restrict__ y,
+                                                    int64_t y_ld)
+{
+    __shared__ float red[kMaxWavesPerRow][R * MT];
+    gemv_rowblock<MT, R, G, SYM, OUT_BF16, M16>(x, N, K, w, scales, zeros, y, y_ld, blockIdx.x, red);
+}
+
+// Several independent products in one launch: the grid is the concatenation of the problems' row blocks
+// (problem p owns blocks [begin[p], begin[p + 1])); a block finds its problem with a uniform scan of the
+// table, which lives in the kernel arguments.
+template <int MT, int R, int G, bool SYM, bool OUT_BF16, bool M16 = false>
+__global__ __launch_bounds__(512) void k_w4a16_gemv_grouped(const GroupedW4A16 table)
+{
+    __shared__ float red[kMaxWavesPerRow][R * MT];
+    const int64_t b = blockIdx.x;
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGroupedProblems; ++i)
+        p += (i < table.count && b >= table.begin[i]) ? 1 : 0;
+    const GroupedW4A16::Problem &q = table.p[p];
+    gemv_rowblock<MT, R, G, SYM, OUT_BF16, M16>(q.x, q.N, q.K, q.w, M16 ? q.scales16 : (const void *)q.scales, q.zeros,
+                                               q.y, q.N, b - table.begin[p], red);
 }
 
 // ------------------------------------------------------------------ matrix-core variant (M >= 5 not taken by the
@@ -916,6 +946,79 @@ hipError_t gemv_g(const W4A16Args &a, int mt, const uint16_t *x, void *y, hipStr
 constexpr int64_t kMfmaMinTokens = 5;
 // Up to this many tokens the staged kernel runs (in launches of 32 tokens, each re-reading the weights).
 constexpr int64_t kStagedMaxTokens = 64;
+
+namespace {
+
+template <int MT, int R, int G, bool SYM>
+hipError_t grouped_launch(const W4A16GroupedArgs &a, hipStream_t st)
+{
+    // problems with the most K first: their blocks run longest, so they are dispatched first
+    int order[kMaxGroupedProblems];
+    int n = 0;
+    for (int i = 0; i < a.count; ++i)
+        if (a.problems[i].N > 0)
+            order[n++] = i;
+    std::stable_sort(order, order + n, [&](int u, int v) { return a.problems[u].K > a.problems[v].K; });
+    if (n == 0)
+        return hipSuccess;
+    GroupedW4A16 t = {};
+    int64_t total = 0, kmin = a.problems[order[0]].K;
+    for (int j = 0; j < n; ++j) {
+        const W4A16Args &q = a.problems[order[j]];
+        t.p[j] = {q.x, q.w, q.scales, nullptr, q.zeros, q.y, q.N, q.K};
+        t.begin[j] = total;
+        total += (q.N + R - 1) / R;
+        kmin = std::min(kmin, q.K);
+    }
+    t.begin[n] = total;
+    for (int j = n + 1; j <= kMaxGroupedProblems; ++j)
+        t.begin[j] = total;
+    t.count = n;
+    const int S = waves_per_row_block(total, kmin, 4096);
+    const dim3 grid((unsigned)total), block(kWave * S);
+    if (a.y_bf16)
+        k_w4a16_gemv_grouped<MT, R, G, SYM, true><<<grid, block, 0, st>>>(t);
+    else
+        k_w4a16_gemv_grouped<MT, R, G, SYM, false><<<grid, block, 0, st>>>(t);
+    return hipGetLastError();
+}
+
+template <int G, bool SYM>
+hipError_t grouped_mt(const W4A16GroupedArgs &a, hipStream_t st)
+{
+    switch (a.M) {
+    case 1:
+        return grouped_launch<1, 4, G, SYM>(a, st);
+    case 2:
+        return grouped_launch<2, 4, G, SYM>(a, st);
+    case 3:
+        return grouped_launch<3, 2, G, SYM>(a, st);
+    default:
+        return grouped_launch<4, 2, G, SYM>(a, st);
+    }
+}
+
+template <bool SYM>
+hipError_t grouped_g(const W4A16GroupedArgs &a, hipStream_t st)
+{
+    switch (a.group_size) {
+    case 32:
+        return grouped_mt<32, SYM>(a, st);
+    case 64:
+        return grouped_mt<64, SYM>(a, st);
+    default:
+        return grouped_mt<128, SYM>(a, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_w4a16_grouped(const W4A16GroupedArgs &a, hipStream_t st)
+{
+    if (a.M < 1 || a.M > 4 || a.count < 1 || a.count > kMaxGroupedProblems)
+        return hipErrorInvalidValue;
+    return a.symmetric ? grouped_g<true>(a, st) : grouped_g<false>(a, st);
+}
 
 hipError_t launch_w4a16(const W4A16Args &a, hipStream_t st)
 {

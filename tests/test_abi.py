@@ -254,3 +254,27 @@ def test_w8a8_noalloc_rejects_before_touching_the_device(lib):
         assert call(**kw) == rc, kw
         assert needle in lib.pqg_last_error().decode(), (kw, lib.pqg_last_error())
     assert call(M=0, x=None) == pqg.OK
+
+
+def test_w4a16_grouped_rejects(lib):
+    """Every problem is checked on the host before anything is enqueued."""
+    P = pqg.W4A16Problem
+
+    def call(n=2, M=1, g=128, sym=1, yd=1, **kw):
+        probs = (P * max(n, 1))()
+        for i in range(max(n, 1)):
+            probs[i] = P(0x10000, 0x10000, 0x10000, None, 0x10000, 1024, 8192)
+        for k, v in kw.items():
+            i, field = k.split("_", 1)
+            setattr(probs[int(i[1:])], field, v)
+        return lib.pqg_qlinear_w4a16_grouped(probs, n, M, g, sym, yd, None)
+    for kw, rc, needle in [(dict(n=0), pqg.EINVAL, "count"), (dict(n=9), pqg.EINVAL, "count"),
+                           (dict(M=5), pqg.EUNSUPPORTED, "M <= 4"), (dict(g=48), pqg.EINVAL, "group_size"),
+                           (dict(yd=3), pqg.EINVAL, "y_dtype"), (dict(p1_K=8000), pqg.EINVAL, "problem 1"),
+                           (dict(p0_x=None), pqg.EINVAL, "required"), (dict(sym=0), pqg.EINVAL, "zeros is required"),
+                           (dict(p1_zeros=0x10000), pqg.EINVAL, "must be NULL"), (dict(p1_K=0), pqg.EUNSUPPORTED, "K == 0"),
+                           (dict(p0_w_packed=0x10001), pqg.EINVAL, "misaligned"), (dict(p1_N=-1), pqg.EINVAL, "negative")]:
+        assert call(**kw) == rc, kw
+        assert needle in lib.pqg_last_error().decode(), (kw, lib.pqg_last_error())
+    assert call(M=0) == pqg.OK
+    assert call(p0_N=0, p1_N=0) == pqg.OK
