@@ -8,7 +8,8 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import announce, normwise, to_f64, to_gpu, to_gpu_bf16
+from helpers import (REL_BF16, REL_W4A16_F32, abs_terms_w4, announce, assert_per_element, normwise, to_f64, to_gpu,
+                     to_gpu_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +48,7 @@ def test_grouped_small_ragged(gpu_lib, m, gs, sym):
         cs.append(to_gpu(oracle.pack_int4(q)))
         ss.append(to_gpu(so))
         zs.append(None if sym else to_gpu(zo))
-        refs.append(oracle.w4a16(x, q, so, zo, gs) if n else None)
+        refs.append((oracle.w4a16(x, q, so, zo, gs), abs_terms_w4(x, q, so, zo, gs)) if n else None)
     ys = gpu_lib.qlinear_w4a16_grouped(xs, cs, ss, None if sym else zs, gs, sym, out_dtype=torch.float32)
     singles = [gpu_lib.qlinear_w4a16(xs[i], cs[i], ss[i], zs[i], gs, sym, out_dtype=torch.float32)
                for i in range(len(shapes))]
@@ -57,7 +58,8 @@ def test_grouped_small_ragged(gpu_lib, m, gs, sym):
         if n == 0:
             continue
         _close_to_single(ys[i], singles[i])
-        assert normwise(to_f64(ys[i]), refs[i]) <= TOL_F32, i
+        assert normwise(to_f64(ys[i]), refs[i][0]) <= TOL_F32, i
+        assert_per_element(to_f64(ys[i]), refs[i][0], refs[i][1], REL_W4A16_F32, "problem %d" % i)
 
 
 def test_grouped_eight_problems_bf16(gpu_lib):
@@ -73,11 +75,12 @@ def test_grouped_eight_problems_bf16(gpu_lib):
         xs.append(to_gpu_bf16(x))
         cs.append(to_gpu(oracle.pack_int4(q)))
         ss.append(to_gpu(so))
-        refs.append(oracle.w4a16(x, q, so, None, 128))
+        refs.append((oracle.w4a16(x, q, so, None, 128), abs_terms_w4(x, q, so, None, 128)))
     ys = gpu_lib.qlinear_w4a16_grouped(xs, cs, ss, None, 128, True)
     torch.cuda.synchronize()
     for i in range(8):
-        assert normwise(to_f64(ys[i]), refs[i]) <= TOL_BF16, i
+        assert normwise(to_f64(ys[i]), refs[i][0]) <= TOL_BF16, i
+        assert_per_element(to_f64(ys[i]), refs[i][0], refs[i][1], REL_BF16, "problem %d" % i)
 
 
 def test_grouped_l70b_layer_m1(gpu_lib):
@@ -91,7 +94,7 @@ def test_grouped_l70b_layer_m1(gpu_lib):
         x = W.l70b_x(p, 1)
         rows = np.unique(np.concatenate([np.random.default_rng(50 + p).choice(n, 22, replace=False), [0, n - 1]]))
         q, so, _ = oracle.quantize(w[rows], 4, True, 2, 128)
-        samples.append((rows, oracle.w4a16(x, q, so, None, 128)))
+        samples.append((rows, oracle.w4a16(x, q, so, None, 128), abs_terms_w4(x, q, so, None, 128)))
         xs.append(to_gpu_bf16(x))
         cs.append(codes)
         ss.append(s)
@@ -101,5 +104,6 @@ def test_grouped_l70b_layer_m1(gpu_lib):
     torch.cuda.synchronize()
     for i in range(7):
         _close_to_single(ys[i], singles[i])
-        rows, ref = samples[i]
+        rows, ref, terms = samples[i]
         assert normwise(to_f64(ys[i])[:, rows], ref) <= TOL_BF16, W.L70B_PROJ[i][0]
+        assert_per_element(to_f64(ys[i])[:, rows], ref, terms, REL_BF16, W.L70B_PROJ[i][0])
