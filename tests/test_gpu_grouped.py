@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import (REL_BF16, REL_W4A16_F32, abs_terms_w4, announce, assert_per_element, normwise, to_f64, to_gpu,
+from helpers import (BOUND_BF16, BOUND_W4A16_F32, abs_terms_w4, announce, assert_per_element, normwise, to_f64, to_gpu,
                      to_gpu_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -59,7 +59,7 @@ def test_grouped_small_ragged(gpu_lib, m, gs, sym):
             continue
         _close_to_single(ys[i], singles[i])
         assert normwise(to_f64(ys[i]), refs[i][0]) <= TOL_F32, i
-        assert_per_element(to_f64(ys[i]), refs[i][0], refs[i][1], REL_W4A16_F32, "problem %d" % i)
+        assert_per_element(to_f64(ys[i]), refs[i][0], refs[i][1], BOUND_W4A16_F32, "problem %d" % i)
 
 
 def test_grouped_eight_problems_bf16(gpu_lib):
@@ -80,7 +80,7 @@ def test_grouped_eight_problems_bf16(gpu_lib):
     torch.cuda.synchronize()
     for i in range(8):
         assert normwise(to_f64(ys[i]), refs[i][0]) <= TOL_BF16, i
-        assert_per_element(to_f64(ys[i]), refs[i][0], refs[i][1], REL_BF16, "problem %d" % i)
+        assert_per_element(to_f64(ys[i]), refs[i][0], refs[i][1], BOUND_BF16, "problem %d" % i)
 
 
 def test_grouped_l70b_layer_m1(gpu_lib):
@@ -106,4 +106,4 @@ def test_grouped_l70b_layer_m1(gpu_lib):
         _close_to_single(ys[i], singles[i])
         rows, ref, terms = samples[i]
         assert normwise(to_f64(ys[i])[:, rows], ref) <= TOL_BF16, W.L70B_PROJ[i][0]
-        assert_per_element(to_f64(ys[i])[:, rows], ref, terms, REL_BF16, W.L70B_PROJ[i][0])
+        assert_per_element(to_f64(ys[i])[:, rows], ref, terms, BOUND_BF16, W.L70B_PROJ[i][0])

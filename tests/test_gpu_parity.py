@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import (REL_BF16, REL_W4A8_F32, REL_W4A16_F32, REL_W8A8_F32, abs_terms_i8, abs_terms_w4, abs_terms_w4a8,
+from helpers import (BOUND_BF16, BOUND_W4A8_F32, BOUND_W4A16_F32, BOUND_W8A8_BF16, BOUND_W8A8_F32, abs_terms_i8, abs_terms_w4, abs_terms_w4a8,
                      announce, assert_per_element, bf16_tensor_bits, normwise, to_f64, to_gpu, to_gpu_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -159,7 +159,7 @@ def w4a16_case(pqg, w_host, w_is_bf16, x_u16, sym, gs, out_dtype):
     q, so, zo = oracle.quantize(w_host, 4, sym, 2, gs)
     y_ref = oracle.w4a16(x_u16, q, so, zo, gs)
     gq = (codes.cpu().numpy(), s.cpu().numpy(), None if z is None else z.cpu().numpy())
-    rel = REL_BF16 if out_dtype == torch.bfloat16 else REL_W4A16_F32
+    rel = BOUND_BF16 if out_dtype == torch.bfloat16 else BOUND_W4A16_F32
     assert_per_element(to_f64(y), y_ref, abs_terms_w4(x_u16, q, so, zo, gs), rel, "W4A16")
     return to_f64(y), y_ref, gq, (q, so, zo)
 
@@ -262,7 +262,7 @@ def test_w4a16_l70b_sampled(gpu_lib, proj):
         y_ref = oracle.w4a16(x[:m], q, so, None, 128)
         err = normwise(ys, y_ref)
         assert err <= TOL_BF16, (m, err)
-        assert_per_element(ys, y_ref, abs_terms_w4(x[:m], q, so, None, 128), REL_BF16, "70B %s M=%d" % (name, m))
+        assert_per_element(ys, y_ref, abs_terms_w4(x[:m], q, so, None, 128), BOUND_BF16, "70B %s M=%d" % (name, m))
 
 
 # --------------------------------------------------------------------------- smoothing and W8A8
@@ -358,7 +358,7 @@ def test_w8a8_full_layer(gpu_lib):
     y_ref = oracle.w8a8_epilogue(acc_ref, sx[toks], sw)
     err = normwise(to_f64(y)[toks], y_ref)
     assert err <= TOL_BF16, err
-    assert_per_element(to_f64(y)[toks], y_ref, abs_terms_i8(qx[toks], sx[toks], qw, sw), REL_BF16, "W8A8 layer")
+    assert_per_element(to_f64(y)[toks], y_ref, abs_terms_i8(qx[toks], sx[toks], qw, sw), BOUND_W8A8_BF16, "W8A8 layer")
 
 
 @pytest.mark.parametrize("mnk", [(5, 77, 96), (130, 200, 512), (300, 264, 128), (513, 385, 192),
@@ -377,7 +377,7 @@ def test_w8a8_small_fp32_out(gpu_lib, mnk):
     assert np.array_equal(w_q.cpu().numpy(), r["q_w"])
     err = normwise(to_f64(y), r["y"])
     assert err <= TOL_F32, err
-    assert_per_element(to_f64(y), r["y"], abs_terms_i8(r["q_x"], r["s_x"], r["q_w"], r["s_w"]), REL_W8A8_F32, "W8A8")
+    assert_per_element(to_f64(y), r["y"], abs_terms_i8(r["q_x"], r["s_x"], r["q_w"], r["s_w"]), BOUND_W8A8_F32, "W8A8")
     # pre-quantized activations (x = NULL): only the GEMM + epilogue runs, same result bit for bit
     y2, _, _ = gpu_lib.qlinear_w8a8(None, None, w_q, s_w, out_dtype=torch.float32, x_q=x_q, x_scales=s_x)
     torch.cuda.synchronize()
@@ -402,7 +402,7 @@ def test_w8a8_small_bf16_out(gpu_lib, mnk):
     assert np.array_equal(w_q.cpu().numpy(), r["q_w"])
     err = normwise(to_f64(y), r["y"])
     assert err <= TOL_BF16, err
-    assert_per_element(to_f64(y), r["y"], abs_terms_i8(r["q_x"], r["s_x"], r["q_w"], r["s_w"]), REL_BF16, "W8A8 bf16")
+    assert_per_element(to_f64(y), r["y"], abs_terms_i8(r["q_x"], r["s_x"], r["q_w"], r["s_w"]), BOUND_W8A8_BF16, "W8A8 bf16")
 
 
 # --------------------------------------------------------------------------- static per-tensor path
@@ -521,7 +521,7 @@ def test_w4a8_small_fp32(gpu_lib, mnk, gs, sym):
     y_ref = oracle.w4a8(qx, sx, q, so, zo, gs)
     err = normwise(to_f64(y), y_ref)
     assert err <= TOL_F32, err
-    assert_per_element(to_f64(y), y_ref, abs_terms_w4a8(qx, sx, q, so, zo, gs), REL_W4A8_F32, "W4A8")
+    assert_per_element(to_f64(y), y_ref, abs_terms_w4a8(qx, sx, q, so, zo, gs), BOUND_W4A8_F32, "W4A8")
 
 
 @pytest.mark.parametrize("mnk,gs,sym", [((130, 200, 384), 128, True), ((257, 136, 256), 32, False),
@@ -540,7 +540,7 @@ def test_w4a8_small_bf16(gpu_lib, mnk, gs, sym):
     y_ref = oracle.w4a8(qx, sx, q, so, zo, gs)
     err = normwise(to_f64(y), y_ref)
     assert err <= TOL_BF16, err
-    assert_per_element(to_f64(y), y_ref, abs_terms_w4a8(qx, sx, q, so, zo, gs), REL_BF16, "W4A8 bf16")
+    assert_per_element(to_f64(y), y_ref, abs_terms_w4a8(qx, sx, q, so, zo, gs), BOUND_BF16, "W4A8 bf16")
 
 
 def test_w4a8_full_layer(gpu_lib):
@@ -566,7 +566,7 @@ def test_w4a8_full_layer(gpu_lib):
     y_ref = oracle.w4a8(qx[toks].astype(np.int8), sx[toks], q, sw, None, 128)
     err = normwise(to_f64(y)[toks], y_ref)
     assert err <= TOL_BF16, err
-    assert_per_element(to_f64(y)[toks], y_ref, abs_terms_w4a8(qx[toks], sx[toks], q, sw, None, 128), REL_BF16,
+    assert_per_element(to_f64(y)[toks], y_ref, abs_terms_w4a8(qx[toks], sx[toks], q, sw, None, 128), BOUND_BF16,
                        "W4A8 layer")
 
 
@@ -757,7 +757,7 @@ def test_meta16_gemv(gpu_lib, m, nk, gs, sym):
     y_ref = oracle.w4a16(x, q, oracle.f16_to_f32(so), zo, gs)
     err = normwise(to_f64(y), y_ref)
     assert err <= TOL_F32, err
-    assert_per_element(to_f64(y), y_ref, abs_terms_w4(x, q, oracle.f16_to_f32(so), zo, gs), REL_W4A16_F32, "meta16")
+    assert_per_element(to_f64(y), y_ref, abs_terms_w4(x, q, oracle.f16_to_f32(so), zo, gs), BOUND_W4A16_F32, "meta16")
 
 
 def test_meta16_gemv_70b_gate(gpu_lib):
@@ -777,7 +777,7 @@ def test_meta16_gemv_70b_gate(gpu_lib):
     y_ref = oracle.w4a16(x, q, oracle.f16_to_f32(so), None, 128)
     err = normwise(to_f64(y)[:, rows], y_ref)
     assert err <= TOL_F32, err
-    assert_per_element(to_f64(y)[:, rows], y_ref, abs_terms_w4(x, q, oracle.f16_to_f32(so), None, 128), REL_W4A16_F32,
+    assert_per_element(to_f64(y)[:, rows], y_ref, abs_terms_w4(x, q, oracle.f16_to_f32(so), None, 128), BOUND_W4A16_F32,
                        "meta16 70B gate")
 
 
