@@ -12,8 +12,9 @@ One step is one pass over every stage of the quantized linear layer on synthetic
              launches back to back; the seven launches with events between them, for per-projection times;
              four launches over q|k|v and gate|up stored as concatenated matrices sharing their input, as
              serving engines store them; and a third copy of the layer with 16-bit metadata)
-  w4a16_m32  the seven projections at batch 32
-  w4a16_m8   the seven projections at batch 8
+  w4a16_m32  the layer at batch 32, four launches over the concatenated layout (q|k|v, o, gate|up, down;
+             every fifth step the seven projections instead, reported apart)
+  w4a16_m8   the same at batch 8
   smooth     SmoothQuant factor, alpha = 0.5, X 2048x4096 (41 channels x50), W 11008x4096
   wquant     W' = W diag(s) -> INT8 per output channel
   w8a8       dynamic per-token INT8 activations + INT8 GEMM + s_x*s_w epilogue, 2048x11008x4096
@@ -128,7 +129,9 @@ def main():
         fused.append(dict(members=g, n=n_sum, k=k,
                           packed=[torch.empty((n_sum, k // 2), dtype=torch.uint8, device=dev) for _ in range(2)],
                           scales=[torch.empty(n_sum * k // 128, dtype=torch.float32, device=dev) for _ in range(2)],
-                          y1=torch.empty((1, n_sum), dtype=torch.bfloat16, device=dev)))
+                          y1=torch.empty((1, n_sum), dtype=torch.bfloat16, device=dev),
+                          y8=torch.empty((8, n_sum), dtype=torch.bfloat16, device=dev),
+                          y32=torch.empty((32, n_sum), dtype=torch.bfloat16, device=dev)))
     projs = []
     for f in fused:
         r0 = 0
@@ -198,6 +201,7 @@ def main():
         # dequantize left in the last-level cache), and the batch-1 decode pass streams copy c, last touched
         # more than 2 GB of traffic earlier: cold weights and a clean cache, as in a decode loop.
         c, o = i % 2, 1 - i % 2
+        mode = i % 5
         marks = {}
         if rec:
             marks["start"] = ev()
@@ -254,12 +258,15 @@ def main():
         if rec:
             marks["kv_append_groups"] = ev()
             marks["kv_append_groups"].record(stream)
-        for p in projs:  # S7: batch 32
+        # the batched passes run over the concatenated layout (q|k|v, o, gate|up, down: four launches), or
+        # over the seven projections in mode 4
+        batched = projs if mode == 4 else fused
+        for p in batched:  # S7: batch 32
             pqg.qlinear_w4a16(p["x"], p["packed"][o], p["scales"][o], None, 128, True, out=p["y32"])
         if rec:
             marks["w4a16_m32"] = ev()
             marks["w4a16_m32"].record(stream)
-        for p in projs:  # S7: batch 8, same copy
+        for p in batched:  # S7: batch 8, same copy
             pqg.qlinear_w4a16(p["x"][:8], p["packed"][o], p["scales"][o], None, 128, True, out=p["y8"])
         if rec:
             marks["w4a16_m8"] = ev()
@@ -268,7 +275,6 @@ def main():
         # 0: value), the seven launches with events between them (mode 1: per-kernel durations; the events
         # break back-to-back dispatch), the four launches of the concatenated layout (mode 2), the seven
         # launches over the copy with 16-bit metadata (mode 3), or the seven launches back to back (mode 4).
-        mode = i % 5
         gemv_ev = []
         if mode == 0:
             pqg.qlinear_w4a16_grouped([p["x"][:1] for p in projs], [p["packed"][c] for p in projs],
@@ -311,12 +317,15 @@ def main():
     seven_seq_ms = []
     fused_seq_ms = []
     meta16_seq_ms = []
+    batched_seven = {"w4a16_m32": [], "w4a16_m8": []}
     for marks, gemv_ev, mode in records:
         prev = marks["start"]
         for k in parts:
             t = prev.elapsed_time(marks[k])
             prev = marks[k]
-            if k != "w4a16_m1" or mode == 0:
+            if k in batched_seven and mode == 4:
+                batched_seven[k].append(t)
+            elif k != "w4a16_m1" or mode == 0:
                 per_part[k].append(t)
             elif mode == 2:
                 fused_seq_ms.append(t)
@@ -402,9 +411,14 @@ def main():
         },
         "per_projection_event_us": {p["name"]: round(float(t) * 1e3, 2) for p, t in zip(projs, launch_ms)},
         "stage_ms": {k: round(v, 4) for k, v in part_ms.items()},
-        # the batched passes over the same weight stream (packed codes + scales), as weight GB/s
+        # the batched passes over the same weight stream (packed codes + scales), as weight GB/s: over the
+        # concatenated layout (four launches), and over the seven projections (steps of mode 4)
         "w4a16_batched_weight_gbs": {m: round(gemv_bytes / (part_ms["w4a16_m%d" % m] * 1e-3) / 1e9, 1)
                                      for m in (8, 32)},
+        "w4a16_batched_layout": ["+".join(W.L70B_PROJ[i][0] for i in g) for g in groups],
+        "w4a16_batched_seven_launches_gbs": {
+            m: (round(gemv_bytes / (med(batched_seven["w4a16_m%d" % m]) * 1e-3) / 1e9, 1)
+                if batched_seven["w4a16_m%d" % m] else None) for m in (8, 32)},
         # the static per-tensor activation quantize of the W8A8 layer (bf16 X' in, INT8 codes and the per-token
         # copy of the scale out), and the static layer = it plus the same GEMM + epilogue launch
         "w8a8_static": {"actquant_us": round(part_ms["w8a8_static_actquant"] * 1e3, 2),

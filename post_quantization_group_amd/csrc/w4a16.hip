@@ -571,8 +571,13 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__
 //     same two 16-byte reads.
 //   * The activations are re-paired as (x_j, x_{j+4}) once, when they are written to LDS, to match the
 //     nibble-pair dequantization.
-//   * One more MFMA against a B of ones gives sum_k x over each group for the lane's tokens, and
-//     acc += s * (D - (128 + off) * xsum) per group.
+//   * acc += s * (D - (128 + off) * xsum) per group, where xsum = sum_k x over the group for the lane's tokens.
+//     Up to 8 tokens, xsum comes from the VALU: when a lane stages its 8 activations it adds them with dot2
+//     against ones, a DPP butterfly over the lanes of its group finishes each token's sum, and the sums go
+//     to LDS beside the activations. For more tokens one more MFMA against a B of ones computes it (the
+//     VALU sums would then cost more issue slots than the MFMA).
+//   * Only the accumulator registers that hold staged tokens are folded, reduced and stored (4 for up to
+//     8 tokens, 8 for up to 16).
 //   * Scales (and zero points) of four groups come with one load; they go through a buffer resource, so the
 //     read past the last row's groups returns zero instead of touching memory.
 //   * The next step's global loads are issued right after the current step's LDS stores, so they are in
@@ -596,8 +601,11 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
     constexpr int GPS = 128 / G;   // groups per 128-code step
     constexpr int TPG = 8 / GPS;   // MFMAs per group
     constexpr int SPM = 4 / GPS;   // steps per metadata load (four groups)
-    constexpr int kRegion = 2048 + XI * 1024;  // 32 rows x 64 B of codes, 4 XI tokens x 256 B
     constexpr int kTokens = 4 * XI;
+    constexpr bool XV = XI <= 2;                // group sums of x on the VALU (else by MFMA)
+    constexpr int NR = XI >= 8 ? 16 : 2 * XI;   // accumulator registers that hold staged tokens
+    // 32 rows x 64 B of codes, 4 XI tokens x 256 B, and with XV the GPS x kTokens group sums of x
+    constexpr int kRegion = 2048 + XI * 1024 + (XV ? GPS * kTokens * 4 : 0);
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStageMaxWaves * kRegion];
     const int lane = threadIdx.x % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -614,6 +622,7 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
     const bf16x8_t ones = as_bf16x8(kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair);
     uint8_t *const wl = lds + wv * kRegion;  // [32 rows][4 chunks of 16 B], chunk ^= (row / 4) % 4
     uint8_t *const xl = wl + 2048;           // [kTokens][16 pieces of 16 B], piece ^= token % 16
+    float *const xsl = reinterpret_cast<float *>(xl + XI * 1024);  // [GPS][kTokens] (XV)
 
     // global -> LDS: weight instruction I covers rows 16 I + lane / 4 (piece lane % 4), activation
     // instruction I tokens 4 I + lane / 16 (piece lane % 16); tokens past M repeat token M - 1.
@@ -708,6 +717,21 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
             *reinterpret_cast<u32x4_t *>(xl + xdst[I]) =
                 u32x4_t{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
                         __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+            if (XV) {
+                // the lane's 8 activations, then the G / 8 lanes of its group (one token's 128 codes fill a
+                // 16-lane row): quads, half rows, the whole row
+                float sx = dot2(v.x, kBf16OnePair,
+                                dot2(v.y, kBf16OnePair, dot2(v.z, kBf16OnePair, dot2(v.w, kBf16OnePair, 0.0f))));
+                sx += dpp_f32<0xB1>(sx);
+                sx += dpp_f32<0x4E>(sx);
+                if (G >= 64)
+                    sx += dpp_f32<0x141>(sx);
+                if (G >= 128)
+                    sx += dpp_f32<0x140>(sx);
+                const int p = lane % 16, t = 4 * I + lane / 16;
+                if (p % (G / 8) == 0)
+                    xsl[(p / (G / 8)) * kTokens + t] = sx;
+            }
         }
         gload(i + 1);  // the LDS stores above have read these registers
         __builtin_amdgcn_sched_barrier(0);
@@ -723,12 +747,23 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
                 xs[r] = 0.0f;
                 d[r] = 0.0f;
             }
+            if (XV) {  // the sums of the lane's tokens 4 h .. 4 h + 3 (and 8 + 4 h .. with NR = 8)
+#pragma unroll
+                for (int q = 0; q < NR / 4; ++q) {
+                    const float4 f = *reinterpret_cast<const float4 *>(xsl + gq * kTokens + 8 * q + 4 * h);
+                    xs[4 * q] = f.x;
+                    xs[4 * q + 1] = f.y;
+                    xs[4 * q + 2] = f.z;
+                    xs[4 * q + 3] = f.w;
+                }
+            }
 #pragma unroll
             for (int t = gq * TPG; t < (gq + 1) * TPG; ++t) {
                 const int piece = (G == 128) ? 8 * h + t : 2 * t + h;
                 const bf16x8_t a = __builtin_bit_cast(
                     bf16x8_t, *reinterpret_cast<const uint4 *>(xl + ti * 256 + 16 * (piece ^ (ti & 15))));
-                xs = mfma_bf16_32(a, ones, xs);
+                if (!XV)
+                    xs = mfma_bf16_32(a, ones, xs);
                 const uint4 wq = b[t / 4];
                 const uint32_t wd = (t % 4 == 0) ? wq.x : (t % 4 == 1) ? wq.y : (t % 4 == 2) ? wq.z : wq.w;
                 const bf16x8_t bw = as_bf16x8(pair_bits(wd, mask, magic), pair_bits(wd >> 4, mask, magic),
@@ -743,7 +778,7 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
             const float off = SYM ? 8.0f : (float)((md.z >> (8 * mi)) & 0xFFu);
             const float cf = -(128.0f + off);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < NR; ++r)
                 acc[r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[r], d[r]), acc[r]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -771,12 +806,12 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
         __syncthreads();
         if (wv >= half && wv < 2 * half)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < NR; ++r)
                 red[((wv - half) * 16 + r) * kWave + lane] = acc[r];
         __syncthreads();
         if (wv < half)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < NR; ++r)
                 acc[r] += red[(wv * 16 + r) * kWave + lane];
     }
     if (wv > 0)
@@ -785,7 +820,7 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
     if (n >= N)
         return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < NR; ++r) {
         const int64_t m = 8 * (r / 4) + 4 * h + r % 4;
         if (m < M) {
             if (OUT_BF16)
@@ -862,15 +897,16 @@ hipError_t mfma_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y
 }
 
 // Staged matrix-core launch (M <= 4 XI tokens at x, output rows at y): 32 rows per block, waves split K
-// until the grid holds about 2048 waves (wide layers keep 4 waves per block, narrow ones up to 8), at least
-// two 128-code steps each.
+// until the grid holds about 2048 waves (wide layers keep 4 waves per block, narrow ones up to 8; with 32
+// tokens at least 4, which keeps more 128-code steps in flight per row block), at least two 128-code
+// steps each.
 template <int XI, int G, bool SYM>
 hipError_t lds_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
 {
     const int64_t blocks = (a.N + 31) / 32;
     const int64_t steps = a.K / 128;
     int S = 1;
-    while (2 * S <= kStageMaxWaves && blocks * S < 2048 && steps / (2 * S) >= 2)
+    while (2 * S <= kStageMaxWaves && (blocks * S < 2048 || (XI == 8 && S < 4)) && steps / (2 * S) >= 2)
         S *= 2;
     const dim3 grid((unsigned)blocks), block(kWave * S);
     if (a.y_bf16)
