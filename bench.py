@@ -74,7 +74,41 @@ def parse_args():
                     help="target CPU time per oracle function and thread count")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--m8-paths", action="store_true",
+                    help="only time the 70B gate projection at M = 8 on the matrix-core kernel (one launch) and on "
+                         "the vector kernel (two launches of 4 tokens), for counter runs; prints one JSON line")
     return ap.parse_args()
+
+
+def m8_paths(pqg, W, dev, bf16, reps=10):
+    """The 70B gate projection (28672 x 8192, symmetric INT4, g = 128) at M = 8: the matrix-core kernel the
+    library takes for 5 <= M <= 64, against the vector (decode) kernel run as two launches of 4 tokens (it
+    takes at most 4 per launch), over four weight copies taken in turn (each streamed from HBM)."""
+    import numpy as np
+    import torch
+
+    i = [p[0] for p in W.L70B_PROJ].index("gate")
+    w = bf16(W.l70b_weight(i))
+    x = bf16(W.l70b_x(i, 8))
+    copies = [pqg.quantize(w, 4, True, pqg.GROUP, 128) for _ in range(4)]  # 500 MB: past the 256 MB cache
+    del w
+    y = torch.empty((8, copies[0][0].shape[0]), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {"projection": "gate 28672x8192 sym g128", "M": 8}
+    for name, fn in (("matrix_one_launch", lambda c: pqg.qlinear_w4a16(x, c[0], c[1], None, 128, True, out=y)),
+                     ("vector_two_launches", lambda c: (pqg.qlinear_w4a16(x[:4], c[0], c[1], None, 128, True, out=y[:4]),
+                                                        pqg.qlinear_w4a16(x[4:], c[0], c[1], None, 128, True, out=y[4:])))):
+        ts = []
+        for r in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(copies[r % 4])
+            e1.record(stream)
+            e1.synchronize()
+            if r >= 2:
+                ts.append(e0.elapsed_time(e1))
+        out[name + "_us"] = round(float(np.median(ts)) * 1e3, 2)
+    return out
 
 
 def source_hash(path):
@@ -117,6 +151,10 @@ def main():
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.m8_paths:
+        print(json.dumps(m8_paths(pqg, W, dev, bf16)), flush=True)
+        return
 
     t_setup = time.time()
     # ---------------------------------------------------------------- inputs (resident in HBM)
