@@ -78,10 +78,11 @@ __device__ __forceinline__ void load8<float>(const float *__restrict__ p, float 
 
 // ------------------------------------------------------------------ exact rounding of a quotient
 
-// round-half-to-even of the correctly rounded fp32 quotient v / s, given r = 1/s (correctly rounded).
+// round-half-to-even of the correctly rounded fp32 quotient v / s, given r within one ulp of 1/s (the
+// hardware reciprocal, or the correctly rounded one).
 //
-// Fast path: t = v * r differs from fl(v / s) by at most |v/s| * (3 * 2^-24) (one rounding in r, one in
-// the product, one in the reference quotient). If t is farther than |t| * 2^-20 from the nearest
+// Fast path: t = v * r differs from fl(v / s) by at most |v/s| * 2^-22 * (1 + 2^-23) (an ulp in r, one
+// rounding in the product, one in the reference quotient). If t is farther than |t| * 2^-20 from the nearest
 // half-integer, fl(v / s) lies strictly inside the same rounding interval as t and both round to the same
 // integer. t - rint(t) and 0.5 - |.| are exact in that regime (Sterbenz), so the test itself is exact.
 // Otherwise (a near-tie, or a non-finite t when s is subnormal) the correctly rounded division decides.
@@ -94,6 +95,39 @@ __device__ __forceinline__ float rne_quotient(float v, float s, float r)
         q = __builtin_rintf(v / s);
     return q;
 }
+
+// The margin test of rne_quotient as one fused operation: 0.5 - |t - q| is exact, so
+// fma(-|t|, 2^-20, 0.5 - |t - q|) is the exact difference rounded once, whose sign is the sign of the exact
+// difference (a nonzero difference of fp32 values is at least the smallest subnormal). True when t = v * r
+// is safely away from a half-integer.
+__device__ __forceinline__ bool rne_margin_ok(float t, float q)
+{
+    return __builtin_fmaf(-__builtin_fabsf(t), 0x1p-20f, 0.5f - __builtin_fabsf(t - q)) > 0.0f;
+}
+
+// rne_quotient for 8 values sharing s and r: the reciprocal products for all 8, and one branch, uniform over
+// the wave and rarely taken, in which the lanes redo their near-ties with the correctly rounded division.
+__device__ __forceinline__ void rne_quotient8(const float v[8], float s, float r, float q[8])
+{
+    uint64_t near = 0;  // lanes with a near-tie (ballots are lane masks in scalar registers)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float t = v[i] * r;
+        q[i] = __builtin_rintf(t);
+        near |= __builtin_amdgcn_ballot_w64(!rne_margin_ok(t, q[i]));
+    }
+    if (near) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (!rne_margin_ok(v[i] * r, q[i]))
+                q[i] = __builtin_rintf(v[i] / s);
+    }
+}
+
+// 1/s to within one ulp (v_rcp_f32) for the reciprocal products above. Only for scales below 2^126 (then 1/s
+// is a normal number) or infinite ones (r = 0, and v * 0 rounds as v / inf does); a subnormal s gives an
+// infinite or inexact r whose products fail the margin test and take the division.
+__device__ __forceinline__ float recip_scale(float s) { return __builtin_amdgcn_rcpf(s); }
 
 // ------------------------------------------------------------------ segment parameters
 
@@ -133,7 +167,7 @@ __device__ __forceinline__ SegParams seg_params(float absmax, float lo, float hi
             p.z = __builtin_fminf(__builtin_fmaxf(z, 0.0f), (float)qm);
         }
     }
-    p.r = 1.0f / p.s;
+    p.r = recip_scale(p.s);  // s < 2^126 here: at most FLT_MAX / 7 (symmetric), (2 FLT_MAX) / 15 or infinite
     return p;
 }
 
@@ -146,6 +180,45 @@ __device__ __forceinline__ int code_of(float v, const SegParams &p)
 }
 
 // ------------------------------------------------------------------ wave reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Max / min over aligned groups of WIDTH <= 16 lanes, every lane of a group receiving the result: a DPP
+// butterfly inside the 16-lane rows (neighbours, pairs, mirrored half rows, mirrored rows), no LDS. Every lane
+// of a group must be active.
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v)
+{
+    static_assert(WIDTH >= 1 && WIDTH <= 16 && (WIDTH & (WIDTH - 1)) == 0, "groups inside one DPP row");
+    if (WIDTH >= 2)
+        v = __builtin_fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+    if (WIDTH >= 4)
+        v = __builtin_fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+    if (WIDTH >= 8)
+        v = __builtin_fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+    if (WIDTH >= 16)
+        v = __builtin_fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+    return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_min(float v)
+{
+    static_assert(WIDTH >= 1 && WIDTH <= 16 && (WIDTH & (WIDTH - 1)) == 0, "groups inside one DPP row");
+    if (WIDTH >= 2)
+        v = __builtin_fminf(v, dpp_f32<0xB1>(v));
+    if (WIDTH >= 4)
+        v = __builtin_fminf(v, dpp_f32<0x4E>(v));
+    if (WIDTH >= 8)
+        v = __builtin_fminf(v, dpp_f32<0x141>(v));
+    if (WIDTH >= 16)
+        v = __builtin_fminf(v, dpp_f32<0x140>(v));
+    return v;
+}
 
 template <int WIDTH>
 __device__ __forceinline__ float wave_max(float v)
@@ -173,12 +246,6 @@ __device__ __forceinline__ float wave_sum(float v)
     for (int off = 32; off > 0; off >>= 1)
         v += __shfl_xor(v, off, kWave);
     return v;
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over a full wave, returned as a wave-uniform value. Within each 16-lane row the sum is a
