@@ -43,6 +43,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// The same with one v_cvt_pk_bf16_f32 (round to nearest even; identical to pack_bf16x2 on finite values,
+// subnormals included, and on infinities).
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{lo, hi}, bf16x2v_t));
+}
+
 // Load 8 consecutive elements (bf16 or fp32) as fp32. `p` must be 16-byte aligned.
 template <typename XT>
 __device__ __forceinline__ void load8(const XT *__restrict__ p, float v[8]);

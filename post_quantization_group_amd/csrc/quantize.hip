@@ -352,39 +352,45 @@ __global__ __launch_bounds__(256) void k_quant_static(const XT *__restrict__ x, 
 template <int BITS, bool SYM, int GRAN, bool OUT_BF16>
 __global__ __launch_bounds__(256) void k_dequant(const void *__restrict__ codes, const float *__restrict__ scales,
                                                  const uint8_t *__restrict__ zeros, int64_t n_chunks,
-                                                 int64_t cols, int group_size, void *__restrict__ out)
+                                                 int64_t cols, int group_size, int seg_shift,
+                                                 void *__restrict__ out)
 {
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= n_chunks)
         return;
     const int64_t e = c * 8;
-    const int64_t seg = (GRAN == QG_TENSOR) ? 0 : (GRAN == QG_ROW) ? e / cols : e / group_size;
+    // the segment: a shift when its length (row or group) is a power of two (seg_shift >= 0, uniform)
+    const int64_t len = (GRAN == QG_ROW) ? cols : (int64_t)group_size;
+    const int64_t seg = (GRAN == QG_TENSOR) ? 0 : seg_shift >= 0 ? e >> seg_shift : e / len;
     const float s = scales[seg];
-    const int z = SYM ? 0 : (int)zeros[seg];
-    int q[8];
+    // codes as offset-binary bytes (symmetric two's-complement fields xor their top bit), converted to float
+    // by the byte conversions; q - z = u - (bias + z), exact in fp32
+    const float zb = (SYM ? (float)(1 << (BITS - 1)) : 0.0f) + (SYM ? 0.0f : (float)zeros[seg]);
+    float u[8];
     if (BITS == 4) {
-        const uint32_t w = reinterpret_cast<const uint32_t *>(codes)[c];
+        const uint32_t w = reinterpret_cast<const uint32_t *>(codes)[c] ^ (SYM ? 0x88888888u : 0u);
+        const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;  // codes 0, 2, 4, 6 and 1, 3, 5, 7
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int nib = (int)((w >> (4 * i)) & 0xFu);
-            q[i] = (SYM && nib >= 8) ? nib - 16 : nib;
+        for (int j = 0; j < 4; ++j) {
+            u[2 * j] = (float)((ev >> (8 * j)) & 0xFFu);
+            u[2 * j + 1] = (float)((od >> (8 * j)) & 0xFFu);
         }
     } else {
         const uint2 w = reinterpret_cast<const uint2 *>(codes)[c];
+        const uint32_t w0 = w.x ^ (SYM ? 0x80808080u : 0u), w1 = w.y ^ (SYM ? 0x80808080u : 0u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int b0 = (int)((w.x >> (8 * i)) & 0xFFu), b1 = (int)((w.y >> (8 * i)) & 0xFFu);
-            q[i] = (SYM && b0 >= 128) ? b0 - 256 : b0;
-            q[i + 4] = (SYM && b1 >= 128) ? b1 - 256 : b1;
+        for (int j = 0; j < 4; ++j) {
+            u[j] = (float)((w0 >> (8 * j)) & 0xFFu);
+            u[j + 4] = (float)((w1 >> (8 * j)) & 0xFFu);
         }
     }
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        v[i] = s * (float)(q[i] - z);
+        v[i] = s * (u[i] - zb);
     if (OUT_BF16) {
-        uint4 o = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                             pack_bf16x2(v[6], v[7]));
+        uint4 o = make_uint4(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]), pack_bf16x2_rne(v[4], v[5]),
+                             pack_bf16x2_rne(v[6], v[7]));
         reinterpret_cast<uint4 *>(out)[c] = o;
     } else {
         float4 *o = reinterpret_cast<float4 *>(out) + 2 * c;
@@ -494,17 +500,29 @@ hipError_t quant_dispatch_type(const QuantArgs &a, hipStream_t st)
     return a.symmetric ? quant_dispatch_smooth<XT, 8, true>(a, st) : quant_dispatch_smooth<XT, 8, false>(a, st);
 }
 
+// log2(n) when n is a power of two, else -1
+inline int pow2_shift(int64_t n)
+{
+    if (n <= 0 || (n & (n - 1)) != 0)
+        return -1;
+    int k = 0;
+    while ((int64_t(1) << k) < n)
+        ++k;
+    return k;
+}
+
 template <int BITS, bool SYM, int GRAN>
 hipError_t dequant_out(const DequantArgs &a, hipStream_t st)
 {
     const int64_t n_chunks = a.rows * a.cols / 8;
     const unsigned nb = nblocks(n_chunks, 256);
+    const int shift = pow2_shift(GRAN == QG_ROW ? a.cols : (int64_t)a.group_size);
     if (a.out_bf16)
         k_dequant<BITS, SYM, GRAN, true><<<nb, 256, 0, st>>>(a.codes, a.scales, a.zeros, n_chunks, a.cols,
-                                                             a.group_size, a.out);
+                                                             a.group_size, shift, a.out);
     else
         k_dequant<BITS, SYM, GRAN, false><<<nb, 256, 0, st>>>(a.codes, a.scales, a.zeros, n_chunks, a.cols,
-                                                              a.group_size, a.out);
+                                                              a.group_size, shift, a.out);
     return hipGetLastError();
 }
 
