@@ -38,13 +38,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
-
-// The same with one v_cvt_pk_bf16_f32 (round to nearest even; identical to pack_bf16x2 on finite values,
-// subnormals included, and on infinities).
+// Two fp32 values as a packed bf16 pair (low half first) with one v_cvt_pk_bf16_f32: round to nearest even,
+// the same bits as f32_to_bf16_bits on finite values (subnormals included) and on infinities.
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x2v_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi)

@@ -77,7 +77,7 @@ __device__ __forceinline__ void store4s(const int v[4], int64_t m, int64_t nb, i
     if (MODE == 1) {
         uint16_t *out = static_cast<uint16_t *>(c) + m * N + nb;
         if (vec_ok && nb + 3 < N) {
-            *reinterpret_cast<uint2 *>(out) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+            *reinterpret_cast<uint2 *>(out) = make_uint2(pack_bf16x2_rne(f[0], f[1]), pack_bf16x2_rne(f[2], f[3]));
         } else {
             for (int r = 0; r < 4; ++r)
                 if (nb + r < N)
@@ -239,7 +239,7 @@ __global__ __launch_bounds__((BN / WN) * (BM / WM) * 64) void k_gemm_i8(
                     }
                     const int chunk = (nl * 2 / 16) ^ (ml & 15);
                     *reinterpret_cast<uint2 *>(smem + ml * ROWB + chunk * 16 + (nl * 2) % 16) =
-                        make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+                        make_uint2(pack_bf16x2_rne(f[0], f[1]), pack_bf16x2_rne(f[2], f[3]));
                 }
         }
         __syncthreads();
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kRingThreads, 2) void k_gemm_i8_ring(const int8_t *
                     }
                     const int chunk = (nl * 2 / 16) ^ (ml & 15);
                     *reinterpret_cast<uint2 *>(rp + chunk * 16 + (nl * 2) % 16) =
-                        make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+                        make_uint2(pack_bf16x2_rne(f[0], f[1]), pack_bf16x2_rne(f[2], f[3]));
                 }
         }
         __syncthreads();

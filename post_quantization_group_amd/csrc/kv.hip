@@ -214,8 +214,8 @@ __global__ __launch_bounds__(256) void k_kv_dequant_keys(const void *__restrict_
         }
         if (OUT_BF16)
             *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + e) =
-                make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                           pack_bf16x2(v[6], v[7]));
+                make_uint4(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]), pack_bf16x2_rne(v[4], v[5]),
+                           pack_bf16x2_rne(v[6], v[7]));
         else {
             float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(out) + e);
             o[0] = make_float4(v[0], v[1], v[2], v[3]);

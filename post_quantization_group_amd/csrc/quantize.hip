@@ -420,8 +420,8 @@ __global__ __launch_bounds__(256) void k_dequant16(const uint8_t *__restrict__ c
         v[i] = s * (float)(q - z);
     }
     if (OUT_BF16) {
-        reinterpret_cast<uint4 *>(out)[c] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+        reinterpret_cast<uint4 *>(out)[c] = make_uint4(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]),
+                                                       pack_bf16x2_rne(v[4], v[5]), pack_bf16x2_rne(v[6], v[7]));
     } else {
         float4 *o = reinterpret_cast<float4 *>(out) + 2 * c;
         o[0] = make_float4(v[0], v[1], v[2], v[3]);

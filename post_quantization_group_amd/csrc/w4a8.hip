@@ -324,8 +324,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_w4a8(const int8_t *__restrict__
         if (vec_ok) {  // N % 8 == 0: a chunk never crosses N
             if (OUT_BF16)
                 *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(y) + m * N + nb) =
-                    make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                               pack_bf16x2(v[6], v[7]));
+                    make_uint4(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]), pack_bf16x2_rne(v[4], v[5]),
+                               pack_bf16x2_rne(v[6], v[7]));
             else {
                 float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(y) + m * N + nb);
                 o[0] = make_float4(v[0], v[1], v[2], v[3]);
