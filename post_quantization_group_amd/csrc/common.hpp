@@ -252,6 +252,28 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// Max / min over a full wave, returned as a wave-uniform value: the DPP butterfly of group_max / group_min
+// inside each 16-lane row, then the four row results read out. Every lane must be active.
+__device__ __forceinline__ float wave_max_uniform(float v)
+{
+    v = group_max<16>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return __builtin_fmaxf(__builtin_fmaxf(r0, r1), __builtin_fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ float wave_min_uniform(float v)
+{
+    v = group_min<16>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return __builtin_fminf(__builtin_fminf(r0, r1), __builtin_fminf(r2, r3));
+}
+
 // Sum over a full wave, returned as a wave-uniform value. Within each 16-lane row the sum is a
 // butterfly of DPP moves (swap neighbours, swap pairs, mirror halves, mirror the row), so every lane of
 // the row holds its row total; the four row totals are then read out and added in a fixed order.

@@ -192,10 +192,10 @@ __device__ __forceinline__ void block_range(float &absmax, float &lo, float &hi,
     constexpr int NW = NT / kWave;
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
     if (SYM) {
-        absmax = wave_max<kWave>(absmax);
+        absmax = wave_max_uniform(absmax);
     } else {
-        lo = wave_min<kWave>(lo);
-        hi = wave_max<kWave>(hi);
+        lo = wave_min_uniform(lo);
+        hi = wave_max_uniform(hi);
     }
     if (lane == 0) {
         red[wv] = absmax;
@@ -457,7 +457,8 @@ hipError_t quant_dispatch_gran(const QuantArgs &a, hipStream_t st)
             break;
         }
     } else if (a.granularity == QG_ROW) {
-        // threads per row: enough that each keeps at most kRowCache chunks in registers
+        // threads per row: enough that each keeps at most kRowCache chunks in registers (four waves per row for
+        // a 2048 x 4096 batch of tokens measured no faster than one)
         const int64_t nch = a.cols / 8;
         const unsigned grid = (unsigned)a.rows;
         if (nch <= 256 * kRowCache / 4)  // short rows: 64 threads
