@@ -80,6 +80,47 @@ def parse_args():
     return ap.parse_args()
 
 
+def device_record(dev):
+    """The properties the runtime reports for the GPU the bench ran on."""
+    import torch
+
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+            "total_memory_gib": round(p.total_memory / 2 ** 30, 1), "l2_cache_bytes": p.L2_cache_size,
+            "warp_size": p.warp_size}
+
+
+def stream_reference(pqg, dev, reps=6):
+    """Measured streaming rates on this GPU, to set the kernels' rates beside: one streaming read of 1 GiB
+    (pqg_stream_read_probe: 16-byte non-temporal loads, four in flight per lane) and a device copy of 1 GiB
+    (torch's copy, reads + writes), event-timed, medians over `reps` after one warm-up; both buffers are far
+    larger than the 256 MB last-level cache."""
+    import numpy as np
+    import torch
+
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, fn, nbytes in (("read_gbs", lambda: pqg.stream_read_probe(src, sink), 4 * n),
+                             ("copy_gbs", lambda: dst.copy_(src), 8 * n)):
+        ts = []
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1))
+        out[name] = round(nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def m8_paths(pqg, W, dev, bf16, reps=10):
     """The 70B gate projection (28672 x 8192, symmetric INT4, g = 128) at M = 8: the matrix-core kernel the
     library takes for 5 <= M <= 64, against the vector (decode) kernel run as two launches of 4 tokens (it
@@ -226,6 +267,8 @@ def main():
     gemv_bytes = sum(p["n"] * p["k"] // 2 + p["n"] * (p["k"] // 128) * 4 for p in projs)
     gemv_bytes16 = sum(p["n"] * p["k"] // 2 + p["n"] * (p["k"] // 128) * 2 for p in projs)
     gemv_bytes_total = gemv_bytes + sum(p["k"] * 2 + p["n"] * 2 for p in projs)  # + x and y
+    # bytes the quantize stage moves (bf16 weights in, packed codes + scales out) and the dequantize the reverse
+    quant_bytes = sum(p["n"] * p["k"] * 2 for p in projs) + gemv_bytes
     w8a8_ops = 2.0 * M8 * N8 * K8
 
     parts = ["quantize", "dequantize", "smooth", "wquant", "w8a8_actquant", "w8a8_gemm", "w8a8_static_actquant",
@@ -449,6 +492,10 @@ def main():
         },
         "per_projection_event_us": {p["name"]: round(float(t) * 1e3, 2) for p, t in zip(projs, launch_ms)},
         "stage_ms": {k: round(v, 4) for k, v in part_ms.items()},
+        # the 70B layer's quantize (bf16 in, packed INT4 + scales out) and dequantize (the reverse): bytes moved
+        # per second, against 8 TB/s
+        "layer_quantize_gbs": round(quant_bytes / (part_ms["quantize"] * 1e-3) / 1e9, 1),
+        "layer_dequantize_gbs": round(quant_bytes / (part_ms["dequantize"] * 1e-3) / 1e9, 1),
         # the batched passes over the same weight stream (packed codes + scales), as weight GB/s: over the
         # concatenated layout (four launches), and over the seven projections (steps of mode 4)
         "w4a16_batched_weight_gbs": {m: round(gemv_bytes / (part_ms["w4a16_m%d" % m] * 1e-3) / 1e9, 1)
@@ -482,6 +529,13 @@ def main():
                                   "ms": round(med(fused_seq_ms), 4)},
         "setup_s": round(setup_s, 1),
     }
+    out["device"] = device_record(dev)
+    ref = stream_reference(pqg, dev)
+    out["stream_reference"] = dict(ref, decode_frac_of_read=round(value / ref["read_gbs"], 4),
+                                   quantize_frac_of_copy=round((quant_bytes / (part_ms["quantize"] * 1e-3) / 1e9)
+                                                               / ref["copy_gbs"], 4),
+                                   dequantize_frac_of_copy=round((quant_bytes / (part_ms["dequantize"] * 1e-3) / 1e9)
+                                                                 / ref["copy_gbs"], 4))
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

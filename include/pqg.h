@@ -372,6 +372,16 @@ int32_t pqg_qlinear_w4a16_meta16(const void *x, int64_t M, int64_t N, int64_t K,
 int32_t pqg_qlinear_w8a8_noalloc(const void *x, const float *smooth, const int8_t *w_q, const float *w_scales,
                                  int64_t M, int64_t N, int64_t K, void *y, int32_t y_dtype, void *stream);
 
+/*
+ * A measurement utility, no step of the method: reads a device buffer once, as a streaming read (16-byte
+ * non-temporal loads, two in flight per lane, a large grid of short-lived blocks), so that the device's
+ * achievable read rate can be measured and the kernels' rates set beside it.
+ *   src   : device memory, 16-byte aligned; bytes: a multiple of 16 (0 enqueues nothing).
+ *   sink  : device memory for one uint32; the call may write an arbitrary word there.
+ * Returns PQG_EINVAL for a NULL or misaligned src (with bytes > 0), a NULL sink, or bytes not a multiple of 16.
+ */
+int32_t pqg_stream_read_probe(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ EXPORTS = [
     "pqg_smooth_workspace_bytes", "pqg_smooth", "pqg_qlinear_w4a16", "pqg_qlinear_w8a8", "pqg_gemm_s8s8s32",
     "pqg_qlinear_w4a8", "pqg_kv_quantize_keys", "pqg_kv_dequantize_keys", "pqg_kv_append",
     "pqg_quantize_meta16", "pqg_dequantize_meta16", "pqg_qlinear_w4a16_meta16", "pqg_qlinear_w8a8_noalloc",
-    "pqg_qlinear_w4a16_grouped",
+    "pqg_qlinear_w4a16_grouped", "pqg_stream_read_probe",
 ]
 
 _lib = None
@@ -100,6 +100,8 @@ def load(path: str = LIB_PATH):
     lib.pqg_qlinear_w4a16_grouped.argtypes = [ctypes.POINTER(W4A16Problem), I32, I64, I32, I32, I32, P]
     lib.pqg_qlinear_w8a8_noalloc.restype = I32
     lib.pqg_qlinear_w8a8_noalloc.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
+    lib.pqg_stream_read_probe.restype = I32
+    lib.pqg_stream_read_probe.argtypes = [P, I64, P, P]
     if lib.pqg_abi_version() != ABI_VERSION:
         raise ImportError("libpqg.so ABI %d != binding ABI %d" % (lib.pqg_abi_version(), ABI_VERSION))
     _lib = lib
@@ -451,3 +453,16 @@ def qlinear_w4a16_meta16(x: torch.Tensor, w_packed: torch.Tensor, scales16: torc
     _check(lib.pqg_qlinear_w4a16_meta16(_ptr(x), M, N, K, _ptr(w_packed), _ptr(scales16), _ptr(zeros4), group_size,
                                         int(symmetric), _ptr(y), _float_dtype(y), _stream(dev)))
     return y
+
+
+def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor = None) -> torch.Tensor:
+    """pqg_stream_read_probe: one streaming read of `buf` (a contiguous device tensor whose byte size is a
+    multiple of 16), for measuring the device's read rate. Returns the 1-element int32 sink (its value is
+    meaningless)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    dev = _dev(buf)
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(load().pqg_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(dev)))
+    return sink

@@ -663,4 +663,18 @@ int32_t pqg_qlinear_w8a8_noalloc(const void *x, const float *smooth, const int8_
     return run_w8a8(x, smooth, w_q, w_scales, M, N, K, y, y_dtype, x_q, x_scales, as_stream(stream));
 }
 
+int32_t pqg_stream_read_probe(const void *src, int64_t bytes, uint32_t *sink, void *stream)
+{
+    g_err[0] = 0;
+    if (bytes < 0 || bytes % 16 != 0)
+        return fail(PQG_EINVAL, "bytes must be a non-negative multiple of 16 (got %lld)", (long long)bytes);
+    if (!sink)
+        return fail(PQG_EINVAL, "sink is required");
+    if (bytes == 0)
+        return PQG_OK;
+    if (!src || !aligned(src, 16))
+        return fail(PQG_EINVAL, "src must be a 16-byte aligned device pointer");
+    return hip_status(pqg::launch_stream_read(src, bytes, sink, as_stream(stream)), "stream read probe");
+}
+
 }  // extern "C"

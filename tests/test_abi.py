@@ -278,3 +278,14 @@ def test_w4a16_grouped_rejects(lib):
         assert needle in lib.pqg_last_error().decode(), (kw, lib.pqg_last_error())
     assert call(M=0) == pqg.OK
     assert call(p0_N=0, p1_N=0) == pqg.OK
+
+
+def test_stream_read_probe_rejects_bad_arguments(lib):
+    """The measurement probe validates on the host: bytes a non-negative multiple of 16, a sink, an aligned src."""
+    misaligned = ctypes.c_void_p(FAKE.value + 4)
+    assert lib.pqg_stream_read_probe(FAKE, 24, FAKE, None) == pqg.EINVAL
+    assert lib.pqg_stream_read_probe(FAKE, -16, FAKE, None) == pqg.EINVAL
+    assert lib.pqg_stream_read_probe(FAKE, 64, None, None) == pqg.EINVAL
+    assert lib.pqg_stream_read_probe(None, 64, FAKE, None) == pqg.EINVAL
+    assert lib.pqg_stream_read_probe(misaligned, 64, FAKE, None) == pqg.EINVAL
+    assert lib.pqg_stream_read_probe(None, 0, FAKE, None) == pqg.OK

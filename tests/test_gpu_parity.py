@@ -794,3 +794,14 @@ def test_reruns_are_bit_identical(gpu_lib):
         outs.append((codes.cpu().numpy(), bf16_tensor_bits(y)))
     for o in outs[1:]:
         assert np.array_equal(o[0], outs[0][0]) and np.array_equal(o[1], outs[0][1])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nbytes", [16, 1 << 20, (1 << 20) + 48])
+def test_stream_read_probe_runs(gpu_lib, nbytes):
+    """The measurement probe reads any multiple of 16 bytes (grid-stride tail included) and returns cleanly."""
+    announce("stream read probe %d B" % nbytes)
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = gpu_lib.stream_read_probe(buf)
+    torch.cuda.synchronize()
+    assert sink.shape == (1,)
