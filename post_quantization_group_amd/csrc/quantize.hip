@@ -15,14 +15,16 @@ namespace pqg {
 
 // ------------------------------------------------------------------ shared per-chunk pieces
 
+// 8 consecutive elements starting at element `elem`, whose first column is `col`, with the smoothing factor of
+// each column applied (divided or multiplied) when SMOOTH asks for it.
 template <typename XT, int SMOOTH>
 __device__ __forceinline__ void load_smoothed8(const XT *__restrict__ x, const float *__restrict__ smooth,
-                                               int64_t elem, int64_t cols, float v[8])
+                                               int64_t elem, int64_t col, float v[8])
 {
     load8<XT>(x + elem, v);
     if (SMOOTH != SMOOTH_NONE) {
         float sv[8];
-        load8<float>(smooth + (elem % cols), sv);
+        load8<float>(smooth + col, sv);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             v[i] = (SMOOTH == SMOOTH_DIV) ? v[i] / sv[i] : v[i] * sv[i];
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void k_quant_group(const XT *__restrict__ x, c
     if (c >= n_chunks)
         return;
     float v[8];
-    load_smoothed8<XT, SMOOTH>(x, smooth, c * 8, cols, v);
+    load_smoothed8<XT, SMOOTH>(x, smooth, c * 8, SMOOTH != SMOOTH_NONE ? (c * 8) % cols : 0, v);
     float absmax = 0.0f, lo = v[0], hi = v[0];
     range8<SYM>(v, absmax, lo, hi);
     if (SYM) {
@@ -225,24 +227,63 @@ __global__ __launch_bounds__(NT) void k_quant_row(const XT *__restrict__ x, cons
     const int64_t nch = cols / 8;
     const int64_t base = row * cols;
     float v[kRowCache][8];
-    float absmax = 0.0f, lo = 0.0f, hi = 0.0f;
-    bool first = true;
+    // Loads first, all in flight together: the iteration count is uniform, and a lane past the row's end in the
+    // last iteration re-reads the row's last chunk (no load sits under a divergent branch, which would make
+    // the compiler wait for every outstanding load at the branch's join). Then the range, over own chunks only.
+    // The raw loads of every chunk go out in one loop, and the arithmetic follows in another, so that no
+    // chunk's smoothing waits for its data before the next chunk's loads are issued.
+    const int iters = (int)((nch + NT - 1) / NT);
+    constexpr int XW = sizeof(XT) * 8 / 16;  // 16-byte words per chunk of x: 1 (bf16) or 2 (fp32)
+    uint4 xr[kRowCache][XW];
+    float4 sr[kRowCache][SMOOTH != SMOOTH_NONE ? 2 : 1];
 #pragma unroll
-    for (int i = 0; i < kRowCache; ++i) {
-        const int64_t ch = threadIdx.x + (int64_t)i * NT;
-        if (ch < nch) {
-            load_smoothed8<XT, SMOOTH>(x, smooth, base + ch * 8, cols, v[i]);
-            if (first) {
-                lo = hi = v[i][0];
-                first = false;
+    for (int i = 0; i < kRowCache; ++i)
+        if (i < iters) {
+            const int64_t ch = std::min<int64_t>(threadIdx.x + (int64_t)i * NT, nch - 1);
+            const uint4 *xp = reinterpret_cast<const uint4 *>(x + base + ch * 8);
+#pragma unroll
+            for (int q = 0; q < XW; ++q)
+                xr[i][q] = xp[q];
+            if (SMOOTH != SMOOTH_NONE) {
+                sr[i][0] = reinterpret_cast<const float4 *>(smooth + ch * 8)[0];
+                sr[i][SMOOTH != SMOOTH_NONE ? 1 : 0] = reinterpret_cast<const float4 *>(smooth + ch * 8)[1];
             }
-            range8<SYM>(v[i], absmax, lo, hi);
         }
-    }
-    if (first) {  // a thread without elements must not disturb the reduction
-        lo = __builtin_huge_valf();
-        hi = -__builtin_huge_valf();
-    }
+#pragma unroll
+    for (int i = 0; i < kRowCache; ++i)
+        if (i < iters) {
+            if (XW == 1) {
+                v[i][0] = bf16_lo(xr[i][0].x);
+                v[i][1] = bf16_hi(xr[i][0].x);
+                v[i][2] = bf16_lo(xr[i][0].y);
+                v[i][3] = bf16_hi(xr[i][0].y);
+                v[i][4] = bf16_lo(xr[i][0].z);
+                v[i][5] = bf16_hi(xr[i][0].z);
+                v[i][6] = bf16_lo(xr[i][0].w);
+                v[i][7] = bf16_hi(xr[i][0].w);
+            } else {
+#pragma unroll
+                for (int q = 0; q < XW; ++q) {
+                    v[i][4 * q + 0] = __uint_as_float(xr[i][q].x);
+                    v[i][4 * q + 1] = __uint_as_float(xr[i][q].y);
+                    v[i][4 * q + 2] = __uint_as_float(xr[i][q].z);
+                    v[i][4 * q + 3] = __uint_as_float(xr[i][q].w);
+                }
+            }
+            if (SMOOTH != SMOOTH_NONE) {
+                const float4 a0 = sr[i][0], a1 = sr[i][SMOOTH != SMOOTH_NONE ? 1 : 0];
+                const float sv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[i][e] = (SMOOTH == SMOOTH_DIV) ? v[i][e] / sv[e] : v[i][e] * sv[e];
+            }
+        }
+    // a thread without elements must not disturb the reduction: lo = +inf, hi = -inf until its first chunk
+    float absmax = 0.0f, lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+#pragma unroll
+    for (int i = 0; i < kRowCache; ++i)
+        if (i < iters && threadIdx.x + (int64_t)i * NT < nch)
+            range8<SYM>(v[i], absmax, lo, hi);
     block_range<BITS, SYM, NT>(absmax, lo, hi, red);
     const SegParams p = seg_params<BITS, SYM>(absmax, lo, hi);
 #pragma unroll
@@ -271,7 +312,7 @@ __global__ __launch_bounds__(256) void k_tensor_range(const XT *__restrict__ x, 
     float absmax = 0.0f, lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
     for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n_chunks; c += (int64_t)gridDim.x * 256) {
         float v[8];
-        load_smoothed8<XT, SMOOTH>(x, smooth, c * 8, cols, v);
+        load_smoothed8<XT, SMOOTH>(x, smooth, c * 8, SMOOTH != SMOOTH_NONE ? (c * 8) % cols : 0, v);
         range8<SYM>(v, absmax, lo, hi);
     }
     block_range<8, SYM, 256>(absmax, lo, hi, red);
@@ -301,7 +342,7 @@ __global__ __launch_bounds__(256) void k_tensor_quant(const XT *__restrict__ x, 
     const SegParams p = seg_params<BITS, SYM>(absmax, lo, hi);
     for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n_chunks; c += (int64_t)gridDim.x * 256) {
         float v[8];
-        load_smoothed8<XT, SMOOTH>(x, smooth, c * 8, cols, v);
+        load_smoothed8<XT, SMOOTH>(x, smooth, c * 8, SMOOTH != SMOOTH_NONE ? (c * 8) % cols : 0, v);
         store_codes8<BITS, SYM>(v, p, codes, c * 8);
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {

@@ -286,6 +286,33 @@ def test_smooth_generic_alpha_within_ulp(gpu_lib):
     assert ulps.max() <= 1
 
 
+# Column maxima in row slices: row counts below, at and across one wave's 16 rows and one block's 64, column
+# counts of one chunk, one 512-column block and a partial second block, every input dtype pair. The largest
+# magnitudes of some columns sit in the first and the last row.
+@pytest.mark.parametrize("tnk", [(1, 3, 8), (17, 130, 520), (64, 65, 512), (200, 1000, 1032)])
+@pytest.mark.parametrize("dts", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"), ("f32", "f32")])
+def test_smooth_ragged_dtypes_bitexact(gpu_lib, tnk, dts):
+    t, n, k = tnk
+    announce("smooth ragged %s %s" % (tnk, dts))
+    g = np.random.default_rng(zlib.crc32(repr(("smooth", tnk, dts)).encode()))
+    x = g.standard_normal((t, k)).astype(np.float32)
+    w = (g.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x[-1, ::7] = -60.0
+    x[0, 3::11] = 55.0
+    w[-1, 1::5] = -0.5
+    w[0, 2::9] = 0.4
+    ins = []
+    for a, dt in ((x, dts[0]), (w, dts[1])):
+        ins.append(W.bf16_bits(a) if dt == "bf16" else a)
+    gx = to_gpu_bf16(ins[0]) if dts[0] == "bf16" else to_gpu(ins[0])
+    gw = to_gpu_bf16(ins[1]) if dts[1] == "bf16" else to_gpu(ins[1])
+    for alpha in (0.5, 1.0, 0.0):
+        s = gpu_lib.smooth(gx, gw, alpha)
+        torch.cuda.synchronize()
+        so = oracle.smooth(ins[0], ins[1], alpha)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32)), alpha
+
+
 def test_smooth_zero_channel(gpu_lib):
     d = W.w8a8(m=64, n=64, k=256)
     x = d["x"].copy()
