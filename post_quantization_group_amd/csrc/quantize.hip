@@ -217,7 +217,7 @@ __device__ __forceinline__ void block_range(float &absmax, float &lo, float &hi,
 
 // One block of NT threads per row. The smoothed values are computed once and kept in registers between
 // the range pass and the code pass.
-template <typename XT, int BITS, bool SYM, int SMOOTH, int NT>
+template <typename XT, int BITS, bool SYM, int SMOOTH, int NT, int RC = kRowCache>
 __global__ __launch_bounds__(NT) void k_quant_row(const XT *__restrict__ x, const float *__restrict__ smooth,
                                                   int64_t cols, void *__restrict__ codes,
                                                   float *__restrict__ scales, uint8_t *__restrict__ zeros)
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(NT) void k_quant_row(const XT *__restrict__ x, cons
     const int64_t row = blockIdx.x;
     const int64_t nch = cols / 8;
     const int64_t base = row * cols;
-    float v[kRowCache][8];
+    float v[RC][8];
     // Loads first, all in flight together: the iteration count is uniform, and a lane past the row's end in the
     // last iteration re-reads the row's last chunk (no load sits under a divergent branch, which would make
     // the compiler wait for every outstanding load at the branch's join). Then the range, over own chunks only.
@@ -234,10 +234,10 @@ __global__ __launch_bounds__(NT) void k_quant_row(const XT *__restrict__ x, cons
     // chunk's smoothing waits for its data before the next chunk's loads are issued.
     const int iters = (int)((nch + NT - 1) / NT);
     constexpr int XW = sizeof(XT) * 8 / 16;  // 16-byte words per chunk of x: 1 (bf16) or 2 (fp32)
-    uint4 xr[kRowCache][XW];
-    float4 sr[kRowCache][SMOOTH != SMOOTH_NONE ? 2 : 1];
+    uint4 xr[RC][XW];
+    float4 sr[RC][SMOOTH != SMOOTH_NONE ? 2 : 1];
 #pragma unroll
-    for (int i = 0; i < kRowCache; ++i)
+    for (int i = 0; i < RC; ++i)
         if (i < iters) {
             const int64_t ch = std::min<int64_t>(threadIdx.x + (int64_t)i * NT, nch - 1);
             const uint4 *xp = reinterpret_cast<const uint4 *>(x + base + ch * 8);
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(NT) void k_quant_row(const XT *__restrict__ x, cons
             }
         }
 #pragma unroll
-    for (int i = 0; i < kRowCache; ++i)
+    for (int i = 0; i < RC; ++i)
         if (i < iters) {
             if (XW == 1) {
                 v[i][0] = bf16_lo(xr[i][0].x);
@@ -281,13 +281,13 @@ __global__ __launch_bounds__(NT) void k_quant_row(const XT *__restrict__ x, cons
     // a thread without elements must not disturb the reduction: lo = +inf, hi = -inf until its first chunk
     float absmax = 0.0f, lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
 #pragma unroll
-    for (int i = 0; i < kRowCache; ++i)
+    for (int i = 0; i < RC; ++i)
         if (i < iters && threadIdx.x + (int64_t)i * NT < nch)
             range8<SYM>(v[i], absmax, lo, hi);
     block_range<BITS, SYM, NT>(absmax, lo, hi, red);
     const SegParams p = seg_params<BITS, SYM>(absmax, lo, hi);
 #pragma unroll
-    for (int i = 0; i < kRowCache; ++i) {
+    for (int i = 0; i < RC; ++i) {
         const int64_t ch = threadIdx.x + (int64_t)i * NT;
         if (ch < nch)
             store_codes8<BITS, SYM>(v[i], p, codes, base + ch * 8);
@@ -502,7 +502,10 @@ hipError_t quant_dispatch_gran(const QuantArgs &a, hipStream_t st)
         // a 2048 x 4096 batch of tokens measured no faster than one)
         const int64_t nch = a.cols / 8;
         const unsigned grid = (unsigned)a.rows;
-        if (nch <= 256 * kRowCache / 4)  // short rows: 64 threads
+        if (nch <= 64 * 2)  // short rows (at most 1024 columns): two chunks per thread, fewer registers
+            k_quant_row<XT, BITS, SYM, SMOOTH, 64, 2><<<grid, 64, 0, st>>>(x, a.smooth, a.cols, a.codes, a.scales,
+                                                                          a.zeros);
+        else if (nch <= 256 * kRowCache / 4)  // 64 threads
             k_quant_row<XT, BITS, SYM, SMOOTH, 64><<<grid, 64, 0, st>>>(x, a.smooth, a.cols, a.codes, a.scales,
                                                                        a.zeros);
         else if (nch <= 256 * kRowCache)

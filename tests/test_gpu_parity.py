@@ -87,6 +87,24 @@ def test_quantize_bitexact_small(gpu_lib, case, dtype, shape):
     assert_quant_equal(gpu, ora, bits, sym)
 
 
+# Per-row quantize at each edge of its launch shapes: 64 threads with two or eight chunks of 8 columns each
+# (up to 1024 / 4096 columns), 256 threads (up to 16384), 1024 threads beyond.
+@pytest.mark.parametrize("cols", [1024, 1056, 4096, 4128, 16384, 16416])
+@pytest.mark.parametrize("case", [(8, True, 0), (8, False, 1), (4, True, 2), (4, False, 0)])
+def test_quantize_row_launch_edges(gpu_lib, cols, case):
+    bits, sym, mode = case
+    announce("row quantize edges %s %s" % (cols, case))
+    rng = np.random.default_rng(zlib.crc32(repr(("row edges", cols, case)).encode()))
+    x32 = (rng.standard_normal((3, cols)) * np.array([[0.05], [1.0], [3.0]])).astype(np.float32)
+    x32[1, -1] = 40.0  # the row maximum in the row's last chunk
+    x32[2, 0] = -50.0  # and in its first
+    xh = W.bf16_bits(x32)
+    sm = rng.uniform(0.25, 4.0, size=cols).astype(np.float32) if mode else None
+    gpu = gpu_quant(gpu_lib, to_gpu_bf16(xh), bits, sym, 1, 0, None if sm is None else to_gpu(sm), mode)
+    ora = oracle.quantize(xh, bits, sym, 1, 0, sm, mode)
+    assert_quant_equal(gpu, ora, bits, sym)
+
+
 def test_quantize_tiny_config(gpu_lib):
     """256x512 fp32 with 0.5 % x20 outliers, symmetric INT4 g=128: codes, packed bytes and scales exact."""
     announce("tiny quantize")
