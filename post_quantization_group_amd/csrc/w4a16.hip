@@ -896,18 +896,24 @@ hipError_t mfma_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y
     return hipGetLastError();
 }
 
-// Staged matrix-core launch (M <= 4 XI tokens at x, output rows at y): 32 rows per block, waves split K
-// until the grid holds about 2048 waves (wide layers keep 4 waves per block, narrow ones up to 8; with 32
-// tokens at least 4, which keeps more 128-code steps in flight per row block), at least two 128-code
-// steps each.
+// Staged matrix-core launch (M <= 4 XI tokens at x, output rows at y): 32 rows per block, S waves per block
+// splitting K. A block of 8 waves fills a CU's register file (at 32 tokens) or most of it, so while the row
+// blocks fit the CUs once, S = 8; beyond that S = 4, so that two blocks share a CU instead of the grid running
+// a second, partial round; up to 8 tokens on layers of at least 768 row blocks S = 2 (longer K slices; the
+// block's LDS is sized for 8 waves, so four such blocks share a CU). Every wave keeps at least two 128-code
+// steps. Measured on the 70B projections
+// (g = 128): the q|k|v launch (320 blocks) 21.7 us at S = 4 against 24.8 at 8, the 28672-row gate at M = 8
+// 37.5 us at S = 2 against 43.0 at 4, the 57344-row gate|up at M = 16 80.3 us at S = 4 against 88.7 at 2.
+constexpr int64_t kRowBlocksPerRound = 256;  // one 32-row block of 8 waves per CU
+
 template <int XI, int G, bool SYM>
 hipError_t lds_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
 {
     const int64_t blocks = (a.N + 31) / 32;
     const int64_t steps = a.K / 128;
-    int S = 1;
-    while (2 * S <= kStageMaxWaves && (blocks * S < 2048 || (XI == 8 && S < 4)) && steps / (2 * S) >= 2)
-        S *= 2;
+    int S = blocks <= kRowBlocksPerRound ? 8 : (XI == 2 && blocks >= 3 * kRowBlocksPerRound) ? 2 : 4;
+    while (S > 1 && steps / S < 2)
+        S /= 2;
     const dim3 grid((unsigned)blocks), block(kWave * S);
     if (a.y_bf16)
         k_w4a16_mfma_lds<XI, G, SYM, true><<<grid, block, 0, st>>>(x, M, a.N, a.K, a.w, a.scales, a.zeros, y);
