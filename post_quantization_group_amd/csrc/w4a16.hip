@@ -831,6 +831,198 @@ __global__ __launch_bounds__(64 * kStageMaxWaves) void k_w4a16_mfma_lds(
     }
 }
 
+// ------------------------------------------------------------------ shared activation tile, 17-32 tokens
+//
+// The staged kernel gives each wave its own K slice, so at 32 tokens every wave stages 8 KB of activations per
+// 2 KB of weights. Here a block of 8 waves is R row waves (32 rows each) x S = 8 / R K groups: the R waves of a
+// K group walk the same 128-code steps and share one activation tile per step, each loading 8 / R of its
+// 8 instructions. The tile (with the per-token sums of the step, on the VALU as in the staged kernel at up to
+// 8 tokens) is double-buffered in LDS with one block barrier per step; each wave stages its own 32 weight rows
+// as in the staged kernel. g = 128, symmetric codes (one scale per row and step), K % 128 == 0. All K groups
+// run the same number of steps (the longest slice); steps past a group's slice re-read its last step with a
+// zero scale. Measured on the 70B projections at M = 32: q|k|v 28.1 us against 31.5 for the staged kernel,
+// gate|up 89 against 97-100, the 28672-row gate 50.6 against 57; on 8192-row layers it loses (o 27.6 against
+// 21.1), so it takes layers of more than 8192 rows.
+template <int R, bool OUT_BF16>
+__global__ __launch_bounds__(512) void k_w4a16_mfma_shared(const uint16_t *__restrict__ x, int64_t M, int64_t N,
+                                                           int64_t K, const uint8_t *__restrict__ w,
+                                                           const float *__restrict__ scales, void *__restrict__ y)
+{
+    constexpr int XI = 8;                      // activation instructions of 4 tokens per step
+    constexpr int S = 8 / R;                   // K groups
+    constexpr int kTokens = 4 * XI;
+    constexpr int NR = 16;                     // accumulator registers (32 tokens)
+    constexpr int XL = XI / R;                 // activation load instructions per wave
+    static_assert(XI % R == 0, "the row waves split the activation instructions");
+    constexpr int kXB = XI * 1024 + kTokens * 4;  // one activation buffer: tile + per-token sums
+    __shared__ __attribute__((aligned(16))) uint8_t wls[8 * 2048];
+    __shared__ __attribute__((aligned(16))) uint8_t xls[S * 2 * kXB];
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int rw = wv % R, kg = wv / R;
+    const int col = lane % 32, h = lane / 32;
+    const int64_t n0 = (int64_t)blockIdx.x * 32 * R + 32 * rw;
+    const int steps = (int)(K / 128);
+    const int nsmax = (steps + S - 1) / S;
+    const int s_begin = steps * kg / S, s_end = steps * (kg + 1) / S;
+    const int s_last = s_end > s_begin ? s_end - 1 : s_begin;  // s_begin < steps for every group
+    const uint32_t mask = vreg_const(kNibbleMask);
+    const uint32_t magic = vreg_const(kMagic128 ^ kSignFlip128);
+    uint8_t *const wl = wls + wv * 2048;
+    uint8_t *const xb0 = xls + kg * 2 * kXB;
+
+    // weights: instruction I covers rows 16 I + lane / 4, piece lane % 4 (chunk ^= (row / 4) % 4 in LDS)
+    const uint8_t *wsrc[2];
+    int wdst[2];
+#pragma unroll
+    for (int I = 0; I < 2; ++I) {
+        const int r = 16 * I + lane / 4, e = lane % 4, swz = (r >> 2) & 3;
+        wsrc[I] = w + std::min<int64_t>(n0 + r, N - 1) * (K / 2) + 16 * e;
+        wdst[I] = r * 64 + 16 * (e ^ swz);
+    }
+    // activations: this wave's instructions J = rw XL + I cover tokens 4 J + lane / 16, piece lane % 16
+    // (piece ^= token % 16 in LDS); tokens past M repeat token M - 1
+    const uint16_t *xsrc[XL];
+    int xdst[XL], xtok[XL];
+#pragma unroll
+    for (int I = 0; I < XL; ++I) {
+        const int J = rw * XL + I;
+        const int t = 4 * J + lane / 16, p = lane % 16;
+        xsrc[I] = x + std::min<int64_t>(t, M - 1) * K + 8 * p;
+        xdst[I] = t * 256 + 16 * (p ^ (t & 15));
+        xtok[I] = t;
+    }
+    int brd[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        brd[q] = col * 64 + 16 * ((2 * h + q) ^ ((col >> 2) & 3));
+    const float *ssrc = scales + std::min<int64_t>(n0 + col, N - 1) * steps;
+
+    u32x4_t wr[2], xr[XL];
+    float sr;
+    auto wload = [&](int i) __attribute__((always_inline)) {
+        const int st = min(s_begin + i, s_last);
+#pragma unroll
+        for (int I = 0; I < 2; ++I)
+            wr[I] = *reinterpret_cast<const u32x4_t *>(wsrc[I] + st * 64);
+        sr = (s_begin + i < s_end) ? ssrc[st] : 0.0f;  // steps past the slice add nothing
+    };
+    auto xload = [&](int i) __attribute__((always_inline)) {
+        const int st = min(s_begin + i, s_last);
+#pragma unroll
+        for (int I = 0; I < XL; ++I)
+            xr[I] = *reinterpret_cast<const u32x4_t *>(xsrc[I] + st * 128);
+    };
+    // activations re-paired as (x_j, x_{j+4}) into buffer buf, and each token's sum over the step (dot2 against
+    // ones, then the 16 lanes of the token added by a DPP butterfly)
+    auto xstore = [&](int buf) __attribute__((always_inline)) {
+        uint8_t *const xl = xb0 + buf * kXB;
+        float *const xsl = reinterpret_cast<float *>(xl + XI * 1024);
+#pragma unroll
+        for (int I = 0; I < XL; ++I) {
+            const u32x4_t v = xr[I];
+            *reinterpret_cast<u32x4_t *>(xl + xdst[I]) =
+                u32x4_t{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                        __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+            float sx = dot2(v.x, kBf16OnePair, dot2(v.y, kBf16OnePair, dot2(v.z, kBf16OnePair,
+                                                                             dot2(v.w, kBf16OnePair, 0.0f))));
+            sx += dpp_f32<0xB1>(sx);   // quad: lanes 1 apart
+            sx += dpp_f32<0x4E>(sx);   // quad: lanes 2 apart
+            sx += dpp_f32<0x141>(sx);  // half-row mirror: the other quad of the 8
+            sx += dpp_f32<0x140>(sx);  // row mirror: the other 8 of the 16
+            if (lane % 16 == 0)
+                xsl[xtok[I]] = sx;
+        }
+    };
+
+    float acc[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+        acc[r] = 0.0f;
+
+    // step 0's activations into buffer 0, step 1's in registers, step 0's weights in registers
+    xload(0);
+    xstore(0);
+    xload(1);
+    wload(0);
+    __syncthreads();
+    for (int i = 0; i < nsmax; ++i) {
+        const int cb = i & 1;
+#pragma unroll
+        for (int I = 0; I < 2; ++I)
+            *reinterpret_cast<u32x4_t *>(wl + wdst[I]) = wr[I];
+        const float sc = sr;
+        wload(i + 1);
+        xstore(cb ^ 1);  // step i + 1's activations into the other buffer
+        xload(i + 2);
+        uint8_t *const xl = xb0 + cb * kXB;
+        const float *xsl = reinterpret_cast<const float *>(xl + XI * 1024);
+        uint4 b[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            b[q] = *reinterpret_cast<const uint4 *>(wl + brd[q]);
+        f32x16_t xs, d;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            xs[r] = 0.0f;
+            d[r] = 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < NR / 4; ++q) {
+            const float4 f = *reinterpret_cast<const float4 *>(xsl + 8 * q + 4 * h);
+            xs[4 * q] = f.x;
+            xs[4 * q + 1] = f.y;
+            xs[4 * q + 2] = f.z;
+            xs[4 * q + 3] = f.w;
+        }
+        // MFMA t: lane h holds codes 64 h + 8 t .. + 8 of the step for token (A) and row (B) col
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int piece = 8 * h + t;
+            const bf16x8_t a = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const uint4 *>(xl + col * 256 + 16 * (piece ^ (col & 15))));
+            const uint4 wq = b[t / 4];
+            const uint32_t wd = (t % 4 == 0) ? wq.x : (t % 4 == 1) ? wq.y : (t % 4 == 2) ? wq.z : wq.w;
+            const bf16x8_t bw = as_bf16x8(pair_bits(wd, mask, magic), pair_bits(wd >> 4, mask, magic),
+                                          pair_bits(wd >> 8, mask, magic), pair_bits(wd >> 12, mask, magic));
+            d = mfma_bf16_32(a, bw, d);
+        }
+        // sum_k x (u - 8) = sum_k x (128 + u) - 136 sum_k x, then the row's scale for this step
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            acc[r] = __builtin_fmaf(sc, __builtin_fmaf(-136.0f, xs[r], d[r]), acc[r]);
+        __syncthreads();  // buffer cb is free for step i + 2; step i + 1's activations are visible
+    }
+
+    // K groups 1 .. S - 1 park their sums over the activation buffers, group 0 adds them in group order
+    float *red = reinterpret_cast<float *>(xls);  // [S - 1][R][NR][64]
+    static_assert((S - 1) * R * NR * kWave * 4 <= S * 2 * kXB, "partials fit");
+    if (kg > 0)
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            red[(((kg - 1) * R + rw) * NR + r) * kWave + lane] = acc[r];
+    __syncthreads();
+    if (kg > 0)
+        return;
+    for (int g = 1; g < S; ++g)
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            acc[r] += red[(((g - 1) * R + rw) * NR + r) * kWave + lane];
+    const int64_t n = n0 + col;
+    if (n >= N)
+        return;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int64_t m = 8 * (r / 4) + 4 * h + r % 4;
+        if (m < M) {
+            if (OUT_BF16)
+                reinterpret_cast<uint16_t *>(y)[m * N + n] = (uint16_t)f32_to_bf16_bits(acc[r]);
+            else
+                reinterpret_cast<float *>(y)[m * N + n] = acc[r];
+        }
+    }
+}
+
 namespace {
 
 // Waves per block: split K until the grid holds about `target_waves` waves, keeping at least one full
@@ -922,6 +1114,26 @@ hipError_t lds_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y,
     return hipGetLastError();
 }
 
+// Shared-activation launch (17-32 tokens): R row waves per block, the smallest of 2, 4, 8 that leaves at most
+// 256 blocks (on the 70B layers: q|k|v 10240 rows at R = 2 28 us against 45 at R = 4; the 28672-row gate at
+// R = 4 50.6 us against 55.6 at R = 2; gate|up at R = 4 or 8 89-90 us against 100 at R = 2).
+template <int R>
+hipError_t shared_launch(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
+{
+    const dim3 grid((unsigned)((a.N + 32 * R - 1) / (32 * R))), block(kWave * 8);
+    if (a.y_bf16)
+        k_w4a16_mfma_shared<R, true><<<grid, block, 0, st>>>(x, M, a.N, a.K, a.w, a.scales, y);
+    else
+        k_w4a16_mfma_shared<R, false><<<grid, block, 0, st>>>(x, M, a.N, a.K, a.w, a.scales, y);
+    return hipGetLastError();
+}
+
+// Layers of more than 8192 rows with at least two 128-code steps per K group of the shared kernel.
+inline bool shared_fits(const W4A16Args &a, int64_t M)
+{
+    return M > 16 && M <= 32 && a.N > 32 * kRowBlocksPerRound && a.K / 128 >= 8;
+}
+
 template <int G, bool SYM>
 hipError_t lds_mg(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hipStream_t st)
 {
@@ -929,6 +1141,13 @@ hipError_t lds_mg(const W4A16Args &a, const uint16_t *x, int64_t M, void *y, hip
         return lds_launch<2, G, SYM>(a, x, M, y, st);
     if (M <= 16)
         return lds_launch<4, G, SYM>(a, x, M, y, st);
+    if (G == 128 && SYM && shared_fits(a, M)) {
+        if (a.N <= 64 * kRowBlocksPerRound)
+            return shared_launch<2>(a, x, M, y, st);
+        if (a.N <= 128 * kRowBlocksPerRound)
+            return shared_launch<4>(a, x, M, y, st);
+        return shared_launch<8>(a, x, M, y, st);
+    }
     return lds_launch<8, G, SYM>(a, x, M, y, st);
 }
 

@@ -254,6 +254,24 @@ def test_w4a16_staged_ragged_fp32(gpu_lib, shape, gs, sym):
     assert err <= TOL_F32, err
 
 
+# 17-32 tokens on layers of more than 8192 rows (symmetric, g = 128) take the shared-activation kernel: 2, 4 or
+# 8 row waves per block (N up to 16384, 32768, beyond), ragged last blocks (and N not a multiple of 32), K-step
+# counts that split unevenly over the K groups (9 and 10 steps over 2 and 4 groups), M = 17, 24, 31, 32
+@pytest.mark.parametrize("shape", [(17, 8224, 1024, "f32"), (32, 9000, 1280, "f32"), (31, 16448, 1152, "f32"),
+                                   (24, 32800, 1024, "f32"), (32, 12000, 2048, "bf16")])
+def test_w4a16_shared_activation(gpu_lib, shape):
+    m, n, k, out = shape
+    announce("w4a16 shared-activation %s" % (shape,))
+    rng = np.random.default_rng(zlib.crc32(repr(("shared", shape)).encode()))
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x = W.bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    y, y_ref, gq, oq = w4a16_case(gpu_lib, w, False, x, True, 128, odt)
+    assert_quant_equal(gq, oq, 4, True)
+    err = normwise(y, y_ref)
+    assert err <= (TOL_F32 if out == "f32" else TOL_BF16), err
+
+
 @pytest.mark.parametrize("proj", range(len(W.L70B_PROJ)))
 def test_w4a16_l70b_sampled(gpu_lib, proj):
     """Full-size 70B projection: GPU quantizes all of it and runs the GEMV at M=1, 8, 32; the oracle checks
