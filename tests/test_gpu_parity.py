@@ -235,9 +235,13 @@ def test_w4a16_ragged_fp32(gpu_lib, shape, sym):
 
 # 5 <= M <= 64 with K % 128 == 0 takes the LDS-staged matrix-core kernel (32 tokens per launch): ragged N
 # (partial 32-row tile), group counts that are not a multiple of the four-group metadata load nor of the K
-# split, one 128-code step, M = 33 and 64 (two launches); K % 128 != 0 and M > 64 take the general one
+# split, one 128-code step, M = 33 and 64 (two launches); K % 128 != 0 and M > 64 take the general one.
+# More than 256 row blocks of 32 take 4 waves per block (2 at up to 8 tokens from 768 blocks on), fewer when K
+# is short: (8, 8224, 256) 257 blocks and 2 steps (one wave), (8, 24608, 512) 769 blocks at 2 waves,
+# (16, 24608, 384) 769 blocks and 3 steps (one wave)
 @pytest.mark.parametrize("shape", [(5, 130, 640), (13, 33, 1152), (20, 1, 384), (32, 257, 2688), (9, 64, 128),
-                                   (32, 96, 8192), (33, 70, 512), (64, 130, 1024), (8, 40, 160), (70, 65, 256)])
+                                   (32, 96, 8192), (33, 70, 512), (64, 130, 1024), (8, 40, 160), (70, 65, 256),
+                                   (8, 8224, 256), (8, 24608, 512), (16, 24608, 384)])
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("sym", [True, False])
 def test_w4a16_staged_ragged_fp32(gpu_lib, shape, gs, sym):
