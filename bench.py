@@ -13,7 +13,8 @@ One step is one pass over every stage of the quantized linear layer on synthetic
              four launches over q|k|v and gate|up stored as concatenated matrices sharing their input, as
              serving engines store them; and a third copy of the layer with 16-bit metadata)
   w4a16_m32  the layer at batch 32, four launches over the concatenated layout (q|k|v, o, gate|up, down;
-             every fifth step the seven projections instead, reported apart)
+             every fifth step the seven projections instead, and in the steps whose decode pass runs as four
+             launches the four products in one grouped launch; both reported apart)
   w4a16_m8   the same at batch 8
   smooth     SmoothQuant factor, alpha = 0.5, X 2048x4096 (41 channels x50), W 11008x4096
   wquant     W' = W diag(s) -> INT8 per output channel
@@ -342,13 +343,21 @@ def main():
         # the batched passes run over the concatenated layout (q|k|v, o, gate|up, down: four launches), or
         # over the seven projections in mode 4
         batched = projs if mode == 4 else fused
-        for p in batched:  # S7: batch 32
-            pqg.qlinear_w4a16(p["x"], p["packed"][o], p["scales"][o], None, 128, True, out=p["y32"])
+        if mode == 2:  # S7: batch 32, the four products in one grouped launch
+            pqg.qlinear_w4a16_grouped([f["x"] for f in fused], [f["packed"][o] for f in fused],
+                                      [f["scales"][o] for f in fused], None, 128, True, outs=[f["y32"] for f in fused])
+        else:
+            for p in batched:  # S7: batch 32
+                pqg.qlinear_w4a16(p["x"], p["packed"][o], p["scales"][o], None, 128, True, out=p["y32"])
         if rec:
             marks["w4a16_m32"] = ev()
             marks["w4a16_m32"].record(stream)
-        for p in batched:  # S7: batch 8, same copy
-            pqg.qlinear_w4a16(p["x"][:8], p["packed"][o], p["scales"][o], None, 128, True, out=p["y8"])
+        if mode == 2:  # S7: batch 8, same copy, the four products in one grouped launch
+            pqg.qlinear_w4a16_grouped([f["x"][:8] for f in fused], [f["packed"][o] for f in fused],
+                                      [f["scales"][o] for f in fused], None, 128, True, outs=[f["y8"] for f in fused])
+        else:
+            for p in batched:  # S7: batch 8, same copy
+                pqg.qlinear_w4a16(p["x"][:8], p["packed"][o], p["scales"][o], None, 128, True, out=p["y8"])
         if rec:
             marks["w4a16_m8"] = ev()
             marks["w4a16_m8"].record(stream)
@@ -399,6 +408,8 @@ def main():
     fused_seq_ms = []
     meta16_seq_ms = []
     batched_seven = {"w4a16_m32": [], "w4a16_m8": []}
+    batched_grouped_m8 = []
+    batched_grouped_m32 = []
     for marks, gemv_ev, mode in records:
         prev = marks["start"]
         for k in parts:
@@ -406,6 +417,10 @@ def main():
             prev = marks[k]
             if k in batched_seven and mode == 4:
                 batched_seven[k].append(t)
+            elif k == "w4a16_m8" and mode == 2:
+                batched_grouped_m8.append(t)
+            elif k == "w4a16_m32" and mode == 2:
+                batched_grouped_m32.append(t)
             elif k != "w4a16_m1" or mode == 0:
                 per_part[k].append(t)
             elif mode == 2:
@@ -497,10 +512,13 @@ def main():
         "layer_quantize_gbs": round(quant_bytes / (part_ms["quantize"] * 1e-3) / 1e9, 1),
         "layer_dequantize_gbs": round(quant_bytes / (part_ms["dequantize"] * 1e-3) / 1e9, 1),
         # the batched passes over the same weight stream (packed codes + scales), as weight GB/s: over the
-        # concatenated layout (four launches), and over the seven projections (steps of mode 4)
+        # concatenated layout (four launches), the same four products in one grouped launch (steps of mode 2), and
+        # over the seven projections (steps of mode 4)
         "w4a16_batched_weight_gbs": {m: round(gemv_bytes / (part_ms["w4a16_m%d" % m] * 1e-3) / 1e9, 1)
                                      for m in (8, 32)},
         "w4a16_batched_layout": ["+".join(W.L70B_PROJ[i][0] for i in g) for g in groups],
+        "w4a16_batched_grouped_gbs": {m: (round(gemv_bytes / (med(v) * 1e-3) / 1e9, 1) if v else None)
+                                      for m, v in ((8, batched_grouped_m8), (32, batched_grouped_m32))},
         "w4a16_batched_seven_launches_gbs": {
             m: (round(gemv_bytes / (med(batched_seven["w4a16_m%d" % m]) * 1e-3) / 1e9, 1)
                 if batched_seven["w4a16_m%d" % m] else None) for m in (8, 32)},

@@ -170,12 +170,15 @@ int32_t pqg_qlinear_w4a16(const void *x, int64_t M, int64_t N, int64_t K, const 
                           void *y, int32_t y_dtype, void *stream);
 
 /*
- * Grouped decode: several independent W4A16 products y_i = x_i W_i^T (as pqg_qlinear_w4a16) in ONE launch
- * [P3 §11.10.1: at decode every weight of the layer is read once per generated token, so the time is the
- * whole weight stream; P3 §11.1.6: INT4 groups]. Streaming the row blocks of all the problems as one grid
- * removes the launch gap and the partly idle tail of each small product (the Llama-70B k and v projections,
- * 1024 x 8192, do not fill the GPU on their own). Use it for products whose inputs are ready together: the
- * projections that read the same normalised hidden state, or expert weights.
+ * Grouped product: several independent W4A16 products y_i = x_i W_i^T (as pqg_qlinear_w4a16), in ONE launch
+ * up to 32 tokens [P3 §11.10.1: at decode every weight of the layer is read once per generated token, so the
+ * time is the whole weight stream; P3 §11.1.6: INT4 groups; P3 §11.3.7: the same products batched]. Streaming
+ * the row blocks of all the problems as one grid removes the launch gap and the partly idle tail of each small
+ * product (the Llama-70B k and v projections, 1024 x 8192, do not fill the GPU on their own). Use it for
+ * products whose inputs are ready together: the projections that read the same normalised hidden state, or
+ * expert weights. Up to 4 tokens the decode kernel runs; 5 to 32 tokens the staged matrix-core kernel, in one
+ * launch when every problem has K % 128 == 0 (else one launch per problem); above 32 tokens one launch per
+ * problem, exactly as pqg_qlinear_w4a16 on each.
  *   problems : HOST array of `count` descriptors (1 <= count <= 8), read during the call only (they are
  *              copied into the launch), each with
  *                x        bf16 [M, K] activations (device),
@@ -183,7 +186,7 @@ int32_t pqg_qlinear_w4a16(const void *x, int64_t M, int64_t N, int64_t K, const 
  *                scales   fp32 [N, K / group_size]; zeros uint8 [N, K / group_size], NULL iff symmetric (device),
  *                y        [M, N] of y_dtype (device, out),
  *                N, K     the problem's shape (K % group_size == 0; a problem with N == 0 is skipped).
- *   M        : tokens, 0 <= M <= 4 (the decode kernel; larger M returns PQG_EUNSUPPORTED), common to all.
+ *   M        : tokens, M >= 0, common to all.
  *   group_size, symmetric, y_dtype : common to all problems, as pqg_qlinear_w4a16.
  * Every problem is checked before anything is enqueued. Each result is that of pqg_qlinear_w4a16 on the
  * problem alone up to the order of the fp32 partial sums: both run the same per-row-block code, but a single

@@ -245,8 +245,8 @@ def qlinear_w4a16(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
 
 def qlinear_w4a16_grouped(xs, ws, scales, zeros, group_size: int, symmetric: bool, out_dtype=torch.bfloat16,
                           outs=None):
-    """pqg_qlinear_w4a16_grouped: one launch over several decode products y_i = x_i @ dequant(w_i)^T. xs: bf16
-    [M, K_i] (M <= 4, common); ws: packed [N_i, K_i / 2]; scales / zeros: per problem (zeros None when
+    """pqg_qlinear_w4a16_grouped: several products y_i = x_i @ dequant(w_i)^T, in one launch up to 32 tokens.
+    xs: bf16 [M, K_i] (M common); ws: packed [N_i, K_i / 2]; scales / zeros: per problem (zeros None when
     symmetric). Returns the list of y_i ([M, N_i] of out_dtype, or the tensors of `outs`)."""
     lib = load()
     n = len(xs)

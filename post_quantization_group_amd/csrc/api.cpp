@@ -284,8 +284,6 @@ int32_t pqg_qlinear_w4a16_grouped(const pqg_w4a16_problem *problems, int32_t cou
         return fail(PQG_EINVAL, "problems is required");
     if (M < 0)
         return fail(PQG_EINVAL, "negative shape");
-    if (M > 4)
-        return fail(PQG_EUNSUPPORTED, "the grouped decode takes M <= 4 tokens (got %lld)", (long long)M);
     if (!valid_float_dtype(y_dtype))
         return fail(PQG_EINVAL, "unknown y_dtype %d", y_dtype);
     if (group_size != 32 && group_size != 64 && group_size != 128)

@@ -269,7 +269,7 @@ def test_w4a16_grouped_rejects(lib):
             setattr(probs[int(i[1:])], field, v)
         return lib.pqg_qlinear_w4a16_grouped(probs, n, M, g, sym, yd, None)
     for kw, rc, needle in [(dict(n=0), pqg.EINVAL, "count"), (dict(n=9), pqg.EINVAL, "count"),
-                           (dict(M=5), pqg.EUNSUPPORTED, "M <= 4"), (dict(g=48), pqg.EINVAL, "group_size"),
+                           (dict(M=-1), pqg.EINVAL, "negative"), (dict(g=48), pqg.EINVAL, "group_size"),
                            (dict(yd=3), pqg.EINVAL, "y_dtype"), (dict(p1_K=8000), pqg.EINVAL, "problem 1"),
                            (dict(p0_x=None), pqg.EINVAL, "required"), (dict(sym=0), pqg.EINVAL, "zeros is required"),
                            (dict(p1_zeros=0x10000), pqg.EINVAL, "must be NULL"), (dict(p1_K=0), pqg.EUNSUPPORTED, "K == 0"),

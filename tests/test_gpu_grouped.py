@@ -1,7 +1,7 @@
-"""Grouped decode (pqg_qlinear_w4a16_grouped) through the C ABI against the oracle within the float tolerances
-("第11章 模型量化与压缩" §11.10.1, §11.1.6), and against pqg_qlinear_w4a16 on each problem alone: equal up to the
-order of the fp32 partial sums (a single small launch may split K over more waves than the grouped grid), i.e.
-within 1e-6 normwise for fp32 outputs and at most one bf16 ulp apart element by element for bf16 outputs."""
+"""Grouped products (pqg_qlinear_w4a16_grouped) through the C ABI against the oracle within the float tolerances
+("第11章 模型量化与压缩" §11.10.1, §11.1.6, §11.3.7), and against pqg_qlinear_w4a16 on each problem alone: equal up
+to the order of the fp32 partial sums (a single small launch may split K over more waves than the grouped grid),
+i.e. within 1e-6 normwise for fp32 outputs and at most one bf16 ulp apart element by element for bf16 outputs."""
 import numpy as np
 import pytest
 import torch
@@ -31,7 +31,9 @@ def _close_to_single(y, y1):
         assert np.all(np.abs(a - b) <= 1), int(np.abs(a - b).max())
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4])
+# up to 4 tokens the decode kernel, 5-32 the staged matrix-core kernel in one launch, 33 and more one launch per
+# problem
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 13, 16, 17, 32, 40])
 @pytest.mark.parametrize("gs,sym", [(128, True), (32, False), (64, True)])
 def test_grouped_small_ragged(gpu_lib, m, gs, sym):
     """Five problems of different shapes (ragged row blocks, several K, one empty) against the oracle and
@@ -58,6 +60,31 @@ def test_grouped_small_ragged(gpu_lib, m, gs, sym):
         if n == 0:
             continue
         _close_to_single(ys[i], singles[i])
+        assert normwise(to_f64(ys[i]), refs[i][0]) <= TOL_F32, i
+        assert_per_element(to_f64(ys[i]), refs[i][0], refs[i][1], BOUND_W4A16_F32, "problem %d" % i)
+
+
+def test_grouped_staged_falls_back_per_problem(gpu_lib):
+    """8 tokens with one problem whose K is not a multiple of 128: every problem runs as its own product."""
+    shapes = [(100, 1056), (40, 2048)]
+    announce("grouped fallback")
+    rng = np.random.default_rng(77)
+    xs, cs, ss, zs, refs = [], [], [], [], []
+    for n, k in shapes:
+        w = W.bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+        x = W.bf16_bits(rng.standard_normal((8, k)).astype(np.float32))
+        q, so, zo = oracle.quantize(w, 4, False, oracle.GROUP, 32)
+        xs.append(to_gpu_bf16(x))
+        cs.append(to_gpu(oracle.pack_int4(q)))
+        ss.append(to_gpu(so))
+        zs.append(to_gpu(zo))
+        refs.append((oracle.w4a16(x, q, so, zo, 32), abs_terms_w4(x, q, so, zo, 32)))
+    ys = gpu_lib.qlinear_w4a16_grouped(xs, cs, ss, zs, 32, False, out_dtype=torch.float32)
+    singles = [gpu_lib.qlinear_w4a16(xs[i], cs[i], ss[i], zs[i], 32, False, out_dtype=torch.float32)
+               for i in range(len(shapes))]
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert np.array_equal(_bits(ys[i]), _bits(singles[i])), i  # the same launches
         assert normwise(to_f64(ys[i]), refs[i][0]) <= TOL_F32, i
         assert_per_element(to_f64(ys[i]), refs[i][0], refs[i][1], BOUND_W4A16_F32, "problem %d" % i)
 
