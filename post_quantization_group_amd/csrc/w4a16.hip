@@ -1318,7 +1318,7 @@ bool staged_fits(const W4A16Args &a)
 }
 
 // Several staged products (5-32 tokens) in one launch: the problems' 32-row blocks as one grid (most K first),
-// S waves per block by the staged rule over the whole grid and the shortest K.
+// S waves per block from the whole grid and the shortest K.
 template <int XI, int G, bool SYM>
 hipError_t grouped_staged_launch(const W4A16GroupedArgs &a, hipStream_t st)
 {
@@ -1342,7 +1342,9 @@ hipError_t grouped_staged_launch(const W4A16GroupedArgs &a, hipStream_t st)
     for (int j = n; j <= kMaxGroupedProblems; ++j)
         t.begin[j] = total;
     t.count = n;
-    int S = total <= kRowBlocksPerRound ? 8 : (XI == 2 && total >= 3 * kRowBlocksPerRound) ? 2 : 4;
+    // 8 waves while the blocks fit the CUs once, else 4 (the single launch's 2 for wide layers at up to 8 tokens
+    // is slower here: the 70B layer's four products at M = 8 take 136 us with 2, 120 us with 4, 127 us with 8)
+    int S = total <= kRowBlocksPerRound ? 8 : 4;
     while (S > 1 && (kmin / 128) / S < 2)
         S /= 2;
     const dim3 grid((unsigned)total), block(kWave * S);
