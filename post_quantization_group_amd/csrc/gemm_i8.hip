@@ -500,11 +500,25 @@ hipError_t ring_launch(const GemmI8Args &g, hipStream_t st)
 //   * 64-byte K steps in a three-stage direct-to-LDS ring (3 x 40 KB), loads two steps ahead, as in the
 //     ring kernel. Stages are separate LDS blocks so that the compiler can tell a direct load into one
 //     stage from the fragment reads of another.
+//   * Ping-pong schedule. Waves w and w + 4 share a SIMD; waves 0-3 form group 0 and waves 4-7 group 1,
+//     and group 1 runs one barrier behind group 0. Each 32-deep sub-step is a memory phase (the direct
+//     loads two steps ahead at the first sub-step of a step, the wave's seven 16-byte fragment reads, and
+//     the wait for them) and a compute phase (its 12 MFMAs), each ended by a block barrier. So while one
+//     group's MFMAs run, the other group's fragment reads are in flight, and every SIMD always has a wave
+//     with operands in registers. With both groups in step (the same phases, no offset) the layer took 116
+//     us; with the compiler's own interleaving of reads and MFMAs 99-103 us; with the ping-pong 95-98 us.
+//     Raising the compute phase's wave priority made no difference. A memory phase moves 28 KB of fragments
+//     through the LDS for 384 cycles of MFMA per SIMD, so it is as long as the compute phase: the loop runs
+//     about 1.25 x the time of its MFMAs alone.
 //   * The tile's 384 weight and 256 token scales are loaded straight into LDS (640 floats) before the ring
-//     starts, so the epilogue reads each group of four weight scales with one LDS read. Taking them from
-//     global memory per output group cost 16 us of the 114 us the layer took; the epilogue then stores each
-//     group of four outputs from the accumulators (8-byte bf16 / 16-byte fp32 or int32 stores), which was
-//     3 us faster than staging bf16 rows through the ring stages.
+//     starts, so the epilogue reads each group of four weight scales with one LDS read.
+//   * bf16 epilogue: each wave passes every 32-row slice of its 128 x 96 tile through a wave-private LDS
+//     buffer (the ring stages, free by then) and writes it back as 16-byte stores along rows, 192-byte runs
+//     per row. The store phase of the one round is exposed (nothing else runs then): 45 MB of bf16 output
+//     took 15-17 us as 8-byte stores straight from the accumulators (16-byte pieces of 32 rows per
+//     instruction) and takes 6 us this way (2048 x 11008 x 4096: 98-100 us -> 87-90 us, bit-identical).
+//     int32 and fp32 outputs, and bf16 outputs whose rows are not whole 16-byte chunks, keep the stores
+//     straight from the accumulators.
 //   * Operand loads carry the sc0 cache-policy bit (3 % faster on the layer; sc1 or both were slower).
 // Taken when its tiles fill between three quarters and all of the CUs in a single round; otherwise the
 // ring kernel (more, smaller tiles) balances better.
@@ -515,8 +529,12 @@ constexpr int kWideThreads = kWideWaves * kWave;
 constexpr int kWideStage = (kWideBM + kWideBN) * kWideBK;         // 40960 bytes
 constexpr int kWideLoads = kWideStage / 16 / kWideThreads;         // 5 direct loads per thread per step
 constexpr int kWideALoads = kWideBM * kWideBK / 16 / kWideThreads;  // the first 2 fill activation rows
+constexpr int kWideStagePitch = 208;  // bytes per row of a wave's 32 x 96 bf16 epilogue slice (192 + 16)
 static_assert(kWideStage % (16 * kWideThreads) == 0 && (kWideBM * kWideBK) % (16 * kWideThreads) == 0,
               "each load instruction fills whole rows of one operand");
+static_assert(kWideWaves == 8, "the ping-pong schedule pairs waves w and w + 4");
+static_assert(6 * 32 * kWideStagePitch <= kWideStage && 2 * 32 * kWideStagePitch <= kWideStage,
+              "six waves' epilogue slices fit in stage 0, two in stage 1");
 
 
 template <int MODE>
@@ -542,6 +560,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_gemm_i8_wide(const int8_t *
 
     const int tid = threadIdx.x, lane = tid % kWave;
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int grp = w / 4;  // ping-pong group
     const int wm = w % (BM / WM), wn = w / (BM / WM);
     const int fr = lane % 32, fh = lane / 32;
 
@@ -579,28 +598,43 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_gemm_i8_wide(const int8_t *
             for (int e = 0; e < 16; ++e)
                 acc[i][j][e] = 0;
 
-    auto multiply = [&](const int8_t *xs) __attribute__((always_inline)) {
+    // A block barrier that no instruction is scheduled across (the phases must stay where they are written).
+    auto phase_end = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Sub-step s of step k on stage xs. Hazards of the ring, with every wave passing the same barriers:
+    //   * the loads for step k + 2 overwrite the stage of step k - 1, whose last fragment reads (sub-step 1
+    //     of step k - 1) every wave finished (its lgkmcnt wait) before a barrier that precedes this issue;
+    //   * step k + 1's stage is read from the first sub-step of step k + 1 on; each wave waits for its own
+    //     loads of step k + 1 (all but the 5 just issued) in this memory phase, before two more barriers.
+    auto substep = [&](const int8_t *xs, int8_t *after_next, int k, int s) __attribute__((always_inline)) {
         const int8_t *ws = xs + BM * BK;
+        if (s == 0)
+            issue(after_next, k + 2);
+        v4i fx[TM], fw[TN];
 #pragma unroll
-        for (int s = 0; s < BK / 32; ++s) {
-            v4i fx[TM];
+        for (int j = 0; j < TM; ++j)
+            fx[j] = *reinterpret_cast<const v4i *>(xs + lds_off<64>(wm * WM + j * 32 + fr, 2 * s + fh));
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+            fw[i] = *reinterpret_cast<const v4i *>(ws + lds_off<64>(wn * WN + i * 32 + fr, 2 * s + fh));
+        if (s == 0)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWideLoads, 0));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        phase_end();
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
             for (int j = 0; j < TM; ++j)
-                fx[j] = *reinterpret_cast<const v4i *>(xs + lds_off<64>(wm * WM + j * 32 + fr, 2 * s + fh));
-#pragma unroll
-            for (int i = 0; i < TN; ++i) {
-                const v4i fw = *reinterpret_cast<const v4i *>(ws + lds_off<64>(wn * WN + i * 32 + fr, 2 * s + fh));
-#pragma unroll
-                for (int j = 0; j < TM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw, fx[j], acc[i][j], 0, 0, 0);
-            }
-        }
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[i], fx[j], acc[i][j], 0, 0, 0);
+        phase_end();
     };
     auto step = [&](int8_t *cur, int8_t *after_next, int k) __attribute__((always_inline)) {
-        issue(after_next, k + 2);
-        multiply(cur);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWideLoads, 0));  // step k + 1 landed, fragment reads done
-        __builtin_amdgcn_s_barrier();
+        substep(cur, after_next, k, 0);
+        substep(cur, after_next, k, 1);
     };
 
     // The tile's scales, straight into LDS before the ring starts: BN weight scales, then BM token scales (rows
@@ -619,6 +653,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_gemm_i8_wide(const int8_t *
     issue(s1, 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(kWideLoads, 15));
     __builtin_amdgcn_s_barrier();
+    // group 1 starts one barrier late and group 0 ends with one more, so both pass the same number
+    if (grp == 1)
+        phase_end();
     int k = 0;
     for (; k + 3 <= nsteps; k += 3) {
         step(s0, s2, k);
@@ -629,9 +666,45 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_gemm_i8_wide(const int8_t *
         step(s0, s2, k);
     if (k + 1 < nsteps)
         step(s1, s0, k + 1);
+    if (grp == 0)
+        phase_end();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // no direct load may land in the stages reused below
 
     __syncthreads();  // every wave's scale loads have landed (each waited for its own above)
+    if (MODE == 1 && (N % 8) == 0 && (reinterpret_cast<uintptr_t>(c) % 16) == 0) {
+        int8_t *const wbuf = w < 6 ? s0 + w * 32 * kWideStagePitch : s1 + (w - 6) * 32 * kWideStagePitch;
+        uint16_t *const y = static_cast<uint16_t *>(c);
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int ml = wm * WM + j * 32 + fr;
+            const float sxm = lsc[BN + ml];
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int cl = i * 32 + 8 * g + 4 * fh;  // column within the wave's 96
+                    const float4 s4 = *reinterpret_cast<const float4 *>(lsc + wn * WN + cl);
+                    const float f0 = (float)acc[i][j][4 * g] * (sxm * s4.x);
+                    const float f1 = (float)acc[i][j][4 * g + 1] * (sxm * s4.y);
+                    const float f2 = (float)acc[i][j][4 * g + 2] * (sxm * s4.z);
+                    const float f3 = (float)acc[i][j][4 * g + 3] * (sxm * s4.w);
+                    *reinterpret_cast<uint2 *>(wbuf + fr * kWideStagePitch + cl * 2) =
+                        make_uint2(pack_bf16x2_rne(f0, f1), pack_bf16x2_rne(f2, f3));
+                }
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+            // 32 rows x 12 chunks of 16 bytes; N % 8 == 0, so a chunk is wholly inside or outside N
+#pragma unroll
+            for (int u = 0; u < 6; ++u) {
+                const int q = lane + kWave * u, row = q / 12, ch = q % 12;
+                const v4i v = *reinterpret_cast<const v4i *>(wbuf + row * kWideStagePitch + ch * 16);
+                const int64_t m = m0 + wm * WM + j * 32 + row, n = n0 + wn * WN + ch * 8;
+                if (m < M && n < N)
+                    *reinterpret_cast<v4i *>(y + m * N + n) = v;
+            }
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));  // the slice is read out before the next overwrites it
+        }
+        return;
+    }
     const bool vec_ok = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(c) % (MODE == 1 ? 8 : 16)) == 0;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
