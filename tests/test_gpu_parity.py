@@ -472,6 +472,26 @@ def test_w8a8_small_bf16_out(gpu_lib, mnk):
     assert_per_element(to_f64(y), r["y"], abs_terms_i8(r["q_x"], r["s_x"], r["q_w"], r["s_w"]), BOUND_W8A8_BF16, "W8A8 bf16")
 
 
+def test_w8a8_bf16_out_unaligned_matches(gpu_lib):
+    """The wide kernel's bf16 epilogue into an output that is not 16-byte aligned (stores straight from the
+    accumulators) gives the same bits as into an aligned one (rows staged through LDS); the aligned result is
+    checked against the oracle at this shape in test_w8a8_small_bf16_out."""
+    announce("w8a8 bf16 unaligned output")
+    m, n, k = 2000, 11000, 128
+    d = W.w8a8(m=m, n=n, k=k)
+    xg, wg = to_gpu_bf16(d["x"]), to_gpu_bf16(d["w"])
+    s = gpu_lib.smooth(xg, wg, 0.5)
+    w_q, s_w, _ = gpu_lib.quantize(wg, 8, True, 1, 0, s, 2)
+    y, x_q, s_x = gpu_lib.qlinear_w8a8(xg, s, w_q, s_w, out_dtype=torch.bfloat16)
+    assert y.data_ptr() % 16 == 0
+    buf = torch.empty(m * n + 4, dtype=torch.bfloat16, device=y.device)
+    y_off = buf[4:].view(m, n)
+    assert y_off.data_ptr() % 16 == 8
+    gpu_lib.qlinear_w8a8(None, None, w_q, s_w, out=y_off, x_q=x_q, x_scales=s_x)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_off.view(torch.int16))
+
+
 # --------------------------------------------------------------------------- static per-tensor path
 
 # The scale is 0.7 x the calibration batch's own per-tensor scale, so that about the top 30 % of the range
