@@ -9,9 +9,10 @@
 // 16x16x64 form on gfx950, so it is the building block. The weight tile is the MFMA "A" operand and the
 // activation tile "B": lane l holds output column m = l % 32 and, in accumulator register r, output row
 // n = 8 (r / 4) + 4 (l / 32) + r % 4, i.e. four consecutive output channels per group of four registers.
-// In the 128 x 128 and ring kernels the bf16 epilogue (when output rows are 16-byte aligned) stages the scaled
-// tile in LDS and writes it back as 16-byte stores along output rows; otherwise, and always in the wide
-// kernel, each group of four registers is one 16-byte (int32 / fp32) or 8-byte (bf16) store.
+// The bf16 epilogue (when output rows are whole 16-byte chunks) stages the scaled tile in LDS and writes it back
+// as 16-byte stores along output rows: the whole tile at once in the 128 x 128 and ring kernels, each wave's
+// 32-row slices in the wide kernel; otherwise each group of four registers is one 16-byte (int32 / fp32) or
+// 8-byte (bf16) store.
 // Three kernels share this layout. With K % 64 == 0, the wide kernel at the end (256 x 384 tiles, one block
 // of eight waves per CU) takes shapes whose tiles fill three quarters to all of the CUs in one round, and the
 // ring kernel (256 x 128 tiles) other shapes with M >= 256; both load their operands straight into a
@@ -505,9 +506,10 @@ hipError_t ring_launch(const GemmI8Args &g, hipStream_t st)
 //     loads two steps ahead at the first sub-step of a step, the wave's seven 16-byte fragment reads, and
 //     the wait for them) and a compute phase (its 12 MFMAs), each ended by a block barrier. So while one
 //     group's MFMAs run, the other group's fragment reads are in flight, and every SIMD always has a wave
-//     with operands in registers. With both groups in step (the same phases, no offset) the layer took 116
-//     us; with the compiler's own interleaving of reads and MFMAs 99-103 us; with the ping-pong 95-98 us.
-//     Raising the compute phase's wave priority made no difference. A memory phase moves 28 KB of fragments
+//     with operands in registers. With the epilogue below, the compiler's own interleaving of reads and
+//     MFMAs took 89.5-94 us on the 2048 x 11008 x 4096 layer, the ping-pong 87-90 us; with both groups in
+//     step (the same phases, no offset) it took 116 us (stores straight from the accumulators). Raising the
+//     compute phase's wave priority made no difference. A memory phase moves 28 KB of fragments
 //     through the LDS for 384 cycles of MFMA per SIMD, so it is as long as the compute phase: the loop runs
 //     about 1.25 x the time of its MFMAs alone.
 //   * The tile's 384 weight and 256 token scales are loaded straight into LDS (640 floats) before the ring
@@ -519,7 +521,8 @@ hipError_t ring_launch(const GemmI8Args &g, hipStream_t st)
 //     instruction) and takes 6 us this way (2048 x 11008 x 4096: 98-100 us -> 87-90 us, bit-identical).
 //     int32 and fp32 outputs, and bf16 outputs whose rows are not whole 16-byte chunks, keep the stores
 //     straight from the accumulators.
-//   * Operand loads carry the sc0 cache-policy bit (3 % faster on the layer; sc1 or both were slower).
+//   * Operand loads carry the sc0 cache-policy bit (3 % faster with the compiler-interleaved loop, no
+//     difference with the ping-pong; sc1 or both were slower).
 // Taken when its tiles fill between three quarters and all of the CUs in a single round; otherwise the
 // ring kernel (more, smaller tiles) balances better.
 constexpr int kWideBM = 256, kWideBN = 384, kWideWM = 128, kWideWN = 96, kWideBK = 64;
