@@ -38,6 +38,7 @@ launch before it has pushed out of the last-level cache, and no launch waits on 
 
 After the timed steps, the Llama-7B attention and FFN configurations are measured on their own (quantize and
 W4A16 throughput over device copies rotated past the last-level cache, metadata bytes against weight bytes),
+then the tiny 256 x 512 configuration (quantize, dequantize and GEMV times: launch-bound, no roofline claim),
 and the oracle is timed on the host: the decode sample (cpu_baseline) and each function on all threads and on
 one.
 
@@ -577,6 +578,7 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = 1 << 30
     out["llama7b_configs"] = llama7b_configs(pqg, W, dev, bf16)
+    out["tiny_config"] = tiny_config(pqg, W, dev, bf16)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
         out["cpu_oracle_per_function"] = cpu_per_function(args.cpu_function_seconds)
@@ -650,6 +652,46 @@ def llama7b_configs(pqg, W, dev, bf16, reps=8, rounds=6):
         del wr, codes, scales, zeros, ys, w
         torch.cuda.empty_cache()
     return out
+
+
+def tiny_config(pqg, W, dev, bf16, reps=20, rounds=6):
+    """The tiny configuration (fp32 weight 256 x 512 with 0.5 % outliers, symmetric INT4 g = 128; x in R^512):
+    quantize, dequantize to fp32 and the W4A16 GEMV with fp32 output, each timed as `reps` launches back to
+    back between two events (median of `rounds`). 71 KB of data: the times are launch and latency, reported
+    without a roofline fraction."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    d = W.tiny()
+    w = torch.from_numpy(d["w"]).to(dev)
+    x = bf16(d["x"])
+    n, k = w.shape
+    codes, scales, _ = pqg.quantize(w, 4, True, pqg.GROUP, 128)
+    deq = torch.empty((n, k), dtype=torch.float32, device=dev)
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        ts = []
+        for r in range(rounds + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1) / reps)
+        return round(float(np.median(ts)) * 1e3, 2)
+
+    return {"N": n, "K": k, "group_size": 128, "symmetric": True,
+            "note": "per call through the Python binding, back to back: host dispatch sets these times (the "
+                    "kernels alone take 2-3 us in the kernel trace)",
+            "quantize_us": timed(lambda: pqg.quantize(w, 4, True, pqg.GROUP, 128, out=(codes, scales, None))),
+            "dequantize_us": timed(lambda: pqg.dequantize(codes, scales, None, n, k, 4, True, pqg.GROUP, 128,
+                                                          out=deq)),
+            "w4a16_m1_f32_us": timed(lambda: pqg.qlinear_w4a16(x, codes, scales, None, 128, True,
+                                                               out_dtype=torch.float32, out=y))}
 
 
 def cpu_baseline(target_s):
