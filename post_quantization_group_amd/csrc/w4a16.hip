@@ -16,14 +16,18 @@
 //     the slice are clamped to its last chunk) and computes, and chunks outside the slice get a zero
 //     scale. Divergent branches around the loads would make the compiler drain all outstanding loads at
 //     their joins.
-//   * Dequantization stays in registers and costs at most one shift and one v_bitop3_b32 per pair of
-//     codes: the nibble pair (j, j + 4) of a packed word is moved to bits [0, 4) of each 16-bit half and
-//     merged with the bf16 pattern of 128.0, giving the exact value 128 + u (the bf16 mantissa step at 128
-//     is 1). For two's-complement codes the same instruction flips the nibble's sign bit, turning q into
-//     its offset binary q + 8. Pair 0 needs no shift.
+//   * Dequantization stays in registers and costs one shift and one v_bitop3_b32 per pair of codes: the
+//     nibble pair (j, j + 4) of a packed word is moved to bits [3, 7) of each 16-bit half and merged with
+//     the bf16 pattern of 16.0, giving the exact value 16 + u (the bf16 mantissa step at 16 is 1/8, so the
+//     nibble sits in the top four mantissa bits). For two's-complement codes the same instruction flips the
+//     nibble's sign bit, turning q into its offset binary q + 8.
 //   * The products use v_dot2_f32_bf16 (two bf16 products, fp32 accumulation). The code offset is removed
-//     once per 32 codes: sum x (u - off) = sum x (128 + u) - (128 + off) sum x, with off = 8 (symmetric)
-//     or z (asymmetric), then the group scale multiplies the 32-code partial sum.
+//     once per 32 codes: sum x (u - off) = sum x (16 + u) - (16 + off) sum x, with off = 8 (symmetric)
+//     or z (asymmetric), then the group scale multiplies the 32-code partial sum. The fp32 sums run at
+//     about (16 + off) sum |x|: with the value 128 + u (nibble at bits [0, 4), which saves the shift of the
+//     first pair) they ran at (128 + off) sum |x|, and on groups whose codes sit near the zero point with a
+//     wide range (a few outliers 100 x the rest) the fp32 output was off by up to 3.7e-5 normwise against
+//     the binary64 result; the 16 + u form cancels about 6 x less.
 //   * No dequantized weight is ever written to memory.
 //
 // The matrix-core variant below keeps ordinary (allocating) weight loads: with non-temporal ones it ran
@@ -53,14 +57,10 @@ __device__ __forceinline__ uint32_t vreg_const(uint32_t c)
     return r;
 }
 
-// 16 + u form (nibbles at bits [3, 7)), used by the matrix-core kernel
+// the 16 + u form (nibbles at bits [3, 7)), used by every kernel below
 constexpr uint32_t kPairMask = 0x00780078u;
 constexpr uint32_t kMagic16 = 0x41804180u;      // bf16 16.0 | 16.0
 constexpr uint32_t kSignFlip = 0x00400040u;     // bit 6 of each half: the nibble's top bit
-// 128 + u form (nibbles at bits [0, 4)), used by the vector kernel
-constexpr uint32_t kNibbleMask = 0x000F000Fu;
-constexpr uint32_t kMagic128 = 0x43004300u;     // bf16 128.0 | 128.0
-constexpr uint32_t kSignFlip128 = 0x00080008u;  // bit 3 of each half
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // bf16 1.0 | 1.0
 constexpr int kMaxWavesPerRow = 8;
 
@@ -152,10 +152,10 @@ __device__ __forceinline__ void stage_compute(const Stage<MT, R> &st, float acc[
             part[m] = 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const uint32_t b0 = pair_bits(wd[d], mask, magic);
-            const uint32_t b1 = pair_bits(wd[d] >> 4, mask, magic);
-            const uint32_t b2 = pair_bits(wd[d] >> 8, mask, magic);
-            const uint32_t b3 = pair_bits(wd[d] >> 12, mask, magic);
+            const uint32_t b0 = pair_bits(wd[d] << 3, mask, magic);
+            const uint32_t b1 = pair_bits(wd[d] >> 1, mask, magic);
+            const uint32_t b2 = pair_bits(wd[d] >> 5, mask, magic);
+            const uint32_t b3 = pair_bits(wd[d] >> 9, mask, magic);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 part[m] = dot2(xp[m][4 * d + 0], b0, part[m]);
@@ -164,10 +164,10 @@ __device__ __forceinline__ void stage_compute(const Stage<MT, R> &st, float acc[
                 part[m] = dot2(xp[m][4 * d + 3], b3, part[m]);
             }
         }
-        // sum_k x (u - off) = sum_k x (128 + u) - (128 + off) sum_k x, then the group scale
+        // sum_k x (u - off) = sum_k x (16 + u) - (16 + off) sum_k x, then the group scale
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            acc[r][m] = __builtin_fmaf(st.s[r], __builtin_fmaf(-(128.0f + st.z[r]), xsum[m], part[m]), acc[r][m]);
+            acc[r][m] = __builtin_fmaf(st.s[r], __builtin_fmaf(-(16.0f + st.z[r]), xsum[m], part[m]), acc[r][m]);
     }
 }
 
@@ -188,8 +188,8 @@ __device__ __forceinline__ void gemv_rowblock(const uint16_t *__restrict__ x, in
     const int c_begin = (chunks * wv) >> s_shift;
     const int c_end = (chunks * (wv + 1)) >> s_shift;
     const int c_last = c_end - 1;
-    const uint32_t mask = vreg_const(kNibbleMask);
-    const uint32_t magic = vreg_const(SYM ? (kMagic128 ^ kSignFlip128) : kMagic128);
+    const uint32_t mask = vreg_const(kPairMask);
+    const uint32_t magic = vreg_const(SYM ? (kMagic16 ^ kSignFlip) : kMagic16);
 
     Bases<MT, R> bp;
 #pragma unroll
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t *__restrict__
 //     same two 16-byte reads.
 //   * The activations are re-paired as (x_j, x_{j+4}) once, when they are written to LDS, to match the
 //     nibble-pair dequantization.
-//   * acc += s * (D - (128 + off) * xsum) per group, where xsum = sum_k x over the group for the lane's tokens.
+//   * acc += s * (D - (16 + off) * xsum) per group, where xsum = sum_k x over the group for the lane's tokens.
 //     Up to 8 tokens, xsum comes from the VALU: when a lane stages its 8 activations it adds them with dot2
 //     against ones, a DPP butterfly over the lanes of its group finishes each token's sum, and the sums go
 //     to LDS beside the activations. For more tokens one more MFMA against a B of ones computes it (the
@@ -626,8 +626,8 @@ __device__ __forceinline__ void staged_rowblock(const uint16_t *__restrict__ x, 
     const int s_begin = steps * wv / S, s_end = steps * (wv + 1) / S;
     const int ns = s_end - s_begin;
     const int s_last = s_end > s_begin ? s_end - 1 : s_begin;
-    const uint32_t mask = vreg_const(kNibbleMask);
-    const uint32_t magic = vreg_const(SYM ? (kMagic128 ^ kSignFlip128) : kMagic128);
+    const uint32_t mask = vreg_const(kPairMask);
+    const uint32_t magic = vreg_const(SYM ? (kMagic16 ^ kSignFlip) : kMagic16);
     const bf16x8_t ones = as_bf16x8(kBf16OnePair, kBf16OnePair, kBf16OnePair, kBf16OnePair);
     uint8_t *const wl = lds + wv * kRegion;  // [32 rows][4 chunks of 16 B], chunk ^= (row / 4) % 4
     uint8_t *const xl = wl + 2048;           // [kTokens][16 pieces of 16 B], piece ^= token % 16
@@ -775,8 +775,7 @@ __device__ __forceinline__ void staged_rowblock(const uint16_t *__restrict__ x, 
                     xs = mfma_bf16_32(a, ones, xs);
                 const uint4 wq = b[t / 4];
                 const uint32_t wd = (t % 4 == 0) ? wq.x : (t % 4 == 1) ? wq.y : (t % 4 == 2) ? wq.z : wq.w;
-                const bf16x8_t bw = as_bf16x8(pair_bits(wd, mask, magic), pair_bits(wd >> 4, mask, magic),
-                                              pair_bits(wd >> 8, mask, magic), pair_bits(wd >> 12, mask, magic));
+                const bf16x8_t bw = dequant_word(wd, mask, magic);
                 d = mfma_bf16_32(a, bw, d);
             }
             // the element goes through a scalar first: a bit_cast of a vector-element expression reads
@@ -785,7 +784,7 @@ __device__ __forceinline__ void staged_rowblock(const uint16_t *__restrict__ x, 
             const uint32_t sbits = md.s[mi];
             const float sc = __uint_as_float(sbits);
             const float off = SYM ? 8.0f : (float)((md.z >> (8 * mi)) & 0xFFu);
-            const float cf = -(128.0f + off);
+            const float cf = -(16.0f + off);
 #pragma unroll
             for (int r = 0; r < NR; ++r)
                 acc[r] = __builtin_fmaf(sc, __builtin_fmaf(cf, xs[r], d[r]), acc[r]);
@@ -899,8 +898,8 @@ __global__ __launch_bounds__(512) void k_w4a16_mfma_shared(const uint16_t *__res
     const int nsmax = (steps + S - 1) / S;
     const int s_begin = steps * kg / S, s_end = steps * (kg + 1) / S;
     const int s_last = s_end > s_begin ? s_end - 1 : s_begin;  // s_begin < steps for every group
-    const uint32_t mask = vreg_const(kNibbleMask);
-    const uint32_t magic = vreg_const(kMagic128 ^ kSignFlip128);
+    const uint32_t mask = vreg_const(kPairMask);
+    const uint32_t magic = vreg_const(kMagic16 ^ kSignFlip);
     uint8_t *const wl = wls + wv * 2048;
     uint8_t *const xb0 = xls + kg * 2 * kXB;
 
@@ -1016,14 +1015,13 @@ __global__ __launch_bounds__(512) void k_w4a16_mfma_shared(const uint16_t *__res
                 bf16x8_t, *reinterpret_cast<const uint4 *>(xl + col * 256 + 16 * (piece ^ (col & 15))));
             const uint4 wq = b[t / 4];
             const uint32_t wd = (t % 4 == 0) ? wq.x : (t % 4 == 1) ? wq.y : (t % 4 == 2) ? wq.z : wq.w;
-            const bf16x8_t bw = as_bf16x8(pair_bits(wd, mask, magic), pair_bits(wd >> 4, mask, magic),
-                                          pair_bits(wd >> 8, mask, magic), pair_bits(wd >> 12, mask, magic));
+            const bf16x8_t bw = dequant_word(wd, mask, magic);
             d = mfma_bf16_32(a, bw, d);
         }
-        // sum_k x (u - 8) = sum_k x (128 + u) - 136 sum_k x, then the row's scale for this step
+        // sum_k x (u - 8) = sum_k x (16 + u) - 24 sum_k x, then the row's scale for this step
 #pragma unroll
         for (int r = 0; r < NR; ++r)
-            acc[r] = __builtin_fmaf(sc, __builtin_fmaf(-136.0f, xs[r], d[r]), acc[r]);
+            acc[r] = __builtin_fmaf(sc, __builtin_fmaf(-24.0f, xs[r], d[r]), acc[r]);
         __syncthreads();  // buffer cb is free for step i + 2; step i + 1's activations are visible
     }
 

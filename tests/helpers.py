@@ -31,8 +31,8 @@ def announce(msg: str) -> None:
 
 # Per-element bounds on float outputs: |y - y_ref| <= a |y_ref| + b sum_k |x_k| |w_k|, the second sum being the
 # size of the output's terms. a covers the rounding of the output itself (bf16: half an ulp is 2^-9 of |y|),
-# b the fp32 accumulation, which is relative to the terms (the W4A16 kernels sum x (128 + u) and subtract
-# (128 + off) sum x, so their fp32 sums run about 45 x larger than the result; W4A8 adds one fp32 term per
+# b the fp32 accumulation, which is relative to the terms (the W4A16 kernels sum x (16 + u) and subtract
+# (16 + off) sum x, so their fp32 sums run about 8 x larger than the result; W4A8 adds one fp32 term per
 # group; the W8A8 sum is an exact integer, rounded three times). A single output element off by a few percent
 # -- which a normwise error over a whole row hides -- breaks them.
 BOUND_BF16 = (2.0 ** -8, 2.0 ** -11)
