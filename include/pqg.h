@@ -94,7 +94,8 @@ size_t pqg_quantize_workspace_bytes(int64_t rows, int64_t cols, int32_t granular
  *   zeros (out)  : uint8, same count as scales; required iff symmetric == 0, must be NULL otherwise.
  *   workspace    : device scratch of at least pqg_quantize_workspace_bytes() bytes (may be NULL if 0).
  * Rounding is round-half-to-even of the correctly rounded fp32 quotient x / s; smoothing divides or
- * multiplies in fp32; a segment whose step would be 0 gets s = 1, z = 0. Results are bit-identical to a
+ * multiplies in fp32; a segment whose step would be 0 (an all-zero or underflowing range) codes every value
+ * to 0 with z = 0 and stores the scale 0, so that it dequantizes to exactly 0. Results are bit-identical to a
  * strict-IEEE CPU evaluation of the same formulas.
  * Requires cols % 32 == 0 and, for PQG_ROW, cols <= 65536.
  */
@@ -324,7 +325,7 @@ int32_t pqg_kv_append(const void *k_new, const void *v_new, int32_t dtype, int64
  * PQG_GROUP); the scale is stored as binary16 s16 = fp16(s), round to nearest even (a result of 0 becomes the
  * smallest subnormal 2^-24, an overflow the largest finite 65504); the codes and the asymmetric zero point use
  * the stored scale: q = clamp(rne(x / s16) + z), z = clamp(rne(-lo / s16)), so s16 (q - z) is what the
- * metadata encodes.
+ * metadata encodes. A group whose fp32 step is 0 stores 0 (and codes 0), as pqg_quantize does.
  *   x        : [rows, cols] bf16 or fp32 (x_dtype). cols % group_size == 0; group_size in {32, 64, 128}.
  *   codes    : packed INT4 [rows, cols / 2], as pqg_quantize writes them (out).
  *   scales16 : binary16 bits [rows * cols / group_size], row-major, the group index fastest (out).

@@ -66,7 +66,8 @@ static float load_elem(const void *x, int dtype, int64_t i)
 
 /* Parameters of one segment (a tensor, a row or a group). */
 typedef struct {
-    float s;   /* step / scale */
+    float s;      /* step the codes are taken with */
+    float stored; /* the scale written out: s, or 0 for a segment whose step is 0 */
     int z;     /* zero point (0 when symmetric) */
     int qmin;  /* integer range */
     int qmax;
@@ -80,9 +81,10 @@ typedef struct {
  *              s = (hi - lo) / (2^b - 1), z = round(-lo / s) clamped into the range.
  *              The range [lo, hi] is widened to contain 0 so that z is a valid code and a real 0
  *              maps to q = z and back to exactly 0 [P5: the zero point keeps 0 exact].
- * A segment whose computed step is 0 (all values zero, or so tiny that the fp32 division underflows)
- * gets s = 1, z = 0: every value then codes to 0 (or rounds to a code near 0) and no division by zero
- * can occur.
+ * A segment whose computed step is 0 (all values zero, or so tiny that the fp32 division underflows) has
+ * no step to divide by. Its codes are taken with a unit step and z = 0 (every value then codes to 0, and no
+ * division by zero can occur), and the scale it stores is the step the formula gives, 0: the dequantized
+ * segment s (q - z) is exactly 0 whatever way a consumer forms the product.
  */
 static seg_params segment_params(float absmax, float lo, float hi, int bits, int symmetric)
 {
@@ -92,8 +94,11 @@ static seg_params segment_params(float absmax, float lo, float hi, int bits, int
         p.qmin = -p.qmax;
         p.z = 0;
         p.s = absmax / (float)p.qmax;
-        if (!(p.s > 0.0f))
+        p.stored = p.s;
+        if (!(p.s > 0.0f)) {
             p.s = 1.0f;
+            p.stored = 0.0f;
+        }
     } else {
         p.qmin = 0;
         p.qmax = (1 << bits) - 1;
@@ -102,8 +107,10 @@ static seg_params segment_params(float absmax, float lo, float hi, int bits, int
         if (hi < 0.0f)
             hi = 0.0f;
         p.s = (hi - lo) / (float)p.qmax;
+        p.stored = p.s;
         if (!(p.s > 0.0f)) {
             p.s = 1.0f;
+            p.stored = 0.0f;
             p.z = 0;
         } else {
             /* clamped as a float, then converted (the quotient is in range here, but the order is that of
@@ -202,7 +209,7 @@ int or_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, const fl
             }
         }
         seg_params p = segment_params(absmax, lo, hi, bits, symmetric);
-        scales[e] = p.s;
+        scales[e] = p.stored;
         if (zeros)
             zeros[e] = (uint8_t)p.z;
         for (int64_t r = r0; r < r0 + seg_rows; ++r)
@@ -330,7 +337,8 @@ float or_f16_to_f32(uint16_t h)
  * or_quantize; the scale is stored as binary16, s16 = fp16(s) rounded to nearest even (a result of 0 becomes
  * the smallest subnormal 2^-24, an overflow the largest finite 65504); the codes (and the asymmetric zero
  * point) are computed with the stored scale, q = clamp(round(x / s16) + z), z = clamp(round(-lo / s16)), so
- * that s16 (q - z) is the value the stored metadata encodes.
+ * that s16 (q - z) is the value the stored metadata encodes. A segment whose fp32 step is 0 stores 0 (its codes
+ * are all 0, taken with the unit step as in or_quantize).
  * Outputs: q[rows * cols] unpacked, s16[rows * cols / g] binary16 bits, zeros[rows * cols / g] (NULL when
  * symmetric). Returns 0, or -1 on bad arguments.
  */
@@ -360,7 +368,7 @@ int or_quantize_meta16(const void *x, int x_dtype, int64_t rows, int64_t cols, i
             h = 0x0001u;
         else if ((h & 0x7C00u) == 0x7C00u)
             h = 0x7BFFu;
-        s16[e] = h;
+        s16[e] = p.stored > 0.0f ? h : 0u;
         p.s = or_f16_to_f32(h);
         if (!symmetric) {
             /* -l / s16 can lie far beyond the int range when s16 saturated at 65504: clamp the rounded
@@ -410,7 +418,7 @@ int or_kv_keys(const void *x, int x_dtype, int64_t tokens, int64_t channels, int
                 hi = v;
         }
         seg_params p = segment_params(absmax, lo, hi, 8, symmetric);
-        scales[e] = p.s;
+        scales[e] = p.stored;
         if (zeros)
             zeros[e] = (uint8_t)p.z;
         for (int64_t t = t0; t < t1; ++t)

@@ -137,9 +137,11 @@ __device__ __forceinline__ float recip_scale(float s) { return __builtin_amdgcn_
 
 // Scale / zero / code range of one segment from its range statistics. Mirrors the definition:
 // symmetric: s = absmax / qmax; asymmetric: range widened to contain 0, s = (hi - lo) / (2^b - 1),
-// z = rne(-lo / s) clamped. A step of 0 (all-zero or underflowing range) becomes s = 1, z = 0.
+// z = rne(-lo / s) clamped. A step of 0 (all-zero or underflowing range) takes its codes with s = 1, z = 0
+// (all 0, no division by zero) and stores the scale 0, so that s (q - z) is exactly 0 in every consumer.
 struct SegParams {
-    float s, r;  // scale and its correctly rounded reciprocal
+    float s, r;  // step the codes are taken with and its correctly rounded reciprocal
+    float st;    // the scale written out: s, or 0 when the step is 0
     float z;     // zero point (integer valued)
     float qmin, qmax;
 };
@@ -154,8 +156,11 @@ __device__ __forceinline__ SegParams seg_params(float absmax, float lo, float hi
         p.qmin = -(float)qm;
         p.z = 0.0f;
         p.s = absmax / (float)qm;
-        if (!(p.s > 0.0f))
+        p.st = p.s;
+        if (!(p.s > 0.0f)) {
             p.s = 1.0f;
+            p.st = 0.0f;
+        }
     } else {
         constexpr int qm = (1 << BITS) - 1;
         p.qmax = (float)qm;
@@ -163,8 +168,10 @@ __device__ __forceinline__ SegParams seg_params(float absmax, float lo, float hi
         lo = lo > 0.0f ? 0.0f : lo;
         hi = hi < 0.0f ? 0.0f : hi;
         p.s = (hi - lo) / (float)qm;
+        p.st = p.s;
         if (!(p.s > 0.0f)) {
             p.s = 1.0f;
+            p.st = 0.0f;
             p.z = 0.0f;
         } else {
             float z = __builtin_rintf(-lo / p.s);

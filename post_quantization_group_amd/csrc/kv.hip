@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kv_keys(const XT *__restrict__ x
     if (r0 == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            scales[b * channels + c0 + j] = p[j].s;
+            scales[b * channels + c0 + j] = p[j].st;
             if (!SYM)
                 zeros[b * channels + c0 + j] = (uint8_t)p[j].z;
         }
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict_
                 *reinterpret_cast<uint2 *>(v_codes + vrow * channels + ci * 8) = codes8(v[u], ps);
         }
         if (y == 0 && tid == 0) {
-            v_scales[vrow] = sp.s;
+            v_scales[vrow] = sp.st;
             if (!SYM)
                 v_zeros[vrow] = (uint8_t)sp.z;
         }
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict_
             if (ci < nchunk && in_slice(ci)) {
                 *reinterpret_cast<uint2 *>(v_codes + vrow * channels + ci * 8) = codes8(v[u], ps);
                 if (ci % GL == 0) {  // the group's first chunk lies in exactly one slice
-                    v_scales[vrow * ngroups + ci / GL] = sp.s;
+                    v_scales[vrow * ngroups + ci / GL] = sp.st;
                     if (!SYM)
                         v_zeros[vrow * ngroups + ci / GL] = (uint8_t)sp.z;
                 }
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kAppThreads) void k_kv_append(const XT *__restrict_
     if (r0 == 0)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            k_scales[kb * channels + c + j] = ps[j].s;
+            k_scales[kb * channels + c + j] = ps[j].st;
             if (!SYM)
                 k_zeros[kb * channels + c + j] = (uint8_t)ps[j].z;
         }

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void k_quant_group(const XT *__restrict__ x, c
     const SegParams p = seg_params<BITS, SYM>(absmax, lo, hi);
     store_codes8<BITS, SYM>(v, p, codes, c * 8);
     if ((c % LPG) == 0) {
-        scales[c / LPG] = p.s;
+        scales[c / LPG] = p.st;
         if (!SYM)
             zeros[c / LPG] = (uint8_t)p.z;
     }
@@ -123,6 +123,7 @@ __global__ __launch_bounds__(256) void k_quant_group(const XT *__restrict__ x, c
 // the atlas's §1.1 count one 16-bit scale per group). The group's (s, z) as above; the scale is stored as the
 // nearest-even binary16 (0 -> the smallest subnormal, overflow -> the largest finite value), and the codes and
 // the asymmetric zero point are computed with the stored scale, so that s16 (q - z) is what the metadata encodes.
+// A segment whose fp32 step is 0 stores 0 (its codes, all 0, are taken with the unit step).
 template <bool SYM>
 __device__ __forceinline__ uint16_t meta16_params(SegParams &p, float lo)
 {
@@ -137,7 +138,7 @@ __device__ __forceinline__ uint16_t meta16_params(SegParams &p, float lo)
         const float l = lo > 0.0f ? 0.0f : lo;
         p.z = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(-l / p.s), 0.0f), 15.0f);
     }
-    return h;
+    return p.st > 0.0f ? h : (uint16_t)0;
 }
 
 // One thread per chunk of 8 as k_quant_group; the zero points of groups 2i and 2i + 1 (LPG lanes apart, in one
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(NT) void k_quant_row(const XT *__restrict__ x, cons
             store_codes8<BITS, SYM>(v[i], p, codes, base + ch * 8);
     }
     if (threadIdx.x == 0) {
-        scales[row] = p.s;
+        scales[row] = p.st;
         if (!SYM)
             zeros[row] = (uint8_t)p.z;
     }
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(256) void k_tensor_quant(const XT *__restrict__ x, 
         store_codes8<BITS, SYM>(v, p, codes, c * 8);
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-        scales[0] = p.s;
+        scales[0] = p.st;
         if (!SYM)
             zeros[0] = (uint8_t)p.z;
     }
@@ -367,6 +368,7 @@ __global__ __launch_bounds__(256) void k_quant_static(const XT *__restrict__ x, 
 {
     SegParams p;
     p.s = scale;
+    p.st = scale;
     p.r = 1.0f / scale;  // any scale a caller passes: the correctly rounded reciprocal (once per thread)
     p.z = zero;
     p.qmax = SYM ? (float)((1 << (BITS - 1)) - 1) : (float)((1 << BITS) - 1);

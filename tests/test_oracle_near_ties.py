@@ -41,6 +41,7 @@ def _half_even(t: np.float32) -> int:
 
 def _check_against_fractions(x, q, s_el, z_el, bits, sym, limit=1500):
     qmin, qmax = A.code_range(bits, sym)
+    s_el = np.where(s_el == 0, np.float32(1), s_el).astype(np.float32)  # a stored 0: codes took the unit step
     with np.errstate(all="ignore"):
         t = (x / s_el).astype(np.float32)
         tr = (x * (np.float32(1) / s_el)).astype(np.float32)
@@ -107,6 +108,6 @@ def test_special_segments_cover_the_named_cases():
     q, s, _ = oracle.quantize(np.stack(segs), 4, True, oracle.ROW)
     assert s[0] == 1.0 and q[0, 1:8].tolist() == [2, 4, -2, 0, 0, 2, -4]
     zero_row = [i for i, g in enumerate(segs) if not g.any()][0]
-    assert s[zero_row] == 1.0 and not q[zero_row].any()
-    assert s[zero_row + 1] == 1.0  # the smallest subnormal alone: its scale underflows to 0, so s = 1
+    assert s[zero_row] == 0.0 and not q[zero_row].any()
+    assert s[zero_row + 1] == 0.0 and not q[zero_row + 1].any()  # the smallest subnormal alone: step 0
     assert 0 < s[zero_row + 3] < np.float32(2.0 ** -126)  # a subnormal scale

@@ -227,14 +227,15 @@ def test_asymmetric_range_ends_and_all_positive_group():
 
 
 def test_zero_range_and_underflowing_groups():
-    """An all-zero group, and a group whose fp32 scale underflows to 0, get s = 1 (and z = 0)."""
+    """An all-zero group, and a group whose fp32 scale underflows to 0, store s = 0 (and z = 0); their codes
+    are all 0, so s (q - z) is exactly 0."""
     tiny = np.float32(1.4e-45)  # smallest positive subnormal
     x = np.zeros((3, 32), np.float32)
     x[1, 5] = tiny
     x[2, 5] = np.float32(1e-40)  # subnormal but large enough for a nonzero subnormal scale
     for sym in (True, False):
         q, s, z = oracle.quantize(x, 4, sym, oracle.GROUP, 32)
-        assert s[0] == 1.0 and s[1] == 1.0
+        assert s.view(np.uint32)[0] == 0 and s.view(np.uint32)[1] == 0  # +0, not -0
         assert np.all(q[0] == (0 if sym else 0)) and np.all(q[1] == 0)
         assert 0 < s[2] < 1e-40
         assert (q[2, 5] == 7) if sym else (q[2, 5] == 15)
@@ -712,6 +713,8 @@ def test_meta16_scale_is_the_rounded_fp32_scale(sym):
     tiny = np.full((1, 32), 1e-9, np.float32)
     _, st, _ = oracle.quantize_meta16(tiny, True, 32)
     assert st[0] == 0x0001
+    q0, s0, _ = oracle.quantize_meta16(np.zeros((1, 32), np.float32), sym, 32)  # a zero range stores 0
+    assert s0[0] == 0 and not q0.any()
 
 
 @pytest.mark.parametrize("sym", [True, False])
