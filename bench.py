@@ -590,7 +590,10 @@ def llama7b_configs(pqg, W, dev, bf16, reps=8, rounds=6):
     x10, asymmetric UINT4 at g = 32 and g = 128) configurations: quantize and W4A16 throughput with the
     weights rotated over R device copies (R x packed bytes >= 512 MB, twice the last-level cache), so every
     timed call streams its copy from HBM. `reps` launches back to back on consecutive copies are timed as one
-    event pair and averaged; the median over `rounds` such blocks is reported. Also the metadata bytes
+    event pair and averaged; the median over `rounds` such blocks is reported. A call through the binding
+    costs the host about as long as these kernels run, so the same calls are also captured once into a HIP
+    graph over all R copies and replayed (`graph_*`: the kernels back to back without host dispatch in
+    between). Also the metadata bytes
     against the packed weight bytes, as stored (fp32 scales + uint8 zero points) and with 16-bit metadata
     (binary16 scales + 4-bit zero points)."""
     import numpy as np
@@ -610,6 +613,27 @@ def llama7b_configs(pqg, W, dev, bf16, reps=8, rounds=6):
             e1.synchronize()
             if r:
                 ts.append(e0.elapsed_time(e1) / reps)
+        return float(np.median(ts))
+
+    def graphed(fn, count):
+        """`count` calls captured once into a HIP graph (through torch's capture of the current stream), then
+        the graph replayed between two events: per-call time without the host's dispatch of each launch."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(count):
+                fn(j)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for r in range(rounds + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1) / count)
+        del g
         return float(np.median(ts))
 
     cases = [("attn7b_4096x4096_sym_g128", W.attn7b(ms=(16,)), True, 128, (1, 16)),
@@ -636,9 +660,13 @@ def llama7b_configs(pqg, W, dev, bf16, reps=8, rounds=6):
         q_ms = timed(lambda i: pqg.quantize(wr[i % len(wr)], 4, sym, pqg.GROUP, g,
                                             out=(codes[i % R], scales[i % R], zeros[i % R])))
         q_bytes = n * k * 2 + packed_b + meta_b
+        qg_ms = graphed(lambda i: pqg.quantize(wr[i % len(wr)], 4, sym, pqg.GROUP, g,
+                                               out=(codes[i % R], scales[i % R], zeros[i % R])), len(wr))
         e = {"N": n, "K": k, "symmetric": sym, "group_size": g, "copies": R,
              "quantize_us": round(q_ms * 1e3, 2), "quantize_gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
              "quantize_hbm_frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "quantize_graph_us": round(qg_ms * 1e3, 2),
+             "quantize_graph_gbs": round(q_bytes / (qg_ms * 1e-3) / 1e9, 1),
              "weight_bytes": packed_b + meta_b, "packed_bytes": packed_b, "metadata_bytes": meta_b,
              "metadata_share": round(meta_b / packed_b, 5), "metadata16_bytes": meta16_b,
              "metadata16_share": round(meta16_b / packed_b, 5), "w4a16": {}}
@@ -646,8 +674,13 @@ def llama7b_configs(pqg, W, dev, bf16, reps=8, rounds=6):
             t = timed(lambda i, m=m: pqg.qlinear_w4a16(x[:m], codes[i % R], scales[i % R], zeros[i % R], g, sym,
                                                         out=ys[m]))
             gbs = (packed_b + meta_b) / (t * 1e-3) / 1e9
+            tg = graphed(lambda i, m=m: pqg.qlinear_w4a16(x[:m], codes[i % R], scales[i % R], zeros[i % R], g,
+                                                           sym, out=ys[m]), R)
+            gg = (packed_b + meta_b) / (tg * 1e-3) / 1e9
             e["w4a16"][str(m)] = {"us": round(t * 1e3, 2), "weight_gbs": round(gbs, 1),
-                                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+                                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "graph_us": round(tg * 1e3, 2), "graph_weight_gbs": round(gg, 1),
+                                  "graph_hbm_frac": round(gg / HBM_PEAK_GBS, 4)}
         out[name] = e
         del wr, codes, scales, zeros, ys, w
         torch.cuda.empty_cache()
@@ -657,8 +690,9 @@ def llama7b_configs(pqg, W, dev, bf16, reps=8, rounds=6):
 def tiny_config(pqg, W, dev, bf16, reps=20, rounds=6):
     """The tiny configuration (fp32 weight 256 x 512 with 0.5 % outliers, symmetric INT4 g = 128; x in R^512):
     quantize, dequantize to fp32 and the W4A16 GEMV with fp32 output, each timed as `reps` launches back to
-    back between two events (median of `rounds`). 71 KB of data: the times are launch and latency, reported
-    without a roofline fraction."""
+    back between two events (median of `rounds`), both as calls through the binding and as the same calls
+    replayed from a HIP graph. 71 KB of data: the times are launch and latency, reported without a roofline
+    fraction."""
     import numpy as np
     import torch
 
@@ -684,14 +718,36 @@ def tiny_config(pqg, W, dev, bf16, reps=20, rounds=6):
                 ts.append(e0.elapsed_time(e1) / reps)
         return round(float(np.median(ts)) * 1e3, 2)
 
-    return {"N": n, "K": k, "group_size": 128, "symmetric": True,
-            "note": "per call through the Python binding, back to back: host dispatch sets these times (the "
-                    "kernels alone take 2-3 us in the kernel trace)",
-            "quantize_us": timed(lambda: pqg.quantize(w, 4, True, pqg.GROUP, 128, out=(codes, scales, None))),
-            "dequantize_us": timed(lambda: pqg.dequantize(codes, scales, None, n, k, 4, True, pqg.GROUP, 128,
-                                                          out=deq)),
-            "w4a16_m1_f32_us": timed(lambda: pqg.qlinear_w4a16(x, codes, scales, None, 128, True,
-                                                               out_dtype=torch.float32, out=y))}
+    def graphed(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for r in range(rounds + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1) / reps)
+        del g
+        return round(float(np.median(ts)) * 1e3, 2)
+
+    ops = {"quantize": lambda: pqg.quantize(w, 4, True, pqg.GROUP, 128, out=(codes, scales, None)),
+           "dequantize": lambda: pqg.dequantize(codes, scales, None, n, k, 4, True, pqg.GROUP, 128, out=deq),
+           "w4a16_m1_f32": lambda: pqg.qlinear_w4a16(x, codes, scales, None, 128, True, out_dtype=torch.float32,
+                                                     out=y)}
+    r = {"N": n, "K": k, "group_size": 128, "symmetric": True,
+         "note": "per call through the Python binding, back to back: host dispatch sets these times; the "
+                 "graph_us figures replay the same calls captured in a HIP graph (kernels back to back)"}
+    for name, fn in ops.items():
+        r[name + "_us"] = timed(fn)
+        r[name + "_graph_us"] = graphed(fn)
+    return r
 
 
 def cpu_baseline(target_s):

@@ -2,7 +2,8 @@
 
 Small random shapes and value distributions -- plain normal at several magnitudes, half-step grids that put
 quotients on exact ties, all-zero rows, constant groups, subnormal and large magnitudes, sparse outliers --
-through quantize, dequantize and the W4A16 and W8A8 products, against the oracle on the same inputs.
+through quantize, dequantize, the binary16-metadata quantize and decode, the KV keys and the W4A16, W8A8 and
+W4A8 products, against the oracle on the same inputs.
 Bar: codes, packed bytes, scales and zero points bit-exact; dequantized values bit-exact; fp32 products within
 1e-5 normwise and within the per-element bounds.
 """
@@ -14,8 +15,8 @@ from hypothesis import strategies as st
 
 import oracle
 import workloads as W
-from helpers import (BOUND_W4A16_F32, BOUND_W8A8_F32, abs_terms_i8, abs_terms_w4, assert_per_element, normwise,
-                     to_f64, to_gpu, to_gpu_bf16)
+from helpers import (BOUND_W4A8_F32, BOUND_W4A16_F32, BOUND_W8A8_F32, abs_terms_i8, abs_terms_w4, abs_terms_w4a8,
+                     assert_per_element, normwise, to_f64, to_gpu, to_gpu_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +132,91 @@ def test_w8a8_property(gpu_lib, seed, m, n, kchunks, alpha, kinds):
     assert normwise(yg, r["y"]) <= TOL_F32
     assert_per_element(yg, r["y"], abs_terms_i8(r["q_x"], r["s_x"], r["q_w"], r["s_w"]), BOUND_W8A8_F32,
                        "W8A8 property")
+
+
+@PROPS
+@given(seed=st.integers(0, 2 ** 32 - 1), m=st.integers(1, 4), n=st.integers(1, 160), ksteps=st.integers(1, 4),
+       gs=st.sampled_from([32, 64, 128]), sym=st.booleans(),
+       kinds=st.lists(st.sampled_from(PRODUCT_KINDS), min_size=1, max_size=3))
+def test_meta16_decode_property(gpu_lib, seed, m, n, ksteps, gs, sym, kinds):
+    """Binary16 scales and packed zero points: quantize bit-exact, decode against the W4A16 reference on the
+    stored (binary16) scales."""
+    k = 128 * ksteps
+    wh = W.bf16_bits(make_rows(seed, n, k, kinds, gs))
+    x = W.bf16_bits(make_rows(seed + 1, m, k, ("normal", "ties", "outliers"), gs))
+    codes, s16, z4 = gpu_lib.quantize_meta16(to_gpu_bf16(wh), sym, gs)
+    y = gpu_lib.qlinear_w4a16_meta16(to_gpu_bf16(x), codes, s16, z4, gs, sym, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    q, so, zo = oracle.quantize_meta16(wh, sym, gs)
+    assert np.array_equal(codes.cpu().numpy(), oracle.pack_int4(q)), "codes differ"
+    assert np.array_equal(s16.cpu().numpy().view(np.uint16), so), "binary16 scales differ"
+    if not sym:
+        assert np.array_equal(z4.cpu().numpy(), oracle.pack_zeros4(zo)), "packed zero points differ"
+    sf = oracle.f16_to_f32(so)
+    y_ref = oracle.w4a16(x, q, sf, zo, gs)
+    yg = to_f64(y)
+    if not np.any(y_ref):
+        assert not np.any(yg), "all-zero product came out nonzero"
+        return
+    assert normwise(yg, y_ref) <= TOL_F32
+    assert_per_element(yg, y_ref, abs_terms_w4(x, q, sf, zo, gs), BOUND_W4A16_F32, "meta16 property")
+
+
+ACT_KINDS = ("uniform", "zeros", "extreme", "small")
+
+
+@PROPS
+@given(seed=st.integers(0, 2 ** 32 - 1), m=st.integers(1, 200), n=st.integers(1, 300), ksteps=st.integers(1, 4),
+       gs=st.sampled_from([32, 64, 128]), sym=st.booleans(),
+       wkinds=st.lists(st.sampled_from(PRODUCT_KINDS), min_size=1, max_size=3),
+       akinds=st.lists(st.sampled_from(ACT_KINDS), min_size=1, max_size=3))
+def test_w4a8_property(gpu_lib, seed, m, n, ksteps, gs, sym, wkinds, akinds):
+    """INT8 token codes (uniform, all-zero rows with a zero scale, rows at +-127, rows of small codes) times
+    INT4 group weights of the value kinds above, fp32 out, against the oracle."""
+    k = 128 * ksteps
+    rng = np.random.default_rng(seed)
+    qx = np.empty((m, k), np.int8)
+    sx = np.empty(m, np.float32)
+    for r in range(m):
+        kind = akinds[r % len(akinds)]
+        if kind == "uniform":
+            qx[r] = rng.integers(-127, 128, k)
+        elif kind == "zeros":
+            qx[r] = 0
+        elif kind == "extreme":
+            qx[r] = rng.choice(np.array([-127, 127], np.int8), k)
+        else:
+            qx[r] = rng.integers(-2, 3, k)
+        sx[r] = 0.0 if kind == "zeros" else np.float32(rng.uniform(1e-4, 0.05))
+    w = make_rows(seed + 1, n, k, wkinds, gs)
+    codes, s_w, z_w = gpu_lib.quantize(to_gpu(w), 4, sym, 2, gs)
+    y = gpu_lib.qlinear_w4a8(to_gpu(qx), to_gpu(sx), codes, s_w, z_w, gs, sym, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    q, so, zo = oracle.quantize(w, 4, sym, oracle.GROUP, gs)
+    assert np.array_equal(codes.cpu().numpy(), oracle.pack_int4(q)), "weight codes differ"
+    y_ref = oracle.w4a8(qx, sx, q, so, zo, gs)
+    yg = to_f64(y)
+    if not np.any(y_ref):
+        assert not np.any(yg), "all-zero product came out nonzero"
+        return
+    assert normwise(yg, y_ref) <= TOL_F32
+    assert_per_element(yg, y_ref, abs_terms_w4a8(qx, sx, q, so, zo, gs), BOUND_W4A8_F32, "W4A8 property")
+
+
+@PROPS
+@given(seed=st.integers(0, 2 ** 32 - 1), nblocks=st.integers(1, 3), bt=st.sampled_from([32, 64, 128, 256]),
+       cblocks=st.integers(1, 4), sym=st.booleans(), bf16=st.booleans(),
+       kinds=st.lists(st.sampled_from(KINDS), min_size=1, max_size=4))
+def test_kv_keys_property(gpu_lib, seed, nblocks, bt, cblocks, sym, bf16, kinds):
+    """Keys per channel over blocks of tokens: channel c follows kinds[c % len(kinds)] along the tokens. Codes,
+    scales and zero points bit-exact."""
+    tokens, channels = nblocks * bt, 64 * cblocks
+    kt = np.ascontiguousarray(make_rows(seed, channels, tokens, kinds, bt).T)
+    kh = W.bf16_bits(kt) if bf16 else kt
+    q, s, z = gpu_lib.kv_quantize_keys(to_gpu_bf16(kh) if bf16 else to_gpu(kh), bt, sym)
+    torch.cuda.synchronize()
+    qo, so, zo = oracle.kv_quantize_keys(kh, bt, sym)
+    assert np.array_equal(q.cpu().numpy().astype(np.int64), qo.astype(np.int64)), "key codes differ"
+    assert np.array_equal(s.cpu().numpy().view(np.uint32).ravel(), so.view(np.uint32).ravel()), "key scales differ"
+    if not sym:
+        assert np.array_equal(z.cpu().numpy().ravel(), zo.ravel()), "key zero points differ"
