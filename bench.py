@@ -100,7 +100,8 @@ def stream_reference(pqg, dev, reps=6):
     """Measured streaming rates on this GPU, to set the kernels' rates beside: one streaming read of 1 GiB
     (pqg_stream_read_probe: 16-byte non-temporal loads, four in flight per lane) and a device copy of 1 GiB
     (torch's copy, reads + writes), event-timed, medians over `reps` after one warm-up; both buffers are far
-    larger than the 256 MB last-level cache."""
+    larger than the 256 MB last-level cache. Also the int8 matrix-core rate with no memory traffic
+    (pqg_mfma_i8_probe), which the chip's clock under that load sets."""
     import numpy as np
     import torch
 
@@ -124,6 +125,21 @@ def stream_reference(pqg, dev, reps=6):
         out[name] = round(nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
     del src, dst
     torch.cuda.empty_cache()
+    # int8 matrix-core rate from registers alone (pqg_mfma_i8_probe), on the GEMM's 232-block grid and on one
+    # block per CU, each wave issuing as many instructions as a GEMM wave does (3072 per SIMD)
+    iters = 384
+    for blocks in (232, 256):
+        ts = []
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pqg.mfma_i8_probe(blocks, iters, sink)
+            e1.record(stream)
+            e1.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1))
+        ops = blocks * 8 * 4 * iters * 65536
+        out["mfma_i8_tops_%d_blocks" % blocks] = round(ops / (float(np.median(ts)) * 1e-3) / 1e12, 1)
     return out
 
 
@@ -566,6 +582,8 @@ def main():
     out["device"] = device_record(dev)
     ref = stream_reference(pqg, dev)
     out["stream_reference"] = dict(ref, decode_frac_of_read=round(value / ref["read_gbs"], 4),
+                                   gemm_frac_of_mfma_probe=round(out["w8a8_gemm"]["value"]
+                                                                 / ref["mfma_i8_tops_232_blocks"], 4),
                                    quantize_frac_of_copy=round((quant_bytes / (part_ms["quantize"] * 1e-3) / 1e9)
                                                                / ref["copy_gbs"], 4),
                                    dequantize_frac_of_copy=round((quant_bytes / (part_ms["dequantize"] * 1e-3) / 1e9)

@@ -32,7 +32,7 @@ EXPORTS = [
     "pqg_smooth_workspace_bytes", "pqg_smooth", "pqg_qlinear_w4a16", "pqg_qlinear_w8a8", "pqg_gemm_s8s8s32",
     "pqg_qlinear_w4a8", "pqg_kv_quantize_keys", "pqg_kv_dequantize_keys", "pqg_kv_append",
     "pqg_quantize_meta16", "pqg_dequantize_meta16", "pqg_qlinear_w4a16_meta16", "pqg_qlinear_w8a8_noalloc",
-    "pqg_qlinear_w4a16_grouped", "pqg_stream_read_probe",
+    "pqg_qlinear_w4a16_grouped", "pqg_stream_read_probe", "pqg_mfma_i8_probe",
 ]
 
 _lib = None
@@ -102,6 +102,8 @@ def load(path: str = LIB_PATH):
     lib.pqg_qlinear_w8a8_noalloc.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
     lib.pqg_stream_read_probe.restype = I32
     lib.pqg_stream_read_probe.argtypes = [P, I64, P, P]
+    lib.pqg_mfma_i8_probe.restype = I32
+    lib.pqg_mfma_i8_probe.argtypes = [I64, I32, P, P]
     if lib.pqg_abi_version() != ABI_VERSION:
         raise ImportError("libpqg.so ABI %d != binding ABI %d" % (lib.pqg_abi_version(), ABI_VERSION))
     _lib = lib
@@ -465,4 +467,15 @@ def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor = None) -> torch.Ten
     if sink is None:
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
     _check(load().pqg_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(dev)))
+    return sink
+
+
+def mfma_i8_probe(blocks: int, iters: int, sink: torch.Tensor) -> torch.Tensor:
+    """pqg_mfma_i8_probe: `blocks` blocks of 8 waves, each wave issuing 4 * iters int8 32x32x32 matrix
+    instructions from registers (blocks * 8 * 4 * iters * 65536 ops), for measuring the int8 matrix-core rate
+    the device sustains. `sink` is a 1-element int32 device tensor (its value is meaningless)."""
+    if not sink.is_cuda:
+        raise ValueError("sink must be a device tensor")
+    dev = _dev(sink)
+    _check(load().pqg_mfma_i8_probe(int(blocks), int(iters), _ptr(sink), _stream(dev)))
     return sink

@@ -675,4 +675,16 @@ int32_t pqg_stream_read_probe(const void *src, int64_t bytes, uint32_t *sink, vo
     return hip_status(pqg::launch_stream_read(src, bytes, sink, as_stream(stream)), "stream read probe");
 }
 
+int32_t pqg_mfma_i8_probe(int64_t blocks, int32_t iters, uint32_t *sink, void *stream)
+{
+    g_err[0] = 0;
+    if (blocks < 0 || blocks > 65535)
+        return fail(PQG_EINVAL, "blocks must be in [0, 65535] (got %lld)", (long long)blocks);
+    if (iters < 0 || iters > (1 << 20))
+        return fail(PQG_EINVAL, "iters must be in [0, 2^20] (got %d)", iters);
+    if (!sink)
+        return fail(PQG_EINVAL, "sink is required");
+    return hip_status(pqg::launch_mfma_i8(blocks, iters, sink, as_stream(stream)), "int8 matrix-core probe");
+}
+
 }  // extern "C"

@@ -199,5 +199,6 @@ hipError_t launch_kv_append(const KvAppendArgs &a, hipStream_t st);
 
 // One streaming read of `bytes` (a multiple of 16) at 16-byte aligned `src`; `sink` receives at most one word.
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t st);
+hipError_t launch_mfma_i8(int64_t blocks, int32_t iters, uint32_t *sink, hipStream_t st);
 
 }  // namespace pqg

@@ -1,7 +1,15 @@
-// probe.hip -- one streaming read of a device buffer, to measure the device's achievable read rate beside the
-// rates of the library's kernels. Every byte is read once with 16-byte non-temporal loads, four per lane in
-// flight (grid-stride); the loaded words are folded by xor into one word, which reaches `sink` only under a
+// probe.hip -- two measurement utilities, no step of the method.
+//
+// k_stream_read: one streaming read of a device buffer, to measure the device's achievable read rate beside
+// the rates of the library's kernels. Every byte is read once with 16-byte non-temporal loads, four per lane
+// in flight (grid-stride); the loaded words are folded by xor into one word, which reaches `sink` only under a
 // condition on the data (so the loads cannot be dropped); the sink's contents carry no meaning.
+//
+// k_mfma_i8: the int8 matrix-core rate the device sustains with no memory traffic at all, to set the INT8
+// GEMM's rate beside. Blocks of 8 waves (two per SIMD, as the GEMM runs) issue v_mfma_i32_32x32x32_i8 on four
+// independent accumulators per wave from register operands; the clock the chip holds under this load is the
+// one the GEMM sees, so the ratio of the two rates isolates the GEMM's schedule from the chip's power limit.
+// The accumulators are folded into one word that reaches `sink` only under a condition on it.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,6 +33,37 @@ __global__ __launch_bounds__(256) void k_stream_read(const probe_u32x4 *__restri
     const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
     if (r == 0x9E3779B9u)
         sink[0] = r;
+}
+
+typedef int probe_v4i __attribute__((ext_vector_type(4)));
+typedef int probe_v16i __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(512) void k_mfma_i8(int iters, uint32_t *__restrict__ sink)
+{
+    const int t = (int)threadIdx.x + (int)blockIdx.x * 512;
+    const probe_v4i a = {t, t * 3 + 1, t * 5 + 2, t * 7 + 3};
+    const probe_v4i b = {t ^ 0x55, t * 11 + 5, t * 13 + 6, t * 17 + 7};
+    probe_v16i acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
+    for (int i = 0; i < iters; ++i) {
+        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, acc1, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, acc2, 0, 0, 0);
+        acc3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, b, acc3, 0, 0, 0);
+    }
+    uint32_t r = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        r ^= (uint32_t)(acc0[j] ^ acc1[j] ^ acc2[j] ^ acc3[j]);
+    if (r == 0x9E3779B9u)
+        sink[0] = r;
+}
+
+hipError_t launch_mfma_i8(int64_t blocks, int32_t iters, uint32_t *sink, hipStream_t st)
+{
+    if (blocks == 0 || iters == 0)
+        return hipSuccess;
+    k_mfma_i8<<<(unsigned)blocks, 512, 0, st>>>(iters, sink);
+    return hipGetLastError();
 }
 
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t st)

@@ -289,3 +289,13 @@ def test_stream_read_probe_rejects_bad_arguments(lib):
     assert lib.pqg_stream_read_probe(None, 64, FAKE, None) == pqg.EINVAL
     assert lib.pqg_stream_read_probe(misaligned, 64, FAKE, None) == pqg.EINVAL
     assert lib.pqg_stream_read_probe(None, 0, FAKE, None) == pqg.OK
+
+
+def test_mfma_probe_rejects_bad_arguments(lib):
+    """The matrix-core probe validates on the host: blocks in [0, 65535], iters in [0, 2^20], a sink."""
+    assert lib.pqg_mfma_i8_probe(-1, 4, FAKE, None) == pqg.EINVAL
+    assert lib.pqg_mfma_i8_probe(65536, 4, FAKE, None) == pqg.EINVAL
+    assert lib.pqg_mfma_i8_probe(8, -1, FAKE, None) == pqg.EINVAL
+    assert lib.pqg_mfma_i8_probe(8, (1 << 20) + 1, FAKE, None) == pqg.EINVAL
+    assert lib.pqg_mfma_i8_probe(8, 4, None, None) == pqg.EINVAL
+    assert lib.pqg_mfma_i8_probe(0, 4, FAKE, None) == pqg.OK  # empty: nothing enqueued
