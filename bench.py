@@ -126,20 +126,25 @@ def stream_reference(pqg, dev, reps=6):
     del src, dst
     torch.cuda.empty_cache()
     # int8 matrix-core rate from registers alone (pqg_mfma_i8_probe), on the GEMM's 232-block grid and on one
-    # block per CU, each wave issuing as many instructions as a GEMM wave does (3072 per SIMD)
-    iters = 384
+    # block per CU, as 4 launches back to back between two events: each wave issuing as many instructions as
+    # a GEMM wave does (3072 per SIMD, about the GEMM's duration), and 16 times as many (the rate the chip
+    # settles at once its clock has risen under the load; shorter runs include the ramp)
+    for _ in range(4):  # bring the clock up under matrix load first, as the GEMM finds it inside a step
+        pqg.mfma_i8_probe(256, 2048, sink)
     for blocks in (232, 256):
-        ts = []
-        for r in range(reps + 1):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            pqg.mfma_i8_probe(blocks, iters, sink)
-            e1.record(stream)
-            e1.synchronize()
-            if r:
-                ts.append(e0.elapsed_time(e1))
-        ops = blocks * 8 * 4 * iters * 65536
-        out["mfma_i8_tops_%d_blocks" % blocks] = round(ops / (float(np.median(ts)) * 1e-3) / 1e12, 1)
+        for iters, tag in ((128, ""), (2048, "_long")):
+            ts = []
+            for r in range(reps + 1):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(4):
+                    pqg.mfma_i8_probe(blocks, iters, sink)
+                e1.record(stream)
+                e1.synchronize()
+                if r:
+                    ts.append(e0.elapsed_time(e1) / 4)
+            ops = blocks * 8 * 12 * iters * 65536
+            out["mfma_i8_tops_%d_blocks%s" % (blocks, tag)] = round(ops / (float(np.median(ts)) * 1e-3) / 1e12, 1)
     return out
 
 
@@ -584,6 +589,8 @@ def main():
     out["stream_reference"] = dict(ref, decode_frac_of_read=round(value / ref["read_gbs"], 4),
                                    gemm_frac_of_mfma_probe=round(out["w8a8_gemm"]["value"]
                                                                  / ref["mfma_i8_tops_232_blocks"], 4),
+                                   gemm_frac_of_mfma_probe_long=round(out["w8a8_gemm"]["value"]
+                                                                      / ref["mfma_i8_tops_232_blocks_long"], 4),
                                    quantize_frac_of_copy=round((quant_bytes / (part_ms["quantize"] * 1e-3) / 1e9)
                                                                / ref["copy_gbs"], 4),
                                    dequantize_frac_of_copy=round((quant_bytes / (part_ms["dequantize"] * 1e-3) / 1e9)

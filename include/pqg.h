@@ -388,9 +388,9 @@ int32_t pqg_stream_read_probe(const void *src, int64_t bytes, uint32_t *sink, vo
 
 /*
  * A measurement utility, no step of the method: the int8 matrix-core rate with no memory traffic. Enqueues
- * `blocks` blocks of 8 waves (two per SIMD, the INT8 GEMM's layout); each wave issues 4 * iters
- * v_mfma_i32_32x32x32_i8 (32 x 32 x 32 int8 products each, 65,536 ops) from register operands. The work is
- * blocks * 8 * 4 * iters * 65,536 ops; its rate, timed by the caller, is what the chip sustains at the clock
+ * `blocks` blocks of 8 waves (two per SIMD, the INT8 GEMM's layout); each wave issues 12 * iters
+ * v_mfma_i32_32x32x32_i8 (32 x 32 x 32 int8 products each, 65,536 ops) on 12 independent accumulators from
+ * register operands. The work is blocks * 8 * 12 * iters * 65,536 ops; its rate, timed by the caller, is what the chip sustains at the clock
  * it holds under int8 matrix load, the ceiling to set the GEMM's rate against.
  *   blocks : 0 .. 65535 (0 enqueues nothing); iters: 0 .. 2^20.
  *   sink   : device memory for one uint32; the call may write an arbitrary word there.

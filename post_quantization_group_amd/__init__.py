@@ -471,8 +471,8 @@ def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor = None) -> torch.Ten
 
 
 def mfma_i8_probe(blocks: int, iters: int, sink: torch.Tensor) -> torch.Tensor:
-    """pqg_mfma_i8_probe: `blocks` blocks of 8 waves, each wave issuing 4 * iters int8 32x32x32 matrix
-    instructions from registers (blocks * 8 * 4 * iters * 65536 ops), for measuring the int8 matrix-core rate
+    """pqg_mfma_i8_probe: `blocks` blocks of 8 waves, each wave issuing 12 * iters int8 32x32x32 matrix
+    instructions from registers (blocks * 8 * 12 * iters * 65536 ops), for measuring the int8 matrix-core rate
     the device sustains. `sink` is a 1-element int32 device tensor (its value is meaningless)."""
     if not sink.is_cuda:
         raise ValueError("sink must be a device tensor")

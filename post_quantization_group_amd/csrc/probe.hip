@@ -6,8 +6,8 @@
 // condition on the data (so the loads cannot be dropped); the sink's contents carry no meaning.
 //
 // k_mfma_i8: the int8 matrix-core rate the device sustains with no memory traffic at all, to set the INT8
-// GEMM's rate beside. Blocks of 8 waves (two per SIMD, as the GEMM runs) issue v_mfma_i32_32x32x32_i8 on four
-// independent accumulators per wave from register operands; the clock the chip holds under this load is the
+// GEMM's rate beside. Blocks of 8 waves (two per SIMD, as the GEMM runs) issue v_mfma_i32_32x32x32_i8 on twelve
+// independent accumulators per wave (the GEMM wave's 4 x 3 tiles, in VGPRs as there) from register operands; the clock the chip holds under this load is the
 // one the GEMM sees, so the ratio of the two rates isolates the GEMM's schedule from the chip's power limit.
 // The accumulators are folded into one word that reaches `sink` only under a condition on it.
 #include "common.hpp"
@@ -41,19 +41,33 @@ typedef int probe_v16i __attribute__((ext_vector_type(16)));
 __global__ __launch_bounds__(512) void k_mfma_i8(int iters, uint32_t *__restrict__ sink)
 {
     const int t = (int)threadIdx.x + (int)blockIdx.x * 512;
-    const probe_v4i a = {t, t * 3 + 1, t * 5 + 2, t * 7 + 3};
-    const probe_v4i b = {t ^ 0x55, t * 11 + 5, t * 13 + 6, t * 17 + 7};
-    probe_v16i acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
-    for (int i = 0; i < iters; ++i) {
-        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, acc1, 0, 0, 0);
-        acc2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, acc2, 0, 0, 0);
-        acc3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, b, acc3, 0, 0, 0);
-    }
+    probe_v4i fa[4], fb[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        fa[i] = probe_v4i{t + i, t * 3 + i, t * 5 + 2 * i, t * 7 + 3 * i};
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        fb[j] = probe_v4i{t ^ (0x55 + j), t * 11 + j, t * 13 + 2 * j, t * 17 + 3 * j};
+    probe_v16i acc[4][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            acc[i][j] = probe_v16i{};
+    for (int k = 0; k < iters; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
     uint32_t r = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-        r ^= (uint32_t)(acc0[j] ^ acc1[j] ^ acc2[j] ^ acc3[j]);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                r ^= (uint32_t)acc[i][j][e];
     if (r == 0x9E3779B9u)
         sink[0] = r;
 }
