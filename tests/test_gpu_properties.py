@@ -220,3 +220,46 @@ def test_kv_keys_property(gpu_lib, seed, nblocks, bt, cblocks, sym, bf16, kinds)
     assert np.array_equal(s.cpu().numpy().view(np.uint32).ravel(), so.view(np.uint32).ravel()), "key scales differ"
     if not sym:
         assert np.array_equal(z.cpu().numpy().ravel(), zo.ravel()), "key zero points differ"
+
+
+@PROPS
+@given(seed=st.integers(0, 2 ** 32 - 1), B=st.integers(1, 3), T=st.sampled_from([32, 64]), groups=st.integers(1, 2),
+       cblocks=st.integers(1, 3), vg=st.sampled_from([0, 32, 64]), sym=st.booleans(), bf16=st.booleans(),
+       kinds=st.lists(st.sampled_from(KINDS), min_size=1, max_size=4))
+def test_kv_append_property(gpu_lib, seed, B, T, groups, cblocks, vg, sym, bf16, kinds):
+    """Online appends, one token per sequence per step, sequences ending at different lengths (then pointed at
+    -1 or past the cache): the key and value token vectors follow the value kinds above (token t of sequence b
+    takes kinds[(b + t) % len(kinds)]). The whole cache -- codes, scales, zero points and the residual keys --
+    bit-exact against the oracle's step-by-step simulation."""
+    S, C = T * groups, 64 * cblocks
+    rng = np.random.default_rng(seed)
+    ks = make_rows(seed, B * S, C, kinds, 32).reshape(B, S, C)
+    vs = make_rows(seed + 1, B * S, C, kinds[::-1], 32).reshape(B, S, C)
+    if bf16:
+        ks, vs = W.bf16_bits(ks), W.bf16_bits(vs)
+    conv = to_gpu_bf16 if bf16 else to_gpu
+    n_tok = [int(rng.integers(1, S + 1)) for _ in range(B)]
+    nv = C // vg if vg else 1
+    ref = {"k_res": np.zeros((B, T, C), ks.dtype), "k_q": np.zeros((B, S, C), np.int32),
+           "k_s": np.zeros((B, S // T, C), np.float32), "v_q": np.zeros((B, S, C), np.int32),
+           "v_s": np.zeros((B, S, nv), np.float32)}
+    if not sym:
+        ref["k_z"] = np.zeros((B, S // T, C), np.uint8)
+        ref["v_z"] = np.zeros((B, S, nv), np.uint8)
+    cache = gpu_lib.kv_cache_alloc(B, S, C, T, vg, sym, torch.bfloat16 if bf16 else torch.float32)
+    for step in range(max(n_tok) + 1):
+        pos = np.array([step if step < n_tok[b] else (S + 3 if b % 2 else -1) for b in range(B)], np.int64)
+        kn = np.ascontiguousarray(ks[:, min(step, S - 1)])
+        vn = np.ascontiguousarray(vs[:, min(step, S - 1)])
+        gpu_lib.kv_append(cache, conv(kn), conv(vn), to_gpu(pos), T, vg, sym)
+        oracle.kv_append(ref, kn, vn, pos, T, vg, sym)
+    torch.cuda.synchronize()
+    for key in ("k_q", "v_q"):
+        assert np.array_equal(cache[key].cpu().numpy().astype(np.int32), ref[key]), key
+    for key in ("k_s", "v_s"):
+        assert np.array_equal(cache[key].cpu().numpy().view(np.uint32), ref[key].view(np.uint32)), key
+    if not sym:
+        for key in ("k_z", "v_z"):
+            assert np.array_equal(cache[key].cpu().numpy(), ref[key]), key
+    res = cache["k_res"].view(torch.int16).cpu().numpy().view(np.uint16) if bf16 else cache["k_res"].cpu().numpy()
+    assert np.array_equal(res, ref["k_res"]), "residual keys differ"
